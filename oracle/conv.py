@@ -1,0 +1,59 @@
+"""Tensor-field-network convolution, forward and backward (oracle; test infrastructure).
+
+[COURSE] lesson 06a: m_ij = (R(|r_ij|) Y(rhat_ij)) (x)_w h_j aggregated at the
+receiver i; [V2106] Convolution(edge_src, edge_dst, radial) with a
+sqrt(num_neighbors) normalisation; [E3J] 3.1.2 and E.2.2 (stream edges, CSR
+receiver aggregation). Here the radial factor arrives as per-edge weights
+w[e] (one per path and channel), so for a destination node n:
+
+  out[n] = scale * sum_{e : dst(e) = n} TP(x[src(e)], Y[e], w[e])
+
+summed in CSR order. Edge-indexed inputs (Y, w) are in CSR order; ``row_ptr``
+and ``src`` are the CSR arrays of ``graph.csr_from_coo``.
+"""
+
+import numpy as np
+
+from . import tp
+from .graph import dst_of_csr
+
+
+def forward_loops(L, row_ptr, src, x, Y, w, scale):
+    """Explicit per-node, per-edge loops (for tiny graphs)."""
+    N = len(row_ptr) - 1
+    out = np.zeros((N, L.dim_out))
+    for n in range(N):
+        acc = np.zeros(L.dim_out)
+        for e in range(row_ptr[n], row_ptr[n + 1]):
+            acc += tp.forward(L, x[src[e]][None], Y[e][None], w[e][None])[0]
+        out[n] = scale * acc
+    return out
+
+
+def forward(L, row_ptr, src, x, Y, w, scale):
+    """Materialised-message route: TP on gathered rows, then a scatter-add."""
+    x = np.asarray(x, np.float64)
+    N = len(row_ptr) - 1
+    dst = dst_of_csr(row_ptr)
+    msg = tp.forward(L, x[np.asarray(src)], Y, w)
+    out = np.zeros((N, L.dim_out))
+    np.add.at(out, dst, msg)
+    return scale * out
+
+
+def backward(L, row_ptr, src, x, Y, w, scale, g):
+    """Cotangents (dx [N, dim_x], dY [E, dim_y], dw [E, W]) for out cotangent g [N, dim_out]."""
+    x = np.asarray(x, np.float64)
+    dst = dst_of_csr(row_ptr)
+    src = np.asarray(src)
+    ge = scale * np.asarray(g, np.float64)[dst]
+    dxe, dY, dw = tp.backward(L, x[src], Y, w, ge)
+    dx = np.zeros_like(x)
+    np.add.at(dx, src, dxe)
+    return dx, dY, dw
+
+
+def avg_neighbors_scale(N, E):
+    """1 / sqrt(E / N): the sqrt(num_neighbors) normalisation of [V2106] with the
+    average degree of the built graph."""
+    return 1.0 / np.sqrt(E / N) if E > 0 else 1.0

@@ -1,0 +1,94 @@
+"""uvu Clebsch-Gordan tensor product, forward and backward (oracle; test infrastructure).
+
+[COURSE] lesson 03b: the learnable layer x (x)_w y built from instructions in a
+connection mode (uvw, uvu, ...), reproducible "with a bare einsum"; [E3J] 3.1.1
+(full CG tensor product) and E.1 (reverse-mode rules obtained by transposing the
+linear maps, using bilinearity and index permutations).
+
+For every path p = (i1, i2, l3) with x block i1 of multiplicity u:
+
+  out[z, p, m3, u] = w[(z,) p, u] * sum_{m1, m2} C_p[m1, m2, m3] x[z, i1, m1, u] y[z, i2, m2]
+
+``w`` is either shared, shape [W], or one row per z, shape [B, W], where
+W = sum_p mul_p. Two forward routes are given: explicit loops over the nonzero
+CG entries (``forward``) and one dense einsum per path (``forward_dense``).
+"""
+
+import numpy as np
+
+from .cg import cg_real
+from .irreps import Layout
+
+
+def _w_of(L, w, p, B):
+    wb = L.w_block(w, p)
+    if wb.ndim == 1:
+        wb = np.broadcast_to(wb, (B, wb.shape[0]))
+    return wb
+
+
+def forward(L, x, y, w):
+    """Sparse route: loop over paths and the nonzero entries of each CG block."""
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    w = np.asarray(w, np.float64)
+    B = x.shape[0]
+    out = np.zeros((B, L.dim_out))
+    for p in L.paths:
+        C = cg_real(p["l1"], p["l2"], p["l3"])
+        xb = L.x_block(x, p["i1"])            # [B, 2l1+1, u]
+        yb = L.y_block(y, p["i2"])            # [B, 2l2+1]
+        ob = np.zeros((B, 2 * p["l3"] + 1, p["mul"]))
+        for m1, m2, m3 in zip(*np.nonzero(C)):
+            ob[:, m3, :] += C[m1, m2, m3] * xb[:, m1, :] * yb[:, m2][:, None]
+        ob *= _w_of(L, w, p, B)[:, None, :]
+        L.out_block(out, p)[...] = ob
+    return out
+
+
+def forward_dense(L, x, y, w):
+    """Dense route: one einsum per path over the full CG block ([COURSE] 03b)."""
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    w = np.asarray(w, np.float64)
+    B = x.shape[0]
+    out = np.zeros((B, L.dim_out))
+    for p in L.paths:
+        C = cg_real(p["l1"], p["l2"], p["l3"])
+        ob = np.einsum("abc,zau,zb,zu->zcu", C, L.x_block(x, p["i1"]),
+                       L.y_block(y, p["i2"]), _w_of(L, w, p, B))
+        L.out_block(out, p)[...] = ob
+    return out
+
+
+def backward(L, x, y, w, g):
+    """Cotangents of x, y, w given the output cotangent g (transposition rules).
+
+      dx[z,i1,m1,u] = sum_p w * sum_{m2,m3} C y[m2] g[m3,u]
+      dy[z,i2,m2]   = sum_p sum_u w * sum_{m1,m3} C x[m1,u] g[m3,u]
+      dw[(z,)p,u]   = sum_{(z),m1,m2,m3} C x[m1,u] y[m2] g[m3,u]
+    A shared w gets its cotangent summed over rows.
+    """
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    w = np.asarray(w, np.float64)
+    g = np.asarray(g, np.float64)
+    B = x.shape[0]
+    dx = np.zeros_like(x)
+    dy = np.zeros_like(y)
+    dw_rows = np.zeros((B, L.w_numel))
+    for p in L.paths:
+        C = cg_real(p["l1"], p["l2"], p["l3"])
+        xb = L.x_block(x, p["i1"])
+        yb = L.y_block(y, p["i2"])
+        gb = L.out_block(g, p)
+        wb = _w_of(L, w, p, B)
+        L.x_block(dx, p["i1"])[...] += np.einsum("abc,zb,zcu,zu->zau", C, yb, gb, wb)
+        L.y_block(dy, p["i2"])[...] += np.einsum("abc,zau,zcu,zu->zb", C, xb, gb, wb)
+        dw_rows[:, p["w_off"]:p["w_off"] + p["mul"]] = np.einsum("abc,zau,zb,zcu->zu", C, xb, yb, gb)
+    dw = dw_rows if w.ndim == 2 else dw_rows.sum(axis=0)
+    return dx, dy, dw
+
+
+def make_layout(irreps_x, irreps_y, irreps_out):
+    return Layout(irreps_x, irreps_y, irreps_out)
