@@ -1,0 +1,251 @@
+// C ABI of libcgtp: argument checks, error translation, dispatch to launchers.
+// Nothing here computes; every step of the path runs in the HIP kernels.
+#include <cstring>
+#include <exception>
+#include <new>
+#include <string>
+
+#include "common.hpp"
+#include "graph.hpp"
+
+namespace cgtp {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+template <typename F>
+cgtp_status guarded(F&& f) {
+  try {
+    g_last_error.clear();
+    f();
+    return CGTP_OK;
+  } catch (const Error& e) {
+    g_last_error = e.msg;
+    return e.code;
+  } catch (const std::bad_alloc&) {
+    g_last_error = "host allocation failed";
+    return CGTP_ERR_ALLOC;
+  } catch (const std::exception& e) {
+    g_last_error = e.what();
+    return CGTP_ERR_INVALID_ARG;
+  } catch (...) {
+    g_last_error = "unknown error";
+    return CGTP_ERR_INVALID_ARG;
+  }
+}
+
+inline void need(bool ok, const char* what) {
+  if (!ok) throw Error{CGTP_ERR_INVALID_ARG, what};
+}
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace cgtp
+
+using namespace cgtp;
+
+extern "C" {
+
+const char* cgtp_status_string(cgtp_status s) {
+  switch (s) {
+    case CGTP_OK: return "ok";
+    case CGTP_ERR_INVALID_ARG: return "invalid argument";
+    case CGTP_ERR_PARSE: return "irreps parse error";
+    case CGTP_ERR_UNSUPPORTED: return "unsupported";
+    case CGTP_ERR_INDEX: return "index out of range";
+    case CGTP_ERR_WORKSPACE: return "workspace too small";
+    case CGTP_ERR_HIP: return "HIP error";
+    case CGTP_ERR_ALLOC: return "allocation failed";
+  }
+  return "unknown status";
+}
+
+const char* cgtp_last_error(void) { return g_last_error.c_str(); }
+
+cgtp_status cgtp_plan_create(const char* irreps_x, const char* irreps_y, const char* irreps_out,
+                             const char* mode, cgtp_dtype dtype, cgtp_wkind wkind, cgtp_plan* out) {
+  return guarded([&] {
+    need(out != nullptr, "out handle is NULL");
+    *out = nullptr;
+    *out = build_plan(irreps_x, irreps_y, irreps_out, mode, dtype, wkind);
+  });
+}
+
+cgtp_status cgtp_plan_destroy(cgtp_plan plan) {
+  return guarded([&] {
+    if (!plan) return;
+    free_plan_tables(plan);
+    delete plan;
+  });
+}
+
+cgtp_status cgtp_plan_query(cgtp_plan plan, int64_t* dim_x, int64_t* dim_y, int64_t* dim_out,
+                            int64_t* num_paths, int64_t* w_numel) {
+  return guarded([&] {
+    need(plan != nullptr, "plan is NULL");
+    if (dim_x) *dim_x = plan->dim_x;
+    if (dim_y) *dim_y = plan->dim_y;
+    if (dim_out) *dim_out = plan->dim_out;
+    if (num_paths) *num_paths = int64_t(plan->paths.size());
+    if (w_numel) *w_numel = plan->w_numel;
+  });
+}
+
+cgtp_status cgtp_plan_paths(cgtp_plan plan, int32_t* t) {
+  return guarded([&] {
+    need(plan != nullptr && t != nullptr, "NULL argument");
+    for (size_t i = 0; i < plan->paths.size(); ++i) {
+      const PathInfo& p = plan->paths[i];
+      const int32_t row[6] = {p.i1, p.i2, p.l1, p.l2, p.l3, p.p3};
+      std::memcpy(t + 6 * i, row, sizeof(row));
+    }
+  });
+}
+
+cgtp_status cgtp_plan_cg(cgtp_plan plan, int32_t path, double* host_dense) {
+  return guarded([&] {
+    need(plan != nullptr && host_dense != nullptr, "NULL argument");
+    need(path >= 0 && size_t(path) < plan->paths.size(), "path index out of range");
+    const auto& C = plan->cg_dense[size_t(path)];
+    std::memcpy(host_dense, C.data(), C.size() * sizeof(double));
+  });
+}
+
+cgtp_status cgtp_tp_forward(cgtp_plan plan, int64_t B, const void* x, const void* y, const void* w,
+                            void* out, void* stream) {
+  return guarded([&] {
+    need(plan != nullptr, "plan is NULL");
+    need(B >= 0, "B < 0");
+    if (B == 0) return;
+    need(x && y && w && out, "NULL tensor with B > 0");
+    tp_forward_launch(plan, B, x, y, w, out, as_stream(stream));
+  });
+}
+
+cgtp_status cgtp_tp_backward(cgtp_plan plan, int64_t B, const void* x, const void* y, const void* w,
+                             const void* grad_out, void* grad_x, void* grad_y, void* grad_w,
+                             void* ws, size_t ws_bytes, void* stream) {
+  return guarded([&] {
+    need(plan != nullptr, "plan is NULL");
+    need(B >= 0, "B < 0");
+    if (B == 0) {
+      // an empty batch still defines a (zero) gradient for shared weights
+      if (grad_w && plan->wkind == CGTP_W_SHARED)
+        CGTP_CHECK_HIP(hipMemsetAsync(grad_w, 0, size_t(plan->w_numel) * dtype_size(plan->dtype),
+                                      as_stream(stream)));
+      return;
+    }
+    need(x && y && w && grad_out, "NULL input tensor with B > 0");
+    if (!grad_x && !grad_y && !grad_w) return;
+    tp_backward_launch(plan, B, x, y, w, grad_out, grad_x, grad_y, grad_w, ws, ws_bytes,
+                       as_stream(stream));
+  });
+}
+
+cgtp_status cgtp_workspace_size(cgtp_plan plan, cgtp_graph graph, int64_t B, int op, size_t* bytes) {
+  return guarded([&] {
+    need(plan != nullptr && bytes != nullptr, "NULL argument");
+    if (op == CGTP_OP_TP_BACKWARD) {
+      need(B >= 0, "B < 0");
+      *bytes = tp_backward_ws_bytes(plan, B);
+    } else if (op == CGTP_OP_CONV_BACKWARD) {
+      need(graph != nullptr, "graph is NULL");
+      *bytes = conv_backward_ws_bytes(plan, graph);
+    } else {
+      throw Error{CGTP_ERR_INVALID_ARG, "unknown op"};
+    }
+  });
+}
+
+cgtp_status cgtp_csr_from_coo(int64_t N, int64_t E, const int32_t* src, const int32_t* dst,
+                              int32_t* row_ptr, int32_t* src_sorted, int32_t* perm, void* stream) {
+  return guarded([&] {
+    need(N >= 0 && E >= 0, "negative size");
+    need(N < INT32_MAX && E < INT32_MAX, "graph too large for int32 indices");
+    need(row_ptr != nullptr, "row_ptr is NULL");
+    need(E == 0 || (src && dst && src_sorted && perm), "NULL edge array");
+    csr_from_coo_launch(N, E, src, dst, row_ptr, src_sorted, perm, as_stream(stream));
+  });
+}
+
+cgtp_status cgtp_graph_create(int64_t N, int64_t E, const int32_t* row_ptr, const int32_t* src,
+                              void* stream, cgtp_graph* out) {
+  return guarded([&] {
+    need(out != nullptr, "out handle is NULL");
+    *out = nullptr;
+    need(N >= 0 && E >= 0, "negative size");
+    need(N < INT32_MAX && E < INT32_MAX, "graph too large for int32 indices");
+    need(row_ptr != nullptr, "row_ptr is NULL");
+    need(E == 0 || src != nullptr, "src is NULL");
+    *out = graph_create(N, E, row_ptr, src, as_stream(stream));
+  });
+}
+
+cgtp_status cgtp_graph_destroy(cgtp_graph graph) {
+  return guarded([&] {
+    if (graph) graph_destroy(graph);
+  });
+}
+
+cgtp_status cgtp_graph_transpose(cgtp_graph graph, int32_t* col_ptr, int32_t* eid, void* stream) {
+  return guarded([&] {
+    need(graph != nullptr && col_ptr != nullptr, "NULL argument");
+    need(graph->E == 0 || eid != nullptr, "eid is NULL");
+    graph_transpose_copy(graph, col_ptr, eid, as_stream(stream));
+  });
+}
+
+cgtp_status cgtp_conv_forward(cgtp_plan plan, cgtp_graph graph, const void* x, const void* sh,
+                              const void* w, double scale, void* out, void* stream) {
+  return guarded([&] {
+    need(plan != nullptr && graph != nullptr, "NULL plan or graph");
+    if (plan->wkind != CGTP_W_PER_ROW)
+      throw Error{CGTP_ERR_UNSUPPORTED, "the convolution needs per-edge weights (CGTP_W_PER_ROW)"};
+    if (graph->N == 0) return;
+    need(out != nullptr, "out is NULL");
+    need(graph->E == 0 || (x && sh && w), "NULL input tensor");
+    conv_forward_launch(plan, graph, x, sh, w, scale, out, as_stream(stream));
+  });
+}
+
+cgtp_status cgtp_conv_backward(cgtp_plan plan, cgtp_graph graph, const void* x, const void* sh,
+                               const void* w, double scale, const void* grad_out, void* grad_x,
+                               void* grad_sh, void* grad_w, void* ws, size_t ws_bytes, void* stream) {
+  return guarded([&] {
+    need(plan != nullptr && graph != nullptr, "NULL plan or graph");
+    if (plan->wkind != CGTP_W_PER_ROW)
+      throw Error{CGTP_ERR_UNSUPPORTED, "the convolution needs per-edge weights (CGTP_W_PER_ROW)"};
+    need(graph->E == 0 || (x && sh && w && grad_out), "NULL input tensor");
+    conv_backward_launch(plan, graph, x, sh, w, scale, grad_out, grad_x, grad_sh, grad_w, ws,
+                         ws_bytes, as_stream(stream));
+  });
+}
+
+cgtp_status cgtp_sh_forward(int lmax, cgtp_dtype dtype, int64_t n, const void* vec, void* sh,
+                            void* stream) {
+  return guarded([&] {
+    need(n >= 0, "n < 0");
+    if (lmax < 0 || lmax > kLmax) throw Error{CGTP_ERR_UNSUPPORTED, "lmax outside 0..CGTP_LMAX"};
+    need(dtype == CGTP_F32 || dtype == CGTP_F64 || dtype == CGTP_BF16, "bad dtype");
+    if (n == 0) return;
+    need(vec && sh, "NULL tensor");
+    sh_forward_launch(lmax, dtype, n, vec, sh, as_stream(stream));
+  });
+}
+
+cgtp_status cgtp_sh_backward(int lmax, cgtp_dtype dtype, int64_t n, const void* vec,
+                             const void* grad_sh, void* grad_vec, void* stream) {
+  return guarded([&] {
+    need(n >= 0, "n < 0");
+    if (lmax < 0 || lmax > kLmax) throw Error{CGTP_ERR_UNSUPPORTED, "lmax outside 0..CGTP_LMAX"};
+    need(dtype == CGTP_F32 || dtype == CGTP_F64 || dtype == CGTP_BF16, "bad dtype");
+    if (n == 0) return;
+    need(vec && grad_sh && grad_vec, "NULL tensor");
+    sh_backward_launch(lmax, dtype, n, vec, grad_sh, grad_vec, as_stream(stream));
+  });
+}
+
+}  // extern "C"

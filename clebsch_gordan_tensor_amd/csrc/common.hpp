@@ -1,0 +1,138 @@
+// Internal types shared by the planner, the launchers and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "cgtp.h"
+
+namespace cgtp {
+
+constexpr int kLmax = CGTP_LMAX;
+constexpr int kBlock = 256;  // threads per workgroup for the row kernels
+
+// ---------------------------------------------------------------- errors
+void set_error(const std::string& msg);
+struct Error {
+  cgtp_status code;
+  std::string msg;
+};
+#define CGTP_CHECK_HIP(expr)                                                              \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess)                                                                 \
+      throw ::cgtp::Error{CGTP_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)}; \
+  } while (0)
+
+// ------------------------------------------------------------ plan types
+struct Irrep {
+  int mul, l, p;
+};
+
+// One path in path order. Offsets are element offsets inside a row.
+struct PathInfo {
+  int i1, i2, l1, l2, l3, p3, mul;
+  int x_off, y_off, out_off, w_off, coef_off;
+  int i2_end;  // one past the last path of the run with the same (i1, i2)
+};
+
+// One x block with the contiguous range of paths that read it.
+struct BlockInfo {
+  int l1, mul, x_off, path_begin, path_end;
+};
+
+// Device copies (plain 32-bit fields).
+struct alignas(16) PathDev {
+  int32_t l2, l3, y_off, out_off;
+  int32_t w_off, coef_off, i2_end, mul;
+  int32_t l1, x_off, pad0, pad1;
+};
+struct alignas(16) BlockDev {
+  int32_t l1, mul, x_off, path_begin;
+  int32_t path_end, pad0, pad1, pad2;
+};
+
+struct DevTables {
+  PathDev* paths = nullptr;
+  BlockDev* blocks = nullptr;
+  void* coef = nullptr;          // float (f32/bf16 plans) or double (f64 plans)
+  int32_t* slot_paths = nullptr;  // fused convolution: path index per (block, slot), -1 = none
+  int32_t* slot_off = nullptr;    // first slot of each block
+};
+
+}  // namespace cgtp
+
+struct cgtp_plan_s {
+  std::vector<cgtp::Irrep> X, Y, O;
+  std::vector<cgtp::PathInfo> paths;
+  std::vector<cgtp::BlockInfo> blocks;
+  std::vector<std::vector<double>> cg_dense;  // per path, [2l1+1][2l2+1][2l3+1]
+  std::vector<double> coef64;                 // packed in kernel pattern order
+  std::vector<float> coef32;
+  int64_t dim_x = 0, dim_y = 0, dim_out = 0, w_numel = 0;
+  int max_mul = 0;
+  int vec = 1;  // channels per lane of the vectorised kernels
+  // Fused convolution (edge loop outside, all paths of one x block in
+  // registers): possible when each degree occurs at most once in y. Slots of
+  // block b are every (l2, l3) with l2, l3 <= conv_L and |l1-l2| <= l3 <= l1+l2,
+  // ordered by l2 then l3; slot_paths maps them to path indices (-1 = absent).
+  bool conv_fused = false;
+  int conv_L = 0;
+  int yoff_by_l[CGTP_LMAX + 1] = {-1, -1, -1, -1, -1};
+  std::vector<int32_t> slot_paths, slot_off;
+  cgtp_dtype dtype = CGTP_F32;
+  cgtp_wkind wkind = CGTP_W_SHARED;
+  std::mutex mu;
+  std::map<int, cgtp::DevTables> dev;  // per HIP device id
+};
+
+namespace cgtp {
+
+// Planner (plan.cpp).
+cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const char* mode,
+                        cgtp_dtype dtype, cgtp_wkind wkind);
+// Real CG block by the ladder construction, [2l1+1][2l2+1][2l3+1], fp64.
+std::vector<double> real_cg_ladder(int l1, int l2, int l3);
+// Device tables of a plan on the current device (uploaded on first use).
+const DevTables& plan_tables(cgtp_plan_s* plan);
+void free_plan_tables(cgtp_plan_s* plan);
+
+inline size_t dtype_size(cgtp_dtype d) { return d == CGTP_F64 ? 8 : (d == CGTP_BF16 ? 2 : 4); }
+inline size_t acc_size(cgtp_dtype d) { return d == CGTP_F64 ? 8 : 4; }
+
+// Launchers (tp_kernels.hip).
+void tp_forward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* y, const void* w,
+                       void* out, hipStream_t stream);
+void tp_backward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* y,
+                        const void* w, const void* g, void* dx, void* dy, void* dw, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+size_t tp_backward_ws_bytes(const cgtp_plan_s* plan, int64_t B);
+
+// Backward over generic rows: row r reads x row x_idx[r] (or r), grad_out row
+// g_idx[r] (or r) times g_scale, y/w row r; writes grad_x row r either in the
+// storage type (dx) or the accumulation type (dx_ws), grad_y row r, and grad_w
+// row r (dw, storage type) or its accumulation-type partial (dw_ws).
+struct TPBackwardRows {
+  int64_t rows = 0;
+  const void* x = nullptr;
+  const int32_t* x_idx = nullptr;
+  const void* y = nullptr;
+  const void* w = nullptr;
+  int64_t w_stride = 0;
+  const void* g = nullptr;
+  const int32_t* g_idx = nullptr;
+  double g_scale = 1.0;
+  void* dx = nullptr;
+  void* dx_ws = nullptr;
+  void* dy = nullptr;
+  void* dw = nullptr;
+  void* dw_ws = nullptr;
+};
+void tp_backward_rows(cgtp_plan_s* plan, const TPBackwardRows& r, hipStream_t stream);
+
+}  // namespace cgtp

@@ -1,0 +1,269 @@
+// Message-passing convolution over CSR-by-destination edges.
+//
+// What is computed: the tensor-field-network convolution of the MolSSI e3nn
+// course, lesson 06a, m_ij = (R(|r_ij|) Y(rhat_ij)) (x)_w h_j summed at the
+// receiver i, with the radial factor given as per-edge, per-path, per-channel
+// weights and a constant scale (the sqrt(num_neighbors) normalisation of
+// e3nn_mlx "Modular v2106 point models"):
+//   out[n] = scale * sum_{e: dst(e)=n} TP(x[src(e)], sh[e], w[e]).
+// "E3J: An Efficient and Open-Source Backend for Euclidean Equivariant
+// Operations on GPU and TPU", 3.1.2 / E.2.2 / E.3 / E.4: stream the edges of a
+// receiver, aggregate in CSR order without atomics, never write edge messages
+// to memory (complex layers that materialise edge-wise intermediates pay for
+// it in traffic, as the Sobek card page notes).
+//
+// Forward, fused form (each degree occurs at most once in y): one wave owns
+// (receiver n, x block b, 64-channel chunk); lanes are channels. For every
+// edge of n it gathers x[src] for block b (one coalesced 256-byte run per m1),
+// reads sh[e] with uniform loads, streams the block's weights w[e, p, :], and
+// accumulates every path of the block in registers - the register layout of
+// the accumulators is fixed at compile time by (l1 of the block, L), so the
+// paths live at constant register offsets. One store per output element.
+// Forward, general form (any y): one wave per (receiver, path, chunk).
+//
+// Backward: the row-parallel tensor-product backward runs over edges with x
+// gathered by src and grad_out gathered by dst (times scale): it writes
+// grad_sh[e] and grad_w[e] directly and a per-edge grad_x partial; the partials
+// are then summed per source node over the transpose, in CSR-position order.
+#pragma once
+
+#include "cg_pattern.h"
+#include "common.hpp"
+#include "device_util.hpp"
+#include "graph.hpp"
+#include "tp_core.hpp"
+
+namespace cgtp {
+
+// ------------------------------------------------- compile-time slot layout
+struct SlotT {
+  int l2, l3, acc;  // acc: first accumulator register of the slot
+};
+
+constexpr int imin(int a, int b) { return a < b ? a : b; }
+constexpr int idiff(int a, int b) { return a > b ? a - b : b - a; }
+
+constexpr int slot_count(int L1, int L) {
+  int n = 0;
+  for (int l2 = 0; l2 <= L; ++l2)
+    for (int l3 = idiff(L1, l2); l3 <= imin(L1 + l2, L); ++l3) ++n;
+  return n;
+}
+constexpr int slot_regs(int L1, int L) {
+  int n = 0;
+  for (int l2 = 0; l2 <= L; ++l2)
+    for (int l3 = idiff(L1, l2); l3 <= imin(L1 + l2, L); ++l3) n += 2 * l3 + 1;
+  return n;
+}
+
+template <int L1, int L>
+struct Slots {
+  static constexpr int NS = slot_count(L1, L);
+  static constexpr int NACC = slot_regs(L1, L);
+  struct Arr {
+    SlotT p[NS > 0 ? NS : 1];
+  };
+  static constexpr Arr build() {
+    Arr a{};
+    int k = 0, acc = 0;
+    for (int l2 = 0; l2 <= L; ++l2)
+      for (int l3 = idiff(L1, l2); l3 <= imin(L1 + l2, L); ++l3) {
+        a.p[k++] = SlotT{l2, l3, acc};
+        acc += 2 * l3 + 1;
+      }
+    return a;
+  }
+  static constexpr Arr arr = build();
+};
+
+struct ConvArgs {
+  const PathDev* paths;
+  const BlockDev* blocks;
+  const void* coef;
+  const int32_t* slot_paths;
+  const int32_t* slot_off;
+  const int32_t* row_ptr;
+  const int32_t* src;
+  const void* x;
+  const void* sh;
+  const void* w;
+  void* out;
+  int64_t N;
+  int dim_x, dim_y, dim_out, W;
+  int nblocks, nchunks, npaths, L;
+  int yoff[kLmax + 1];
+  double scale;
+};
+
+constexpr int kWaves = kBlock / 64;
+
+__device__ __forceinline__ int conv_wave_id() { return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6); }
+
+// ------------------------------------------------------------ fused forward
+template <typename T, typename A, int L1, int L>
+__device__ __forceinline__ void fwd_fused_block(const ConvArgs& a, int64_t n, int b,
+                                                const BlockDev& blk, int c) {
+  using S = Slots<L1, L>;
+  constexpr int NS = S::NS;
+  A acc[S::NACC];
+#pragma unroll
+  for (int i = 0; i < S::NACC; ++i) acc[i] = A(0);
+  int pid[NS], woff[NS], coff[NS];
+  const int so = a.slot_off[b];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    pid[s] = a.slot_paths[so + s];
+    woff[s] = pid[s] >= 0 ? a.paths[pid[s]].w_off : 0;
+    coff[s] = pid[s] >= 0 ? a.paths[pid[s]].coef_off : 0;
+  }
+  const A* __restrict__ cf = static_cast<const A*>(a.coef);
+  const T* __restrict__ X = static_cast<const T*>(a.x);
+  const int32_t e0 = a.row_ptr[n], e1 = a.row_ptr[n + 1];
+  for (int32_t e = e0; e < e1; ++e) {
+    const int64_t j = a.src[e];
+    A xb[2 * L1 + 1][1];
+#pragma unroll
+    for (int m = 0; m < 2 * L1 + 1; ++m) xb[m][0] = to_acc<A>(X[j * a.dim_x + blk.x_off + m * blk.mul + c]);
+    const T* __restrict__ Ye = static_cast<const T*>(a.sh) + int64_t(e) * a.dim_y;
+    const T* __restrict__ we = static_cast<const T*>(a.w) + int64_t(e) * a.W;
+    A ycur[2 * L + 1];
+    static_for<0, NS>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      constexpr SlotT st = S::arr.p[i];
+      constexpr int prev = i > 0 ? i - 1 : 0;
+      constexpr bool first_of_l2 = (i == 0) || (S::arr.p[prev].l2 != st.l2);
+      if constexpr (first_of_l2) {
+        const int yo = a.yoff[st.l2];
+        if (yo >= 0) {
+#pragma unroll
+          for (int m = 0; m < 2 * st.l2 + 1; ++m) ycur[m] = to_acc<A>(Ye[yo + m]);
+        }
+      }
+      if (pid[i] >= 0) {
+        const A wv = to_acc<A>(we[woff[i] + c]);
+        A yb[2 * st.l2 + 1];
+#pragma unroll
+        for (int m = 0; m < 2 * st.l2 + 1; ++m) yb[m] = ycur[m];
+        A t[2 * st.l3 + 1][1];
+        fwd_core<L1, st.l2, st.l3, 1, A>(xb, yb, cf + coff[i], t);
+#pragma unroll
+        for (int m = 0; m < 2 * st.l3 + 1; ++m) acc[st.acc + m] = fma(wv, t[m][0], acc[st.acc + m]);
+      }
+    });
+  }
+  T* __restrict__ outn = static_cast<T*>(a.out) + n * a.dim_out;
+  const A sc = A(a.scale);
+  static_for<0, NS>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    constexpr SlotT st = S::arr.p[i];
+    if (pid[i] >= 0) {
+      const PathDev pd = a.paths[pid[i]];
+#pragma unroll
+      for (int m = 0; m < 2 * st.l3 + 1; ++m) from_acc(outn[pd.out_off + m * pd.mul + c], sc * acc[st.acc + m]);
+    }
+  });
+}
+
+template <typename T, typename A>
+__global__ __launch_bounds__(kBlock) void conv_fwd_fused_kernel(ConvArgs a) {
+  const int64_t item = int64_t(blockIdx.x) * kWaves + conv_wave_id();
+  const int64_t per_node = int64_t(a.nblocks) * a.nchunks;
+  const int64_t n = item / per_node;
+  if (n >= a.N) return;
+  const int rem = int(item - n * per_node);
+  const int b = rem / a.nchunks;
+  const int chunk = rem - b * a.nchunks;
+  const BlockDev blk = a.blocks[b];
+  const int c = chunk * 64 + int(threadIdx.x & 63);
+  if (c >= blk.mul) return;
+  static_for<0, kLmax + 1>([&](auto L1c) {
+    constexpr int L1 = decltype(L1c)::value;
+    if (blk.l1 == L1) {
+      static_for<0, kLmax + 1>([&](auto Lc) {
+        constexpr int L = decltype(Lc)::value;
+        if constexpr (Slots<L1, L>::NS > 0) {
+          if (a.L == L) fwd_fused_block<T, A, L1, L>(a, n, b, blk, c);
+        }
+      });
+    }
+  });
+}
+
+// ----------------------------------------------------------- general forward
+template <typename T, typename A, int L1, int L2, int L3>
+__device__ __forceinline__ void fwd_general_path(const ConvArgs& a, int64_t n, const PathDev& pd, int c) {
+  A acc[2 * L3 + 1];
+#pragma unroll
+  for (int m = 0; m < 2 * L3 + 1; ++m) acc[m] = A(0);
+  const A* __restrict__ cf = static_cast<const A*>(a.coef) + pd.coef_off;
+  const T* __restrict__ X = static_cast<const T*>(a.x);
+  const int32_t e0 = a.row_ptr[n], e1 = a.row_ptr[n + 1];
+  for (int32_t e = e0; e < e1; ++e) {
+    const int64_t j = a.src[e];
+    A xb[2 * L1 + 1][1];
+#pragma unroll
+    for (int m = 0; m < 2 * L1 + 1; ++m) xb[m][0] = to_acc<A>(X[j * a.dim_x + pd.x_off + m * pd.mul + c]);
+    const T* __restrict__ Ye = static_cast<const T*>(a.sh) + int64_t(e) * a.dim_y;
+    A yb[2 * L2 + 1];
+#pragma unroll
+    for (int m = 0; m < 2 * L2 + 1; ++m) yb[m] = to_acc<A>(Ye[pd.y_off + m]);
+    const A wv = to_acc<A>(static_cast<const T*>(a.w)[int64_t(e) * a.W + pd.w_off + c]);
+    A t[2 * L3 + 1][1];
+    fwd_core<L1, L2, L3, 1, A>(xb, yb, cf, t);
+#pragma unroll
+    for (int m = 0; m < 2 * L3 + 1; ++m) acc[m] = fma(wv, t[m][0], acc[m]);
+  }
+  T* __restrict__ outn = static_cast<T*>(a.out) + n * a.dim_out;
+  const A sc = A(a.scale);
+#pragma unroll
+  for (int m = 0; m < 2 * L3 + 1; ++m) from_acc(outn[pd.out_off + m * pd.mul + c], sc * acc[m]);
+}
+
+template <typename T, typename A>
+__global__ __launch_bounds__(kBlock) void conv_fwd_general_kernel(ConvArgs a) {
+  const int64_t item = int64_t(blockIdx.x) * kWaves + conv_wave_id();
+  const int64_t per_node = int64_t(a.npaths) * a.nchunks;
+  const int64_t n = item / per_node;
+  if (n >= a.N) return;
+  const int rem = int(item - n * per_node);
+  const int p = rem / a.nchunks;
+  const int chunk = rem - p * a.nchunks;
+  const PathDev pd = a.paths[p];
+  const int c = chunk * 64 + int(threadIdx.x & 63);
+  if (c >= pd.mul) return;
+  static_for<0, kLmax + 1>([&](auto A1) {
+    constexpr int L1 = decltype(A1)::value;
+    if (pd.l1 == L1) {
+      static_for<0, kLmax + 1>([&](auto A2) {
+        constexpr int L2 = decltype(A2)::value;
+        if (pd.l2 == L2) {
+          static_for<0, kLmax + 1>([&](auto A3) {
+            constexpr int L3 = decltype(A3)::value;
+            if constexpr (L3 >= idiff(L1, L2) && L3 <= L1 + L2) {
+              if (pd.l3 == L3) fwd_general_path<T, A, L1, L2, L3>(a, n, pd, c);
+            }
+          });
+        }
+      });
+    }
+  });
+}
+
+// ------------------------------------------------------------ typed launchers
+// One translation unit per (kind, storage type): inst/conv_*.hip.
+template <typename T>
+void conv_fwd_fused_typed(const ConvArgs& a, dim3 grid, hipStream_t s) {
+  using A = typename AccOf<T>::type;
+  hipLaunchKernelGGL((conv_fwd_fused_kernel<T, A>), grid, dim3(kBlock), 0, s, a);
+}
+template <typename T>
+void conv_fwd_general_typed(const ConvArgs& a, dim3 grid, hipStream_t s) {
+  using A = typename AccOf<T>::type;
+  hipLaunchKernelGGL((conv_fwd_general_kernel<T, A>), grid, dim3(kBlock), 0, s, a);
+}
+
+#define CGTP_CONV_EXTERN(T)                                                        \
+  extern template void conv_fwd_fused_typed<T>(const ConvArgs&, dim3, hipStream_t); \
+  extern template void conv_fwd_general_typed<T>(const ConvArgs&, dim3, hipStream_t);
+
+}  // namespace cgtp

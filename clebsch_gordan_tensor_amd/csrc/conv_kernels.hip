@@ -1,0 +1,132 @@
+// Launchers of the message-passing convolution (kernels in conv_impl.hpp).
+#include "conv_impl.hpp"
+
+namespace cgtp {
+
+CGTP_CONV_EXTERN(float)
+CGTP_CONV_EXTERN(double)
+CGTP_CONV_EXTERN(bf16)
+
+namespace {
+
+// ------------------------------------------------------- backward helpers
+template <typename T, typename A>
+__global__ __launch_bounds__(kBlock) void dx_gather_kernel(const int32_t* __restrict__ col_ptr,
+                                                           const int32_t* __restrict__ eid,
+                                                           const A* __restrict__ part, T* __restrict__ dx,
+                                                           int dim_x) {
+  const int64_t n = blockIdx.x;
+  const int32_t t0 = col_ptr[n], t1 = col_ptr[n + 1];
+  for (int k = threadIdx.x; k < dim_x; k += kBlock) {
+    A s = A(0);
+    for (int32_t t = t0; t < t1; ++t) s += part[int64_t(eid[t]) * dim_x + k];
+    from_acc(dx[n * dim_x + k], s);
+  }
+}
+
+ConvArgs make_conv_args(cgtp_plan_s* plan, const DevTables& t, const cgtp_graph_s* g) {
+  ConvArgs a{};
+  a.paths = t.paths;
+  a.blocks = t.blocks;
+  a.coef = t.coef;
+  a.slot_paths = t.slot_paths;
+  a.slot_off = t.slot_off;
+  a.row_ptr = g->row_ptr;
+  a.src = g->src;
+  a.N = g->N;
+  a.dim_x = int(plan->dim_x);
+  a.dim_y = int(plan->dim_y);
+  a.dim_out = int(plan->dim_out);
+  a.W = int(plan->w_numel);
+  a.nblocks = int(plan->blocks.size());
+  a.npaths = int(plan->paths.size());
+  a.nchunks = (plan->max_mul + 63) / 64;
+  a.L = plan->conv_L;
+  for (int l = 0; l <= kLmax; ++l) a.yoff[l] = plan->yoff_by_l[l];
+  return a;
+}
+
+template <typename T>
+void fwd_typed(cgtp_plan_s* plan, const ConvArgs& a, hipStream_t s) {
+  const int64_t per_node = plan->conv_fused ? int64_t(a.nblocks) * a.nchunks : int64_t(a.npaths) * a.nchunks;
+  const int64_t items = a.N * per_node;
+  const dim3 grid(unsigned((items + kWaves - 1) / kWaves));
+  if (plan->conv_fused)
+    conv_fwd_fused_typed<T>(a, grid, s);
+  else
+    conv_fwd_general_typed<T>(a, grid, s);
+  CGTP_CHECK_HIP(hipGetLastError());
+}
+
+template <typename T>
+void dx_gather(const cgtp_graph_s* g, const void* part, void* dx, int dim_x, hipStream_t s) {
+  using A = typename AccOf<T>::type;
+  hipLaunchKernelGGL((dx_gather_kernel<T, A>), dim3(unsigned(g->N)), dim3(kBlock), 0, s, g->col_ptr, g->eid,
+                     static_cast<const A*>(part), static_cast<T*>(dx), dim_x);
+  CGTP_CHECK_HIP(hipGetLastError());
+}
+
+}  // namespace
+
+void conv_forward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x, const void* sh,
+                         const void* w, double scale, void* out, hipStream_t s) {
+  if (g->E == 0) {
+    CGTP_CHECK_HIP(hipMemsetAsync(out, 0, size_t(g->N) * plan->dim_out * dtype_size(plan->dtype), s));
+    return;
+  }
+  const DevTables& t = plan_tables(plan);
+  ConvArgs a = make_conv_args(plan, t, g);
+  a.x = x;
+  a.sh = sh;
+  a.w = w;
+  a.out = out;
+  a.scale = scale;
+  switch (plan->dtype) {
+    case CGTP_F32: fwd_typed<float>(plan, a, s); break;
+    case CGTP_F64: fwd_typed<double>(plan, a, s); break;
+    case CGTP_BF16: fwd_typed<bf16>(plan, a, s); break;
+  }
+}
+
+size_t conv_backward_ws_bytes(const cgtp_plan_s* plan, const cgtp_graph_s* g) {
+  return size_t(g->E) * size_t(plan->dim_x) * acc_size(plan->dtype);
+}
+
+void conv_backward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x, const void* sh,
+                          const void* w, double scale, const void* grad_out, void* grad_x,
+                          void* grad_sh, void* grad_w, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (g->E == 0) {
+    if (grad_x && g->N > 0)
+      CGTP_CHECK_HIP(hipMemsetAsync(grad_x, 0, size_t(g->N) * plan->dim_x * dtype_size(plan->dtype), s));
+    return;
+  }
+  if (grad_x) {
+    const size_t need = conv_backward_ws_bytes(plan, g);
+    if (!ws || ws_bytes < need)
+      throw Error{CGTP_ERR_WORKSPACE, "conv_backward needs " + std::to_string(need) + " workspace bytes"};
+  }
+  if (!grad_x && !grad_sh && !grad_w) return;
+  TPBackwardRows r;
+  r.rows = g->E;
+  r.x = x;
+  r.x_idx = g->src;
+  r.y = sh;
+  r.w = w;
+  r.w_stride = plan->w_numel;
+  r.g = grad_out;
+  r.g_idx = g->dst;
+  r.g_scale = scale;
+  r.dx_ws = grad_x ? ws : nullptr;
+  r.dy = grad_sh;
+  r.dw = grad_w;
+  tp_backward_rows(plan, r, s);
+  if (grad_x) {
+    switch (plan->dtype) {
+      case CGTP_F32: dx_gather<float>(g, ws, grad_x, int(plan->dim_x), s); break;
+      case CGTP_F64: dx_gather<double>(g, ws, grad_x, int(plan->dim_x), s); break;
+      case CGTP_BF16: dx_gather<bf16>(g, ws, grad_x, int(plan->dim_x), s); break;
+    }
+  }
+}
+
+}  // namespace cgtp

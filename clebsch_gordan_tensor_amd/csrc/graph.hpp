@@ -1,0 +1,39 @@
+// Graph handle, convolution and harmonics launchers.
+#pragma once
+
+#include "common.hpp"
+
+struct cgtp_graph_s {
+  int64_t N = 0, E = 0;
+  const int32_t* row_ptr = nullptr;  // caller-owned CSR by destination
+  const int32_t* src = nullptr;
+  int32_t* col_ptr = nullptr;  // owned: transpose (edges grouped by source)
+  int32_t* eid = nullptr;      // CSR position of each source-ordered edge
+  int32_t* dst = nullptr;      // owned: destination of each CSR edge
+  int device = 0;
+};
+
+namespace cgtp {
+
+void csr_from_coo_launch(int64_t N, int64_t E, const int32_t* src, const int32_t* dst,
+                         int32_t* row_ptr, int32_t* src_sorted, int32_t* perm, hipStream_t s);
+cgtp_graph_s* graph_create(int64_t N, int64_t E, const int32_t* row_ptr, const int32_t* src,
+                           hipStream_t s);
+void graph_destroy(cgtp_graph_s* g);
+void graph_transpose_copy(const cgtp_graph_s* g, int32_t* col_ptr, int32_t* eid, hipStream_t s);
+
+void conv_forward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x, const void* sh,
+                         const void* w, double scale, void* out, hipStream_t s);
+void conv_backward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x, const void* sh,
+                          const void* w, double scale, const void* grad_out, void* grad_x,
+                          void* grad_sh, void* grad_w, void* ws, size_t ws_bytes, hipStream_t s);
+size_t conv_backward_ws_bytes(const cgtp_plan_s* plan, const cgtp_graph_s* g);
+
+void sh_forward_launch(int lmax, cgtp_dtype dtype, int64_t n, const void* vec, void* sh, hipStream_t s);
+void sh_backward_launch(int lmax, cgtp_dtype dtype, int64_t n, const void* vec, const void* grad_sh,
+                        void* grad_vec, hipStream_t s);
+
+// Exclusive prefix sum of counts[0..n) into out[0..n] (out[n] = total), int32.
+void exclusive_scan_i32(const int32_t* counts, int32_t* out, int64_t n, hipStream_t s);
+
+}  // namespace cgtp

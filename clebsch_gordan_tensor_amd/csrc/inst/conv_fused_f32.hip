@@ -1,0 +1,6 @@
+// Instantiation of the fused convolution forward kernel for storage type float.
+#include "../conv_impl.hpp"
+
+namespace cgtp {
+template void conv_fwd_fused_typed<float>(const ConvArgs&, dim3, hipStream_t);
+}  // namespace cgtp

@@ -1,0 +1,6 @@
+// Instantiation of the fwd tensor-product kernel for storage type double, 1 channel(s) per lane.
+#include "../tp_impl.hpp"
+
+namespace cgtp {
+template void tp_fwd_typed<double, 1>(const TPArgs&, hipStream_t);
+}  // namespace cgtp

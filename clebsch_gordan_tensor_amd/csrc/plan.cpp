@@ -1,0 +1,400 @@
+// Planner: irreps parsing, path enumeration, Clebsch-Gordan tables.
+//
+// Irreps strings and the parity rule: MolSSI e3nn course, lessons 02a and 03a.
+// CG values: the construction of "E3J: An Efficient and Open-Source Backend
+// for Euclidean Equivariant Operations on GPU and TPU", appendix G.2 - the
+// top-weight vector of each coupled degree solves the raising-operator
+// condition (a triangular, here bidiagonal, system) and every lower weight
+// follows by applying the lowering operator and normalising. The complex
+// (Condon-Shortley) result is then taken to the real harmonic basis.
+#include <algorithm>
+#include <cctype>
+#include <cmath>
+#include <complex>
+#include <cstring>
+#include <memory>
+#include <set>
+#include <utility>
+
+#include "cg_pattern.h"
+#include "common.hpp"
+
+namespace cgtp {
+
+namespace {
+
+Error parse_error(const std::string& s, const std::string& why) {
+  return Error{CGTP_ERR_PARSE, "irreps '" + s + "': " + why};
+}
+
+std::vector<Irrep> parse_irreps(const char* cstr) {
+  std::string s;
+  for (const char* c = cstr; *c; ++c)
+    if (!std::isspace(static_cast<unsigned char>(*c))) s.push_back(*c);
+  std::vector<Irrep> out;
+  if (s.empty()) return out;
+  size_t pos = 0;
+  while (true) {
+    size_t end = s.find('+', pos);
+    std::string t = s.substr(pos, end == std::string::npos ? std::string::npos : end - pos);
+    if (t.empty()) throw parse_error(cstr, "empty term");
+    long mul = 1;
+    size_t i = 0;
+    size_t xpos = t.find('x');
+    if (xpos != std::string::npos) {
+      if (xpos == 0) throw parse_error(cstr, "missing multiplicity before 'x'");
+      for (size_t k = 0; k < xpos; ++k)
+        if (!std::isdigit(static_cast<unsigned char>(t[k]))) throw parse_error(cstr, "bad multiplicity");
+      if (xpos > 9) throw parse_error(cstr, "multiplicity too large");
+      mul = std::stol(t.substr(0, xpos));
+      i = xpos + 1;
+    }
+    size_t j = i;
+    while (j < t.size() && std::isdigit(static_cast<unsigned char>(t[j]))) ++j;
+    if (j == i || j > i + 4) throw parse_error(cstr, "bad degree in '" + t + "'");
+    if (j + 1 != t.size() || (t[j] != 'e' && t[j] != 'o'))
+      throw parse_error(cstr, "term '" + t + "' must end in e or o");
+    if (mul < 1) throw parse_error(cstr, "multiplicity must be >= 1");
+    out.push_back(Irrep{static_cast<int>(mul), std::stoi(t.substr(i, j - i)), t[j] == 'e' ? 1 : -1});
+    if (end == std::string::npos) break;
+    pos = end + 1;
+  }
+  return out;
+}
+
+// ladder coefficients: J+|j m> = up(j,m)|j m+1>, J-|j m> = dn(j,m)|j m-1>
+double up(int j, int m) { return std::sqrt(double(j) * (j + 1) - double(m) * (m + 1)); }
+double dn(int j, int m) { return std::sqrt(double(j) * (j + 1) - double(m) * (m - 1)); }
+
+// Complex CG block <j1 m1 j2 m2 | J M> as dense [2j1+1][2j2+1][2J+1].
+std::vector<double> complex_cg_ladder(int j1, int j2, int J) {
+  const int n1 = 2 * j1 + 1, n2 = 2 * j2 + 1, n3 = 2 * J + 1;
+  std::vector<double> C(size_t(n1) * n2 * n3, 0.0);
+  auto at = [&](int m1, int m2, int M) -> double& {
+    return C[(size_t(m1 + j1) * n2 + (m2 + j2)) * n3 + (M + J)];
+  };
+  // Top weight |J J> = sum_m1 a[m1] |m1>|J-m1>. The raising condition
+  // (J1+ + J2+)|J J> = 0 couples neighbours only: for every k,
+  //   a[k-1] up(j1, k-1) + a[k] up(j2, J-k) = 0,
+  // solved upward from the lowest allowed m1.
+  const int lo = std::max(-j1, J - j2), hi = std::min(j1, J + j2);
+  std::vector<double> a(size_t(hi - lo + 1), 0.0);
+  a[0] = 1.0;
+  for (int k = lo + 1; k <= hi; ++k)
+    a[size_t(k - lo)] = -a[size_t(k - 1 - lo)] * up(j1, k - 1) / up(j2, J - k);
+  double nrm = 0.0;
+  for (double v : a) nrm += v * v;
+  nrm = std::sqrt(nrm);
+  // Condon-Shortley: <j1 j1 j2 J-j1 | J J> > 0 (hi == j1 always holds here)
+  const double sgn = a.back() > 0 ? 1.0 : -1.0;
+  for (int k = lo; k <= hi; ++k) at(k, J - k, J) = sgn * a[size_t(k - lo)] / nrm;
+  // Lowering: |J M-1> = (J1- + J2-)|J M> / dn(J, M).
+  for (int M = J; M > -J; --M) {
+    const double inv = 1.0 / dn(J, M);
+    for (int m1 = -j1; m1 <= j1; ++m1) {
+      const int m2 = M - 1 - m1;
+      if (m2 < -j2 || m2 > j2) continue;
+      double v = 0.0;
+      if (m1 + 1 <= j1) v += at(m1 + 1, m2, M) * dn(j1, m1 + 1);  // J1- from m1+1
+      if (m2 + 1 <= j2) v += at(m1, m2 + 1, M) * dn(j2, m2 + 1);  // J2- from m2+1
+      at(m1, m2, M - 1) = v * inv;
+    }
+  }
+  return C;
+}
+
+// Real harmonics from complex ones: row = real m, column = complex M.
+//  m > 0: (Y^{-m} + (-1)^m Y^m)/sqrt2;  m = 0: Y^0;  m < 0: i (Y^m - (-1)^m Y^{-m})/sqrt2.
+std::complex<double> U(int l, int m, int M) {
+  const double r = 1.0 / std::sqrt(2.0);
+  const double s = (m % 2 == 0) ? 1.0 : -1.0;
+  if (m > 0) {
+    if (M == -m) return {r, 0.0};
+    if (M == m) return {s * r, 0.0};
+  } else if (m == 0) {
+    if (M == 0) return {1.0, 0.0};
+  } else {
+    if (M == m) return {0.0, r};
+    if (M == -m) return {0.0, -s * r};
+  }
+  (void)l;
+  return {0.0, 0.0};
+}
+
+}  // namespace
+
+std::vector<double> real_cg_ladder(int l1, int l2, int l3) {
+  const int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1, n3 = 2 * l3 + 1;
+  const std::vector<double> Cc = complex_cg_ladder(l1, l2, l3);
+  std::vector<std::complex<double>> X(size_t(n1) * n2 * n3);
+  for (int m1 = -l1; m1 <= l1; ++m1)
+    for (int m2 = -l2; m2 <= l2; ++m2)
+      for (int m3 = -l3; m3 <= l3; ++m3) {
+        // U(l, m, M) is nonzero only for M = +-m: visit each distinct M once
+        const int nM1 = m1 == 0 ? 1 : 2, nM2 = m2 == 0 ? 1 : 2, nM3 = m3 == 0 ? 1 : 2;
+        std::complex<double> acc = 0.0;
+        for (int a = 0; a < nM1; ++a)
+          for (int b = 0; b < nM2; ++b)
+            for (int d = 0; d < nM3; ++d) {
+              const int M1 = a ? -m1 : m1, M2 = b ? -m2 : m2, M3 = d ? -m3 : m3;
+              if (M1 + M2 != M3) continue;
+              const double c = Cc[(size_t(M1 + l1) * n2 + (M2 + l2)) * n3 + (M3 + l3)];
+              if (c == 0.0) continue;
+              acc += std::conj(U(l1, m1, M1)) * std::conj(U(l2, m2, M2)) * U(l3, m3, M3) * c;
+            }
+        X[(size_t(m1 + l1) * n2 + (m2 + l2)) * n3 + (m3 + l3)] = acc;
+      }
+  double re = 0.0, im = 0.0;
+  for (auto& v : X) {
+    re = std::max(re, std::abs(v.real()));
+    im = std::max(im, std::abs(v.imag()));
+  }
+  std::vector<double> C(X.size());
+  const bool take_re = re >= im;
+  for (size_t i = 0; i < X.size(); ++i) {
+    double v = take_re ? X[i].real() : X[i].imag();
+    C[i] = std::abs(v) < 1e-15 ? 0.0 : v;
+  }
+  // Sign rule: even paths C[0,0,0] > 0; odd paths first nonzero positive.
+  double ref = 0.0;
+  if ((l1 + l2 + l3) % 2 == 0) {
+    ref = C[(size_t(l1) * n2 + l2) * n3 + l3];
+  } else {
+    for (double v : C)
+      if (std::abs(v) > 1e-9) {
+        ref = v;
+        break;
+      }
+  }
+  if (ref < 0)
+    for (double& v : C) v = -v;
+  return C;
+}
+
+namespace {
+
+std::vector<double> real_cg_checked(int l1, int l2, int l3) {
+  std::vector<double> C = real_cg_ladder(l1, l2, l3);
+  const int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1, n3 = 2 * l3 + 1;
+  for (int a = 0; a < n3; ++a)
+    for (int b = 0; b < n3; ++b) {
+      double g = 0.0;
+      for (int i = 0; i < n1 * n2; ++i) g += C[size_t(i) * n3 + a] * C[size_t(i) * n3 + b];
+      if (std::abs(g - (a == b ? 1.0 : 0.0)) > 1e-12)
+        throw Error{CGTP_ERR_UNSUPPORTED, "internal: CG block not orthonormal"};
+    }
+  return C;
+}
+
+// Pack one path's coefficients in the kernels' compile-time order.
+template <int L1, int L2, int L3>
+void pack_one(const std::vector<double>& C, std::vector<double>& out) {
+  using P = Pattern<L1, L2, L3>;
+  const int n2 = 2 * L2 + 1, n3 = 2 * L3 + 1;
+  std::vector<char> covered(C.size(), 0);
+  for (int k = 0; k < P::NP; ++k) {
+    const PairT& pr = P::arr.p[k];
+    for (int t = 0; t < pr.n; ++t) {
+      const int m2 = t == 0 ? pr.m2a : pr.m2b;
+      const size_t idx = (size_t(pr.m1 + L1) * n2 + (m2 + L2)) * n3 + (pr.m3 + L3);
+      out.push_back(C[idx]);
+      covered[idx] = 1;
+    }
+  }
+  for (size_t i = 0; i < C.size(); ++i)
+    if (!covered[i] && std::abs(C[i]) > 1e-12)
+      throw Error{CGTP_ERR_UNSUPPORTED, "internal: CG entry outside the sparsity pattern"};
+}
+
+void pack_path(int l1, int l2, int l3, const std::vector<double>& C, std::vector<double>& out) {
+  bool done = false;
+  static_for<0, kLmax + 1>([&](auto A) {
+    static_for<0, kLmax + 1>([&](auto B) {
+      static_for<0, kLmax + 1>([&](auto D) {
+        constexpr int a = decltype(A)::value, b = decltype(B)::value, d = decltype(D)::value;
+        if constexpr (d >= (a > b ? a - b : b - a) && d <= a + b) {
+          if (!done && l1 == a && l2 == b && l3 == d) {
+            pack_one<a, b, d>(C, out);
+            done = true;
+          }
+        }
+      });
+    });
+  });
+  if (!done) throw Error{CGTP_ERR_UNSUPPORTED, "degree above CGTP_LMAX"};
+}
+
+}  // namespace
+
+cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const char* mode,
+                        cgtp_dtype dtype, cgtp_wkind wkind) {
+  if (!ix || !iy || !io || !mode) throw Error{CGTP_ERR_INVALID_ARG, "null irreps or mode"};
+  if (std::strcmp(mode, "uvu") != 0)
+    throw Error{CGTP_ERR_UNSUPPORTED, std::string("mode '") + mode + "' (only uvu)"};
+  if (dtype != CGTP_F32 && dtype != CGTP_F64 && dtype != CGTP_BF16)
+    throw Error{CGTP_ERR_INVALID_ARG, "bad dtype"};
+  if (wkind != CGTP_W_SHARED && wkind != CGTP_W_PER_ROW)
+    throw Error{CGTP_ERR_INVALID_ARG, "bad weight kind"};
+  auto plan = std::make_unique<cgtp_plan_s>();
+  plan->X = parse_irreps(ix);
+  plan->Y = parse_irreps(iy);
+  plan->O = parse_irreps(io);
+  plan->dtype = dtype;
+  plan->wkind = wkind;
+  for (auto* v : {&plan->X, &plan->Y, &plan->O})
+    for (const Irrep& r : *v)
+      if (r.l > kLmax) throw Error{CGTP_ERR_UNSUPPORTED, "degree " + std::to_string(r.l) + " > CGTP_LMAX"};
+  for (const Irrep& r : plan->Y)
+    if (r.mul != 1) throw Error{CGTP_ERR_UNSUPPORTED, "uvu needs multiplicity 1 on the second operand"};
+  std::set<std::pair<int, int>> allowed;
+  for (const Irrep& r : plan->O) allowed.insert({r.l, r.p});
+
+  std::vector<int> xoff, yoff;
+  int64_t o = 0;
+  for (const Irrep& r : plan->X) {
+    xoff.push_back(int(o));
+    o += int64_t(r.mul) * (2 * r.l + 1);
+    plan->max_mul = std::max(plan->max_mul, r.mul);
+  }
+  plan->dim_x = o;
+  o = 0;
+  for (const Irrep& r : plan->Y) {
+    yoff.push_back(int(o));
+    o += 2 * r.l + 1;
+  }
+  plan->dim_y = o;
+
+  int64_t out_off = 0, w_off = 0;
+  std::vector<double> coef;
+  for (int i1 = 0; i1 < int(plan->X.size()); ++i1) {
+    const Irrep& a = plan->X[i1];
+    BlockInfo blk{a.l, a.mul, xoff[i1], int(plan->paths.size()), 0};
+    for (int i2 = 0; i2 < int(plan->Y.size()); ++i2) {
+      const Irrep& b = plan->Y[i2];
+      const int run_begin = int(plan->paths.size());
+      for (int l3 = std::abs(a.l - b.l); l3 <= a.l + b.l; ++l3) {
+        const int p3 = a.p * b.p;
+        if (!allowed.count({l3, p3})) continue;
+        PathInfo p{};
+        p.i1 = i1; p.i2 = i2; p.l1 = a.l; p.l2 = b.l; p.l3 = l3; p.p3 = p3; p.mul = a.mul;
+        p.x_off = xoff[i1];
+        p.y_off = yoff[i2];
+        p.out_off = int(out_off);
+        p.w_off = int(w_off);
+        p.coef_off = int(coef.size());
+        std::vector<double> C = real_cg_checked(a.l, b.l, l3);
+        pack_path(a.l, b.l, l3, C, coef);
+        plan->cg_dense.push_back(std::move(C));
+        out_off += int64_t(a.mul) * (2 * l3 + 1);
+        w_off += a.mul;
+        plan->paths.push_back(p);
+      }
+      for (int k = run_begin; k < int(plan->paths.size()); ++k) plan->paths[k].i2_end = int(plan->paths.size());
+    }
+    blk.path_end = int(plan->paths.size());
+    if (blk.path_end > blk.path_begin) plan->blocks.push_back(blk);
+  }
+  if (plan->paths.empty()) throw Error{CGTP_ERR_UNSUPPORTED, "no path connects the irreps"};
+  if (out_off > INT32_MAX || w_off > INT32_MAX || plan->dim_x > INT32_MAX)
+    throw Error{CGTP_ERR_UNSUPPORTED, "row too large for 32-bit offsets"};
+  plan->dim_out = out_off;
+  plan->w_numel = w_off;
+  plan->coef64 = coef;
+  plan->coef32.assign(coef.begin(), coef.end());
+
+  // Channels per lane: 16-byte vectors when every multiplicity allows it.
+  const int vmax = dtype == CGTP_F64 ? 2 : 4;
+  bool ok = true;
+  for (const Irrep& r : plan->X) ok = ok && (r.mul % vmax == 0);
+  plan->vec = ok ? vmax : 1;
+
+  // Fused-convolution slot tables.
+  int ly = 0, lo = 0;
+  bool distinct = true;
+  for (int i2 = 0; i2 < int(plan->Y.size()); ++i2) {
+    const int l = plan->Y[i2].l;
+    if (plan->yoff_by_l[l] >= 0) distinct = false;
+    plan->yoff_by_l[l] = yoff[i2];
+    ly = std::max(ly, l);
+  }
+  for (const PathInfo& p : plan->paths) lo = std::max(lo, p.l3);
+  plan->conv_fused = distinct;
+  plan->conv_L = std::max(ly, lo);
+  if (distinct) {
+    const int L = plan->conv_L;
+    for (const BlockInfo& b : plan->blocks) {
+      plan->slot_off.push_back(int32_t(plan->slot_paths.size()));
+      for (int l2 = 0; l2 <= L; ++l2)
+        for (int l3 = std::abs(b.l1 - l2); l3 <= std::min(b.l1 + l2, L); ++l3) {
+          int32_t found = -1;
+          for (int q = b.path_begin; q < b.path_end; ++q)
+            if (plan->paths[q].l2 == l2 && plan->paths[q].l3 == l3) found = q;
+          plan->slot_paths.push_back(found);
+        }
+    }
+    plan->slot_off.push_back(int32_t(plan->slot_paths.size()));
+  }
+  return plan.release();
+}
+
+const DevTables& plan_tables(cgtp_plan_s* plan) {
+  int dev = 0;
+  CGTP_CHECK_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(plan->mu);
+  auto it = plan->dev.find(dev);
+  if (it != plan->dev.end()) return it->second;
+  std::vector<PathDev> pd;
+  for (const PathInfo& p : plan->paths)
+    pd.push_back(PathDev{p.l2, p.l3, p.y_off, p.out_off, p.w_off, p.coef_off, p.i2_end, p.mul,
+                         p.l1, p.x_off, 0, 0});
+  std::vector<BlockDev> bd;
+  for (const BlockInfo& b : plan->blocks)
+    bd.push_back(BlockDev{b.l1, b.mul, b.x_off, b.path_begin, b.path_end, 0, 0, 0});
+  DevTables t;
+  const bool f64 = plan->dtype == CGTP_F64;
+  const size_t cbytes = f64 ? plan->coef64.size() * 8 : plan->coef32.size() * 4;
+  try {
+    CGTP_CHECK_HIP(hipMalloc(&t.paths, pd.size() * sizeof(PathDev)));
+    CGTP_CHECK_HIP(hipMalloc(&t.blocks, bd.size() * sizeof(BlockDev)));
+    CGTP_CHECK_HIP(hipMalloc(&t.coef, std::max<size_t>(cbytes, 16)));
+    CGTP_CHECK_HIP(hipMemcpy(t.paths, pd.data(), pd.size() * sizeof(PathDev), hipMemcpyHostToDevice));
+    CGTP_CHECK_HIP(hipMemcpy(t.blocks, bd.data(), bd.size() * sizeof(BlockDev), hipMemcpyHostToDevice));
+    CGTP_CHECK_HIP(hipMemcpy(t.coef, f64 ? static_cast<const void*>(plan->coef64.data())
+                                         : static_cast<const void*>(plan->coef32.data()),
+                             cbytes, hipMemcpyHostToDevice));
+    if (plan->conv_fused) {
+      CGTP_CHECK_HIP(hipMalloc(&t.slot_paths, plan->slot_paths.size() * 4 + 4));
+      CGTP_CHECK_HIP(hipMalloc(&t.slot_off, plan->slot_off.size() * 4));
+      CGTP_CHECK_HIP(hipMemcpy(t.slot_paths, plan->slot_paths.data(), plan->slot_paths.size() * 4,
+                               hipMemcpyHostToDevice));
+      CGTP_CHECK_HIP(hipMemcpy(t.slot_off, plan->slot_off.data(), plan->slot_off.size() * 4,
+                               hipMemcpyHostToDevice));
+    }
+  } catch (...) {
+    (void)hipFree(t.paths);
+    (void)hipFree(t.blocks);
+    (void)hipFree(t.coef);
+    (void)hipFree(t.slot_paths);
+    (void)hipFree(t.slot_off);
+    throw;
+  }
+  return plan->dev.emplace(dev, t).first->second;
+}
+
+void free_plan_tables(cgtp_plan_s* plan) {
+  int cur = 0;
+  const bool have = hipGetDevice(&cur) == hipSuccess;
+  for (auto& kv : plan->dev) {
+    if (hipSetDevice(kv.first) == hipSuccess) {
+      (void)hipFree(kv.second.paths);
+      (void)hipFree(kv.second.blocks);
+      (void)hipFree(kv.second.coef);
+      (void)hipFree(kv.second.slot_paths);
+      (void)hipFree(kv.second.slot_off);
+    }
+  }
+  if (have) (void)hipSetDevice(cur);
+  plan->dev.clear();
+}
+
+}  // namespace cgtp

@@ -1,0 +1,351 @@
+// Row-parallel uvu Clebsch-Gordan tensor product, forward and backward.
+//
+// What is computed: the full CG tensor product x (x)_w y of "E3J: An Efficient
+// and Open-Source Backend for Euclidean Equivariant Operations on GPU and TPU",
+// section 3.1.1 (memory-bound; not a compute bottleneck for L <= 3), with the
+// uvu connection mode of the MolSSI e3nn course, lesson 03b, and the reverse
+// rules of E3J appendix E.1 (transposition of the bilinear map).
+//
+// Mapping on gfx950 (64-wide waves): a row is owned by a power-of-two group of
+// lanes; each lane owns VEC consecutive channels (16-byte loads/stores), so
+// every load/store instruction of a row moves one contiguous channel run.
+// The CG tables follow a compile-time sparsity pattern per (l1, l2, l3) and
+// are read with uniform (scalar) loads; per path the lane first forms
+// A[m1, m3] = sum_m2 C y[m2] for its row, then applies A to its channels
+// (the channel-parallel, feature-sequential order of E3J E.2.1, with the
+// coefficient cost amortised over VEC channels). Nothing is reduced across
+// lanes in the forward pass; the backward pass reduces grad_y across the
+// row's lanes with shuffles, and grad_w of shared weights in a fixed
+// two-stage order (no atomics anywhere).
+#pragma once
+
+#include "cg_pattern.h"
+#include "common.hpp"
+#include "device_util.hpp"
+#include "tp_core.hpp"
+
+namespace cgtp {
+
+struct TPArgs {
+  const PathDev* paths;
+  const BlockDev* blocks;
+  const void* coef;
+  const void* x;
+  const void* y;
+  const void* w;
+  const void* g;
+  void* out;
+  void* dx;
+  void* dy;
+  void* dw;     // per-row grad_w, storage type (PER_ROW plans)
+  void* dw_ws;  // per-row grad_w partials, accumulation type (SHARED plans)
+  void* dx_ws;  // per-row grad_x in the accumulation type (edge partials of the convolution)
+  const int32_t* x_idx;  // optional: x row of each row (gather)
+  const int32_t* g_idx;  // optional: grad_out row of each row (gather)
+  double g_scale;        // grad_out multiplier (1 for the plain tensor product)
+  int64_t B;
+  int64_t w_stride;  // elements between weight rows; 0 for shared weights
+  int dim_x, dim_y, dim_out, W;
+  int nblocks;
+  int lpr_log2;  // lanes per row = 1 << lpr_log2
+  int ngroups;   // channel groups per row = ceil(max_mul / VEC)
+};
+
+template <typename T, typename A, int VEC>
+struct TPFwd {
+  template <int L1, int L2, int L3>
+  __device__ static __forceinline__ void path(const TPArgs& a, const PathDev& pd,
+                                              const A (&xb)[2 * L1 + 1][VEC],
+                                              const A (&yb)[2 * L2 + 1], const T* wr, T* outr,
+                                              int c) {
+    A o[2 * L3 + 1][VEC];
+    fwd_core<L1, L2, L3, VEC, A>(xb, yb, static_cast<const A*>(a.coef) + pd.coef_off, o);
+    A wv[VEC];
+    VecIO<T, VEC>::load(wr + pd.w_off + c, wv);
+#pragma unroll
+    for (int m = 0; m < 2 * L3 + 1; ++m) {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) o[m][v] *= wv[v];
+      VecIO<T, VEC>::store(outr + pd.out_off + m * pd.mul + c, o[m]);
+    }
+  }
+
+  template <int L1, int L2>
+  __device__ static __forceinline__ void run(const TPArgs& a, int p, int pend,
+                                             const A (&xb)[2 * L1 + 1][VEC], const T* yr,
+                                             const T* wr, T* outr, int c) {
+    A yb[2 * L2 + 1];
+    const int yoff = a.paths[p].y_off;
+#pragma unroll
+    for (int m = 0; m < 2 * L2 + 1; ++m) yb[m] = to_acc<A>(yr[yoff + m]);
+    for (int q = p; q < pend; ++q) {
+      const PathDev pd = a.paths[q];
+      static_for<0, kLmax + 1>([&](auto L3c) {
+        constexpr int L3 = decltype(L3c)::value;
+        if constexpr (L3 >= (L1 > L2 ? L1 - L2 : L2 - L1) && L3 <= L1 + L2) {
+          if (pd.l3 == L3) path<L1, L2, L3>(a, pd, xb, yb, wr, outr, c);
+        }
+      });
+    }
+  }
+
+  template <int L1>
+  __device__ static __forceinline__ void block(const TPArgs& a, const BlockDev& blk, const T* xr,
+                                               const T* yr, const T* wr, T* outr, int c) {
+    A xb[2 * L1 + 1][VEC];
+#pragma unroll
+    for (int m = 0; m < 2 * L1 + 1; ++m) VecIO<T, VEC>::load(xr + blk.x_off + m * blk.mul + c, xb[m]);
+    int p = blk.path_begin;
+    while (p < blk.path_end) {
+      const int l2 = a.paths[p].l2;
+      const int pend = a.paths[p].i2_end;
+      static_for<0, kLmax + 1>([&](auto L2c) {
+        constexpr int L2 = decltype(L2c)::value;
+        if (l2 == L2) run<L1, L2>(a, p, pend, xb, yr, wr, outr, c);
+      });
+      p = pend;
+    }
+  }
+};
+
+template <typename T, typename A, int VEC>
+__global__ __launch_bounds__(kBlock) void tp_fwd_kernel(TPArgs a) {
+  const int64_t gt = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+  const int64_t row = gt >> a.lpr_log2;
+  const int lpr = 1 << a.lpr_log2;
+  const int lr = int(gt & (lpr - 1));
+  if (row >= a.B) return;
+  const T* xr = static_cast<const T*>(a.x) + row * a.dim_x;
+  const T* yr = static_cast<const T*>(a.y) + row * a.dim_y;
+  const T* wr = static_cast<const T*>(a.w) + row * a.w_stride;
+  T* outr = static_cast<T*>(a.out) + row * a.dim_out;
+  for (int grp = lr; grp < a.ngroups; grp += lpr) {
+    const int c = grp * VEC;
+    for (int b = 0; b < a.nblocks; ++b) {
+      const BlockDev blk = a.blocks[b];
+      if (c >= blk.mul) continue;
+      static_for<0, kLmax + 1>([&](auto L1c) {
+        constexpr int L1 = decltype(L1c)::value;
+        if (blk.l1 == L1) TPFwd<T, A, VEC>::template block<L1>(a, blk, xr, yr, wr, outr, c);
+      });
+    }
+  }
+}
+
+// ------------------------------------------------------------------ backward
+
+template <typename T, typename A, int VEC>
+struct TPBwd {
+  template <int L1, int L2, int L3>
+  __device__ static __forceinline__ void path(const TPArgs& a, const PathDev& pd,
+                                              const A (&xb)[2 * L1 + 1][VEC],
+                                              const A (&yb)[2 * L2 + 1], const T* gr,
+                                              const T* wr, T* dwr, A* dwa, int c,
+                                              A (&dxb)[2 * L1 + 1][VEC], A (&dyb)[2 * L2 + 1]) {
+    using P = Pattern<L1, L2, L3>;
+    const A* __restrict__ cf = static_cast<const A*>(a.coef) + pd.coef_off;
+    const A gs = A(a.g_scale);
+    A gb[2 * L3 + 1][VEC];
+#pragma unroll
+    for (int m = 0; m < 2 * L3 + 1; ++m) {
+      VecIO<T, VEC>::load(gr + pd.out_off + m * pd.mul + c, gb[m]);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) gb[m][v] *= gs;
+    }
+    A wv[VEC];
+    VecIO<T, VEC>::load(wr + pd.w_off + c, wv);
+    A xw[2 * L1 + 1][VEC], q[2 * L1 + 1][VEC];
+#pragma unroll
+    for (int m = 0; m < 2 * L1 + 1; ++m)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        xw[m][v] = xb[m][v] * wv[v];
+        q[m][v] = A(0);
+      }
+    // q[m1] = sum_m3 A[m1,m3] g[m3]   (A = C y);  dy[m2] += C sum_u w x[m1] g[m3]
+    static_for<0, P::NP>([&](auto I) {
+      constexpr PairT pr = P::arr.p[decltype(I)::value];
+      const A ca = cf[pr.coef];
+      A av = ca * yb[pr.m2a + L2];
+      A cb = A(0);
+      if constexpr (pr.n == 2) {
+        cb = cf[pr.coef + 1];
+        av = fma(cb, yb[pr.m2b + L2], av);
+      }
+      A s = A(0);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        q[pr.m1 + L1][v] = fma(av, gb[pr.m3 + L3][v], q[pr.m1 + L1][v]);
+        s = fma(xw[pr.m1 + L1][v], gb[pr.m3 + L3][v], s);
+      }
+      dyb[pr.m2a + L2] = fma(ca, s, dyb[pr.m2a + L2]);
+      if constexpr (pr.n == 2) dyb[pr.m2b + L2] = fma(cb, s, dyb[pr.m2b + L2]);
+    });
+    // dw = sum_m1 x[m1] q[m1];  dx[m1] += w q[m1]
+    A d[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) d[v] = A(0);
+#pragma unroll
+    for (int m = 0; m < 2 * L1 + 1; ++m)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        d[v] = fma(xb[m][v], q[m][v], d[v]);
+        dxb[m][v] = fma(wv[v], q[m][v], dxb[m][v]);
+      }
+    if (dwr) VecIO<T, VEC>::store(dwr + pd.w_off + c, d);
+    if (dwa) VecIO<A, VEC>::store(dwa + pd.w_off + c, d);
+  }
+
+  template <int L1, int L2>
+  __device__ static __forceinline__ void run(const TPArgs& a, int p, int pend,
+                                             const A (&xb)[2 * L1 + 1][VEC], const T* yr,
+                                             const T* gr, const T* wr, T* dwr, A* dwa, int c,
+                                             A (&dxb)[2 * L1 + 1][VEC], A* lds) {
+    A yb[2 * L2 + 1], dyb[2 * L2 + 1];
+    const int yoff = a.paths[p].y_off;
+#pragma unroll
+    for (int m = 0; m < 2 * L2 + 1; ++m) {
+      yb[m] = to_acc<A>(yr[yoff + m]);
+      dyb[m] = A(0);
+    }
+    for (int q = p; q < pend; ++q) {
+      const PathDev pd = a.paths[q];
+      static_for<0, kLmax + 1>([&](auto L3c) {
+        constexpr int L3 = decltype(L3c)::value;
+        if constexpr (L3 >= (L1 > L2 ? L1 - L2 : L2 - L1) && L3 <= L1 + L2) {
+          if (pd.l3 == L3) path<L1, L2, L3>(a, pd, xb, yb, gr, wr, dwr, dwa, c, dxb, dyb);
+        }
+      });
+    }
+    // this lane's grad_y partial lives in its own LDS column (no sharing)
+#pragma unroll
+    for (int m = 0; m < 2 * L2 + 1; ++m) lds[(yoff + m) * kBlock + threadIdx.x] += dyb[m];
+  }
+
+  template <int L1>
+  __device__ static __forceinline__ void block(const TPArgs& a, const BlockDev& blk, const T* xr,
+                                               const T* yr, const T* gr, const T* wr, T* dxr,
+                                               A* dxa, T* dwr, A* dwa, int c, A* lds) {
+    A xb[2 * L1 + 1][VEC], dxb[2 * L1 + 1][VEC];
+#pragma unroll
+    for (int m = 0; m < 2 * L1 + 1; ++m) {
+      VecIO<T, VEC>::load(xr + blk.x_off + m * blk.mul + c, xb[m]);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) dxb[m][v] = A(0);
+    }
+    int p = blk.path_begin;
+    while (p < blk.path_end) {
+      const int l2 = a.paths[p].l2;
+      const int pend = a.paths[p].i2_end;
+      static_for<0, kLmax + 1>([&](auto L2c) {
+        constexpr int L2 = decltype(L2c)::value;
+        if (l2 == L2) run<L1, L2>(a, p, pend, xb, yr, gr, wr, dwr, dwa, c, dxb, lds);
+      });
+      p = pend;
+    }
+    if (dxr) {
+#pragma unroll
+      for (int m = 0; m < 2 * L1 + 1; ++m) VecIO<T, VEC>::store(dxr + blk.x_off + m * blk.mul + c, dxb[m]);
+    }
+    if (dxa) {
+#pragma unroll
+      for (int m = 0; m < 2 * L1 + 1; ++m) VecIO<A, VEC>::store(dxa + blk.x_off + m * blk.mul + c, dxb[m]);
+    }
+  }
+};
+
+template <typename T, typename A, int VEC>
+__global__ __launch_bounds__(kBlock) void tp_bwd_kernel(TPArgs a) {
+  extern __shared__ unsigned char smem_raw[];
+  A* lds = reinterpret_cast<A*>(smem_raw);  // [dim_y][kBlock], one column per lane
+  const int64_t gt = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+  const int64_t row = gt >> a.lpr_log2;
+  const int lpr = 1 << a.lpr_log2;
+  const int lr = int(gt & (lpr - 1));
+  const bool active = row < a.B;
+  for (int k = 0; k < a.dim_y; ++k) lds[k * kBlock + threadIdx.x] = A(0);
+  if (active) {
+    const int64_t xrow = a.x_idx ? int64_t(a.x_idx[row]) : row;
+    const int64_t grow = a.g_idx ? int64_t(a.g_idx[row]) : row;
+    const T* xr = static_cast<const T*>(a.x) + xrow * a.dim_x;
+    const T* yr = static_cast<const T*>(a.y) + row * a.dim_y;
+    const T* gr = static_cast<const T*>(a.g) + grow * a.dim_out;
+    const T* wr = static_cast<const T*>(a.w) + row * a.w_stride;
+    T* dxr = a.dx ? static_cast<T*>(a.dx) + row * a.dim_x : nullptr;
+    A* dxa = a.dx_ws ? static_cast<A*>(a.dx_ws) + row * a.dim_x : nullptr;
+    T* dwr = a.dw ? static_cast<T*>(a.dw) + row * a.W : nullptr;
+    A* dwa = a.dw_ws ? static_cast<A*>(a.dw_ws) + row * a.W : nullptr;
+    for (int grp = lr; grp < a.ngroups; grp += lpr) {
+      const int c = grp * VEC;
+      for (int b = 0; b < a.nblocks; ++b) {
+        const BlockDev blk = a.blocks[b];
+        if (c >= blk.mul) continue;
+        static_for<0, kLmax + 1>([&](auto L1c) {
+          constexpr int L1 = decltype(L1c)::value;
+          if (blk.l1 == L1)
+            TPBwd<T, A, VEC>::template block<L1>(a, blk, xr, yr, gr, wr, dxr, dxa, dwr, dwa, c, lds);
+        });
+      }
+    }
+  }
+  // grad_y: sum the row's lanes; lane k % lpr writes component k
+  T* dyr = (a.dy && active) ? static_cast<T*>(a.dy) + row * a.dim_y : nullptr;
+  for (int k = 0; k < a.dim_y; ++k) {
+    const A v = group_sum(lds[k * kBlock + threadIdx.x], lpr);
+    if (dyr && lr == (k & (lpr - 1))) from_acc(dyr[k], v);
+  }
+}
+
+// Shared weights: grad_w[j] = sum over rows of the per-row partials, in a
+// fixed order: contiguous chunks of kRowsPerChunk rows, then over chunks.
+constexpr int kRowsPerChunk = 256;
+
+template <typename A>
+__global__ __launch_bounds__(kBlock) void colsum_stage1(const A* __restrict__ in, A* __restrict__ part,
+                                                        int64_t rows, int W) {
+  const int col = blockIdx.x * kBlock + threadIdx.x;
+  const int64_t r0 = int64_t(blockIdx.y) * kRowsPerChunk;
+  if (col >= W) return;
+  const int64_t r1 = r0 + kRowsPerChunk < rows ? r0 + kRowsPerChunk : rows;
+  A s = A(0);
+  for (int64_t r = r0; r < r1; ++r) s += in[r * W + col];
+  part[int64_t(blockIdx.y) * W + col] = s;
+}
+
+template <typename T, typename A>
+__global__ __launch_bounds__(kBlock) void colsum_stage2(const A* __restrict__ part, T* __restrict__ out,
+                                                        int nchunks, int W) {
+  const int col = blockIdx.x * kBlock + threadIdx.x;
+  if (col >= W) return;
+  A s = A(0);
+  for (int k = 0; k < nchunks; ++k) s += part[int64_t(k) * W + col];
+  from_acc(out[col], s);
+}
+
+// ------------------------------------------------------------ typed launchers
+// Each (storage type, VEC) pair is instantiated in its own translation unit
+// (inst/*.hip) so the large unrolled kernels compile in parallel.
+
+inline dim3 grid_for(int64_t B, int lpr_log2) {
+  const int64_t rows_per_block = kBlock >> lpr_log2;
+  return dim3(unsigned((B + rows_per_block - 1) / rows_per_block));
+}
+
+template <typename T, int VEC>
+void tp_fwd_typed(const TPArgs& a, hipStream_t s) {
+  using A = typename AccOf<T>::type;
+  hipLaunchKernelGGL((tp_fwd_kernel<T, A, VEC>), grid_for(a.B, a.lpr_log2), dim3(kBlock), 0, s, a);
+}
+
+template <typename T, int VEC>
+void tp_bwd_typed(const TPArgs& a, hipStream_t s) {
+  using A = typename AccOf<T>::type;
+  const size_t lds = size_t(a.dim_y) * kBlock * sizeof(A);
+  hipLaunchKernelGGL((tp_bwd_kernel<T, A, VEC>), grid_for(a.B, a.lpr_log2), dim3(kBlock), lds, s, a);
+}
+
+#define CGTP_TP_EXTERN(T, V)                                           \
+  extern template void tp_fwd_typed<T, V>(const TPArgs&, hipStream_t); \
+  extern template void tp_bwd_typed<T, V>(const TPArgs&, hipStream_t);
+
+}  // namespace cgtp

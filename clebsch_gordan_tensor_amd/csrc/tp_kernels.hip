@@ -1,0 +1,155 @@
+// Launchers of the row-parallel tensor product (kernels in tp_impl.hpp).
+#include "tp_impl.hpp"
+
+namespace cgtp {
+
+CGTP_TP_EXTERN(float, 1)
+CGTP_TP_EXTERN(float, 4)
+CGTP_TP_EXTERN(bf16, 1)
+CGTP_TP_EXTERN(bf16, 4)
+CGTP_TP_EXTERN(double, 1)
+CGTP_TP_EXTERN(double, 2)
+
+// ----------------------------------------------------------------- launchers
+
+namespace {
+
+int ilog2_ceil(int v) {
+  int k = 0;
+  while ((1 << k) < v) ++k;
+  return k;
+}
+
+bool aligned(const void* p, size_t bytes) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
+
+TPArgs make_args(cgtp_plan_s* plan, const DevTables& t, int64_t B, int vec) {
+  TPArgs a{};
+  a.g_scale = 1.0;
+  a.paths = t.paths;
+  a.blocks = t.blocks;
+  a.coef = t.coef;
+  a.B = B;
+  a.w_stride = plan->wkind == CGTP_W_PER_ROW ? plan->w_numel : 0;
+  a.dim_x = int(plan->dim_x);
+  a.dim_y = int(plan->dim_y);
+  a.dim_out = int(plan->dim_out);
+  a.W = int(plan->w_numel);
+  a.nblocks = int(plan->blocks.size());
+  a.ngroups = (plan->max_mul + vec - 1) / vec;
+  a.lpr_log2 = ilog2_ceil(a.ngroups < 64 ? a.ngroups : 64);
+  return a;
+}
+
+template <typename T>
+void colsum(const void* in, void* part, void* out, int64_t rows, int W, hipStream_t s) {
+  using A = typename AccOf<T>::type;
+  const int nchunks = int((rows + kRowsPerChunk - 1) / kRowsPerChunk);
+  const unsigned gx = unsigned((W + kBlock - 1) / kBlock);
+  hipLaunchKernelGGL((colsum_stage1<A>), dim3(gx, unsigned(nchunks)), dim3(kBlock), 0, s,
+                     static_cast<const A*>(in), static_cast<A*>(part), rows, W);
+  hipLaunchKernelGGL((colsum_stage2<T, A>), dim3(gx), dim3(kBlock), 0, s, static_cast<const A*>(part),
+                     static_cast<T*>(out), nchunks, W);
+}
+
+}  // namespace
+
+void tp_forward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* y, const void* w,
+                       void* out, hipStream_t stream) {
+  const DevTables& t = plan_tables(plan);
+  const size_t es = dtype_size(plan->dtype);
+  int vec = plan->vec;
+  if (!aligned(x, vec * es) || !aligned(w, vec * es) || !aligned(out, vec * es)) vec = 1;
+  TPArgs a = make_args(plan, t, B, vec);
+  a.x = x;
+  a.y = y;
+  a.w = w;
+  a.out = out;
+  switch (plan->dtype) {
+    case CGTP_F32:
+      vec == 1 ? tp_fwd_typed<float, 1>(a, stream) : tp_fwd_typed<float, 4>(a, stream);
+      break;
+    case CGTP_BF16:
+      vec == 1 ? tp_fwd_typed<bf16, 1>(a, stream) : tp_fwd_typed<bf16, 4>(a, stream);
+      break;
+    case CGTP_F64:
+      vec == 1 ? tp_fwd_typed<double, 1>(a, stream) : tp_fwd_typed<double, 2>(a, stream);
+      break;
+  }
+  CGTP_CHECK_HIP(hipGetLastError());
+}
+
+size_t tp_backward_ws_bytes(const cgtp_plan_s* plan, int64_t B) {
+  if (plan->wkind != CGTP_W_SHARED || B == 0) return 0;
+  const int64_t nchunks = (B + kRowsPerChunk - 1) / kRowsPerChunk;
+  return size_t(B + nchunks) * size_t(plan->w_numel) * acc_size(plan->dtype);
+}
+
+void tp_backward_rows(cgtp_plan_s* plan, const TPBackwardRows& r, hipStream_t stream) {
+  const DevTables& t = plan_tables(plan);
+  const size_t es = dtype_size(plan->dtype), as = acc_size(plan->dtype);
+  int vec = plan->vec;
+  if (!aligned(r.x, vec * es) || !aligned(r.w, vec * es) || !aligned(r.g, vec * es) ||
+      !aligned(r.dx, vec * es) || !aligned(r.dw, vec * es) || !aligned(r.dx_ws, vec * as) ||
+      !aligned(r.dw_ws, vec * as))
+    vec = 1;
+  TPArgs a = make_args(plan, t, r.rows, vec);
+  a.w_stride = r.w_stride;
+  a.x = r.x;
+  a.y = r.y;
+  a.w = r.w;
+  a.g = r.g;
+  a.dx = r.dx;
+  a.dy = r.dy;
+  a.dw = r.dw;
+  a.dw_ws = r.dw_ws;
+  a.dx_ws = r.dx_ws;
+  a.x_idx = r.x_idx;
+  a.g_idx = r.g_idx;
+  a.g_scale = r.g_scale;
+  switch (plan->dtype) {
+    case CGTP_F32:
+      vec == 1 ? tp_bwd_typed<float, 1>(a, stream) : tp_bwd_typed<float, 4>(a, stream);
+      break;
+    case CGTP_BF16:
+      vec == 1 ? tp_bwd_typed<bf16, 1>(a, stream) : tp_bwd_typed<bf16, 4>(a, stream);
+      break;
+    case CGTP_F64:
+      vec == 1 ? tp_bwd_typed<double, 1>(a, stream) : tp_bwd_typed<double, 2>(a, stream);
+      break;
+  }
+  CGTP_CHECK_HIP(hipGetLastError());
+}
+
+void tp_backward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* y,
+                        const void* w, const void* g, void* dx, void* dy, void* dw, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  const bool shared = plan->wkind == CGTP_W_SHARED;
+  if (shared && dw) {
+    const size_t need = tp_backward_ws_bytes(plan, B);
+    if (!ws || ws_bytes < need)
+      throw Error{CGTP_ERR_WORKSPACE, "tp_backward needs " + std::to_string(need) + " workspace bytes"};
+  }
+  TPBackwardRows r;
+  r.rows = B;
+  r.x = x;
+  r.y = y;
+  r.w = w;
+  r.w_stride = shared ? 0 : plan->w_numel;
+  r.g = g;
+  r.dx = dx;
+  r.dy = dy;
+  r.dw = shared ? nullptr : dw;
+  r.dw_ws = (shared && dw) ? ws : nullptr;
+  tp_backward_rows(plan, r, stream);
+  if (shared && dw) {
+    char* part = static_cast<char*>(ws) + size_t(B) * plan->w_numel * acc_size(plan->dtype);
+    switch (plan->dtype) {
+      case CGTP_F32: colsum<float>(ws, part, dw, B, int(plan->w_numel), stream); break;
+      case CGTP_BF16: colsum<bf16>(ws, part, dw, B, int(plan->w_numel), stream); break;
+      case CGTP_F64: colsum<double>(ws, part, dw, B, int(plan->w_numel), stream); break;
+    }
+    CGTP_CHECK_HIP(hipGetLastError());
+  }
+}
+
+}  // namespace cgtp

@@ -1,0 +1,205 @@
+/* cgtp.h - Clebsch-Gordan tensor products and the equivariant point
+ * convolution built on them, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (citations name the page and its section):
+ *  - "E3J: An Efficient and Open-Source Backend for Euclidean Equivariant
+ *    Operations on GPU and TPU", sections 3.1.1 (full Clebsch-Gordan tensor
+ *    product), 3.1.2 and E.2.2 (message-passing convolution with CSR receiver
+ *    aggregation, deterministic, no atomics), E.1 (reverse-mode rules by
+ *    transposition), G.1-G.2 (harmonics and CG coefficients by ladder
+ *    operators and a triangular eigen-system).
+ *  - MolSSI e3nn course, "Curriculum at a glance": lessons 02a (irreps
+ *    strings), 02b (spherical harmonics), 03a (CG decomposition, parity rule
+ *    p3 = p1 p2), 03b (x (x)_w y, connection modes), 05a (edge vector
+ *    r_ij = r_j - r_i), 06a (m_ij = (R(|r_ij|) Y(rhat_ij)) (x)_w h_j).
+ *  - e3nn_mlx "Modular v2106 point models": Convolution(edge_src, edge_dst,
+ *    radial), sqrt(num_neighbors) normalisation, empty edge lists.
+ *
+ * Conventions (fixed by this library where the pages leave them open):
+ *  - Real spherical harmonics, component-normalised (sum_m Y_lm^2 = 2l+1),
+ *    z polar axis, m = -l..l inside a block, l-major blocks: Y_1 = sqrt3 (y,z,x).
+ *  - Real CG blocks are orthonormal over (m1, m2) for each m3. Sign per path:
+ *    even l1+l2+l3 -> C[0,0,0] > 0; odd -> the first nonzero entry in
+ *    lexicographic (m1, m2, m3) order (each m from -l) is positive.
+ *  - Mode "uvu" (channel-wise): for path p = (i1, i2, l3) with x block i1 of
+ *    multiplicity u,
+ *      out[z, p, m3, u] = w[(z,) p, u] sum_{m1,m2} C_p[m1,m2,m3] x[z,i1,m1,u] y[z,i2,m2]
+ *    Every y block must have multiplicity 1. Paths: every x block i1, every y
+ *    block i2, every l3 in |l1-l2|..l1+l2 whose (l3, p1*p2) appears in
+ *    irreps_out (multiplicities of irreps_out are ignored); order i1, i2, l3.
+ *    One output block per path (not collapsed by degree).
+ *  - Row layouts: blocks concatenated in irreps (or path) order; inside a
+ *    block [2l+1][mul] (channel index fastest, "ir_mul"). Weights of one row
+ *    are [path][mul] concatenated (W = sum_p mul_p elements).
+ *
+ * Memory and execution:
+ *  - Every tensor argument is a DEVICE pointer owned by the caller, of the
+ *    plan's dtype unless stated. Indices are int32, sizes int64.
+ *  - Plans and graphs are opaque handles owned by the library; they allocate
+ *    small device tables (once per device for plans) and are immutable after
+ *    creation, so they may be shared between streams and threads.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Compute calls are
+ *    asynchronous on it; outputs are overwritten, never accumulated into.
+ *    A NULL gradient pointer skips that gradient.
+ *  - Results are deterministic: every sum has a fixed order, no atomics touch
+ *    floating-point data, and repeated calls are bitwise identical.
+ *  - Errors are status codes; cgtp_last_error() returns a thread-local
+ *    message for the last failure. Nothing else escapes the ABI.
+ */
+#ifndef CGTP_H
+#define CGTP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CGTP_OK = 0,
+  CGTP_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad enum, misuse   */
+  CGTP_ERR_PARSE = 2,       /* malformed irreps string                         */
+  CGTP_ERR_UNSUPPORTED = 3, /* valid request outside what is compiled in       */
+  CGTP_ERR_INDEX = 4,       /* graph arrays out of range or not monotone       */
+  CGTP_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required      */
+  CGTP_ERR_HIP = 6,         /* a HIP runtime call failed                       */
+  CGTP_ERR_ALLOC = 7        /* host or device allocation failed                */
+} cgtp_status;
+
+typedef enum { CGTP_F32 = 0, CGTP_F64 = 1, CGTP_BF16 = 2 } cgtp_dtype;
+
+/* Weight kinds. SHARED: w is [W]. PER_ROW: w is [rows][W] for the tensor
+ * product (rows = B) and [edges][W] in CSR order for the convolution. */
+typedef enum { CGTP_W_SHARED = 0, CGTP_W_PER_ROW = 1 } cgtp_wkind;
+
+/* Operations for cgtp_workspace_size. */
+typedef enum { CGTP_OP_TP_BACKWARD = 1, CGTP_OP_CONV_BACKWARD = 2 } cgtp_op;
+
+typedef struct cgtp_plan_s* cgtp_plan;
+typedef struct cgtp_graph_s* cgtp_graph;
+
+/* Largest degree compiled into the kernels for x, y and output blocks. */
+#define CGTP_LMAX 4
+
+const char* cgtp_status_string(cgtp_status s);
+/* Message of the last failing call on this thread ("" if none). */
+const char* cgtp_last_error(void);
+
+/* ---------------------------------------------------------------- planning */
+
+/* Build a tensor-product plan (host work only; device tables are uploaded on
+ * first use on each device). Irreps strings follow the course's lesson 02a:
+ * terms "MxLp" joined by '+', M defaults to 1, p in {e, o}; whitespace is
+ * ignored. Path enumeration follows lesson 03a (triangle rule, p3 = p1 p2).
+ * CG values are built with the ladder-operator construction of E3J appendix
+ * G.2: the highest-weight vector of each l3 solves a triangular system, lower
+ * m3 follow by repeated lowering; then the real-basis change and sign rule.
+ *   mode   : "uvu" only.
+ *   dtype  : storage type of every float tensor (bf16 computes in fp32).
+ *   wkind  : see cgtp_wkind.
+ * Errors: PARSE (bad string), UNSUPPORTED (mode != "uvu", a y multiplicity
+ * != 1, any l > CGTP_LMAX, no path at all), INVALID_ARG (null pointers). */
+cgtp_status cgtp_plan_create(const char* irreps_x, const char* irreps_y, const char* irreps_out,
+                             const char* mode, cgtp_dtype dtype, cgtp_wkind wkind, cgtp_plan* out);
+cgtp_status cgtp_plan_destroy(cgtp_plan plan);
+
+/* Sizes in elements per row: dim_x, dim_y, dim_out, the path count and W
+ * (weights per row or per edge). Any output pointer may be NULL. */
+cgtp_status cgtp_plan_query(cgtp_plan plan, int64_t* dim_x, int64_t* dim_y, int64_t* dim_out,
+                            int64_t* num_paths, int64_t* w_numel);
+
+/* HOST table [num_paths][6] of (i1, i2, l1, l2, l3, p3) in path order. */
+cgtp_status cgtp_plan_paths(cgtp_plan plan, int32_t* host_table);
+
+/* Dense real CG block of one path into HOST memory, fp64,
+ * [2l1+1][2l2+1][2l3+1] row-major. */
+cgtp_status cgtp_plan_cg(cgtp_plan plan, int32_t path, double* host_dense);
+
+/* ---------------------------------------------------------- tensor product */
+
+/* out[B][dim_out] = x[B][dim_x] (x)_w y[B][dim_y] (formula above).
+ * w is [W] (SHARED) or [B][W] (PER_ROW). B = 0 is a no-op.
+ * Errors: INVALID_ARG (null pointer with B > 0, B < 0). */
+cgtp_status cgtp_tp_forward(cgtp_plan plan, int64_t B, const void* x, const void* y, const void* w,
+                            void* out, void* stream);
+
+/* Reverse mode by transposition (E3J appendix E.1), with g = grad_out:
+ *   grad_x[z,i1,m1,u] = sum_p w sum_{m2,m3} C y[m2] g[m3,u]
+ *   grad_y[z,i2,m2]   = sum_p sum_u w sum_{m1,m3} C x[m1,u] g[m3,u]
+ *   grad_w[(z,)p,u]   = sum_{(z),m1,m2,m3} C x[m1,u] y[m2] g[m3,u]
+ * A SHARED plan sums grad_w over rows in a fixed two-stage order; that needs
+ * a workspace of cgtp_workspace_size(plan, NULL, B, CGTP_OP_TP_BACKWARD)
+ * bytes (0 for PER_ROW). Errors: WORKSPACE if ws is NULL or too small. */
+cgtp_status cgtp_tp_backward(cgtp_plan plan, int64_t B, const void* x, const void* y, const void* w,
+                             const void* grad_out, void* grad_x, void* grad_y, void* grad_w,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ graphs */
+
+/* COO -> CSR by destination. Sort key (dst, src), ties in input order (so
+ * the result is the stable lexicographic sort of the pairs). Outputs (device,
+ * caller-owned): row_ptr[N+1], src_sorted[E], perm[E] with perm[k] = input
+ * index of CSR edge k. Allocates and frees temporary device memory and
+ * synchronises the stream once (to read back a validation flag).
+ * Errors: INDEX if any src/dst is outside [0, N). */
+cgtp_status cgtp_csr_from_coo(int64_t N, int64_t E, const int32_t* src, const int32_t* dst,
+                              int32_t* row_ptr, int32_t* src_sorted, int32_t* perm, void* stream);
+
+/* Wrap a CSR-by-destination graph (device arrays, caller-owned, must outlive
+ * the handle): validates row_ptr (row_ptr[0] = 0, non-decreasing,
+ * row_ptr[N] = E) and src (in [0, N)), and builds the source-ordered
+ * transpose used by the backward pass (owned by the handle; edges grouped by
+ * source, in CSR-position order). Synchronises the stream once.
+ * Errors: INDEX on invalid arrays. */
+cgtp_status cgtp_graph_create(int64_t N, int64_t E, const int32_t* row_ptr, const int32_t* src,
+                              void* stream, cgtp_graph* out);
+cgtp_status cgtp_graph_destroy(cgtp_graph graph);
+
+/* Copy the handle's transpose into caller device buffers col_ptr[N+1], eid[E]
+ * (eid[k] = CSR position of the k-th source-ordered edge). */
+cgtp_status cgtp_graph_transpose(cgtp_graph graph, int32_t* col_ptr, int32_t* eid, void* stream);
+
+/* ------------------------------------------------------------- convolution */
+
+/* out[n] = scale * sum_{e: dst(e)=n} TP(x[src(e)], sh[e], w[e]) over CSR
+ * segment n, summed in CSR order (course lesson 06a; E3J 3.1.2, E.2.2).
+ *   x [N][dim_x], sh [E][dim_y] and w [E][W] (edge tensors in CSR order),
+ *   out [N][dim_out]. The plan must be PER_ROW (one weight row per edge).
+ * E = 0 writes zeros; nodes without incoming edges get zero rows. Edge
+ * messages never reach memory. Errors: UNSUPPORTED for a SHARED plan. */
+cgtp_status cgtp_conv_forward(cgtp_plan plan, cgtp_graph graph, const void* x, const void* sh,
+                              const void* w, double scale, void* out, void* stream);
+
+/* Reverse mode of cgtp_conv_forward, with g_e = scale * grad_out[dst(e)]:
+ *   grad_sh[e] = d/dsh of <g_e, TP(x[src(e)], sh[e], w[e])>   [E][dim_y]
+ *   grad_w[e]  = d/dw  of the same                             [E][W]
+ *   grad_x[n]  = sum_{e: src(e)=n} d/dx of the same            [N][dim_x]
+ * grad_x is summed over the transpose in fixed order from per-edge partials
+ * kept in the workspace (cgtp_workspace_size(plan, graph, 0,
+ * CGTP_OP_CONV_BACKWARD) bytes). Errors: WORKSPACE if too small. */
+cgtp_status cgtp_conv_backward(cgtp_plan plan, cgtp_graph graph, const void* x, const void* sh,
+                               const void* w, double scale, const void* grad_out, void* grad_x,
+                               void* grad_sh, void* grad_w, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for op (graph may be NULL for the tensor product, B is
+ * ignored for the convolution). */
+cgtp_status cgtp_workspace_size(cgtp_plan plan, cgtp_graph graph, int64_t B, int op, size_t* bytes);
+
+/* --------------------------------------------------- spherical harmonics */
+
+/* sh[n][(lmax+1)^2] = Y_l(vec/|vec|), l = 0..lmax, conventions above (course
+ * lesson 02b; E3J G.1). vec [n][3]. The zero vector gives Y_0 = 1, rest 0.
+ * lmax <= CGTP_LMAX. */
+cgtp_status cgtp_sh_forward(int lmax, cgtp_dtype dtype, int64_t n, const void* vec, void* sh,
+                            void* stream);
+
+/* grad_vec[n][3] = d/dvec of sum(grad_sh * Y(vec/|vec|)); zero for a zero vec. */
+cgtp_status cgtp_sh_backward(int lmax, cgtp_dtype dtype, int64_t n, const void* vec,
+                             const void* grad_sh, void* grad_vec, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CGTP_H */

@@ -1,0 +1,109 @@
+"""Host-side checks of libcgtp (CPU only, no compute calls).
+
+* the library loads and exports every function include/cgtp.h declares;
+* the planner's CG blocks (ladder construction) equal the oracle's (Racah);
+* path tables and row sizes equal the oracle's enumeration;
+* malformed or unsupported plans return the documented status codes.
+"""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import cg as ocg
+from oracle.irreps import Layout
+
+cgtp = pytest.importorskip("clebsch_gordan_tensor_amd.cgtp")
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "cgtp.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cgtp_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 18
+    for n in names:
+        assert hasattr(cgtp._lib, n), n
+    assert sorted(cgtp.EXPORTED) == names
+
+
+def all_triples(lmax=4):
+    for l1 in range(lmax + 1):
+        for l2 in range(lmax + 1):
+            for l3 in range(abs(l1 - l2), l1 + l2 + 1):
+                if l3 <= lmax:
+                    yield l1, l2, l3
+
+
+@pytest.mark.parametrize("l1,l2,l3", list(all_triples()))
+def test_planner_cg_equals_oracle(l1, l2, l3):
+    par = lambda l: "e" if l % 2 == 0 else "o"
+    p3 = "e" if (l1 + l2) % 2 == 0 else "o"
+    plan = cgtp.Plan("1x%d%s" % (l1, par(l1)), "1x%d%s" % (l2, par(l2)), "%d%s" % (l3, p3))
+    assert plan.num_paths == 1
+    assert np.abs(plan.cg(0) - ocg.cg_real(l1, l2, l3)).max() < 1e-13
+
+
+CASES = [
+    ("32x0e+32x1o+32x2e", "0e+1o+2e", "0e+0o+1e+1o+2e+2o"),
+    ("128x0e+128x1o+128x2e+128x3o", "0e+1o+2e+3o", "0e+0o+1e+1o+2e+2o+3e+3o"),
+    ("64x0e+64x1o+64x2e+64x3o+64x4e", "0e+1o+2e+3o+4e", "0e+0o+1e+1o+2e+2o+3e+3o+4e+4o"),
+    ("8x1o+4x0e+3x2o", "1o+0e", "0e+1o+2e"),          # mixed multiplicities, natural parity only
+    ("5x2e", "1o+1e", "1e+1o+2e+3o+3e"),                # repeated degree in y
+    ("2x1o", "2e", "1o+3o+2e"),
+]
+
+
+@pytest.mark.parametrize("ix,iy,io", CASES)
+def test_paths_and_sizes_equal_oracle(ix, iy, io):
+    L = Layout(ix, iy, io)
+    plan = cgtp.Plan(ix, iy, io)
+    assert (plan.dim_x, plan.dim_y, plan.dim_out, plan.num_paths, plan.w_numel) == (
+        L.dim_x, L.dim_y, L.dim_out, len(L.paths), L.w_numel)
+    ref = np.array([[p["i1"], p["i2"], p["l1"], p["l2"], p["l3"], p["p3"]] for p in L.paths])
+    assert np.array_equal(plan.paths(), ref)
+    for k, p in enumerate(L.paths):
+        assert np.abs(plan.cg(k) - ocg.cg_real(p["l1"], p["l2"], p["l3"])).max() < 1e-13
+
+
+def status_of(fn):
+    with pytest.raises(cgtp.CgtpError) as e:
+        fn()
+    return e.value.status
+
+
+def test_error_codes():
+    ERR_INVALID, ERR_PARSE, ERR_UNSUPPORTED = 1, 2, 3
+    assert status_of(lambda: cgtp.Plan("3x", "0e", "0e")) == ERR_PARSE
+    assert status_of(lambda: cgtp.Plan("1x1q", "0e", "0e")) == ERR_PARSE
+    assert status_of(lambda: cgtp.Plan("1e++1o", "0e", "0e")) == ERR_PARSE
+    assert status_of(lambda: cgtp.Plan("0x1e", "0e", "1e")) == ERR_PARSE
+    assert status_of(lambda: cgtp.Plan("1x1o", "1o", "0e", mode="uvw")) == ERR_UNSUPPORTED
+    assert status_of(lambda: cgtp.Plan("1x5o", "0e", "5o")) == ERR_UNSUPPORTED
+    assert status_of(lambda: cgtp.Plan("1x1o", "2x1o", "0e")) == ERR_UNSUPPORTED
+    assert status_of(lambda: cgtp.Plan("1x1o", "1o", "1o")) == ERR_UNSUPPORTED  # no path survives
+    p = cgtp.Plan("1x1o", "1o", "0e")
+    buf = np.zeros(27)
+    assert cgtp._lib.cgtp_plan_cg(p._h, 5, buf.ctypes.data_as(cgtp.ctypes.POINTER(cgtp.ctypes.c_double))) == ERR_INVALID
+    assert cgtp._lib.cgtp_plan_create(None, None, None, None, 0, 0, None) == ERR_INVALID
+    assert cgtp._lib.cgtp_tp_forward(None, 1, None, None, None, None, None) == ERR_INVALID
+    assert cgtp._lib.cgtp_sh_forward(5, 0, 1, None, None, None) == ERR_UNSUPPORTED
+    assert cgtp._lib.cgtp_sh_forward(2, 7, 1, None, None, None) == ERR_INVALID
+    assert cgtp._lib.cgtp_sh_forward(5, 0, 1, None, None, None) == ERR_UNSUPPORTED
+    assert "lmax" in cgtp._lib.cgtp_last_error().decode()
+
+
+def test_workspace_sizes():
+    ps = cgtp.Plan("32x0e+32x1o+32x2e", "0e+1o+2e", "0e+0o+1e+1o+2e+2o", wkind="shared")
+    pr = cgtp.Plan("32x0e+32x1o+32x2e", "0e+1o+2e", "0e+0o+1e+1o+2e+2o", wkind="per_row")
+    assert pr.workspace_size(cgtp.OP_TP_BACKWARD, 4096) == 0
+    # per-row partials + one partial per 256-row chunk, fp32
+    assert ps.workspace_size(cgtp.OP_TP_BACKWARD, 4096) == (4096 + 16) * 480 * 4
+    assert ps.workspace_size(cgtp.OP_TP_BACKWARD, 0) == 0
