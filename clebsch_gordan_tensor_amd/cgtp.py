@@ -11,7 +11,8 @@ import os
 
 import numpy as np
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcgtp.so")
+_LIB_PATH = os.environ.get("CGTP_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                           "libcgtp.so")
 if not os.path.exists(_LIB_PATH):
     raise ImportError("libcgtp.so is not built: run `python -m clebsch_gordan_tensor_amd.build` "
                       "(or __graft_entry__.build())")
@@ -126,7 +127,7 @@ class Plan:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h:
+        if h and _lib is not None:
             _lib.cgtp_plan_destroy(h)
             self._h = None
 
@@ -253,7 +254,7 @@ class Graph:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h:
+        if h and _lib is not None:
             _lib.cgtp_graph_destroy(h)
             self._h = None
 

@@ -83,6 +83,7 @@ struct cgtp_plan_s {
   // ordered by l2 then l3; slot_paths maps them to path indices (-1 = absent).
   bool conv_fused = false;
   int conv_L = 0;
+  int lm = 0;  // largest degree among y blocks and output paths (kernel specialisation)
   int yoff_by_l[CGTP_LMAX + 1] = {-1, -1, -1, -1, -1};
   std::vector<int32_t> slot_paths, slot_off;
   cgtp_dtype dtype = CGTP_F32;

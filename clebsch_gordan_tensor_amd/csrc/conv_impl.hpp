@@ -27,6 +27,8 @@
 // are then summed per source node over the transpose, in CSR-position order.
 #pragma once
 
+#include <type_traits>
+
 #include "cg_pattern.h"
 #include "common.hpp"
 #include "device_util.hpp"
@@ -91,6 +93,8 @@ struct ConvArgs {
   int64_t N;
   int dim_x, dim_y, dim_out, W;
   int nblocks, nchunks, npaths, L;
+  int block;    // x block of a degree-specialised launch
+  int lg_log2;  // lanes per edge group (fused forward)
   int yoff[kLmax + 1];
   double scale;
 };
@@ -100,92 +104,168 @@ constexpr int kWaves = kBlock / 64;
 __device__ __forceinline__ int conv_wave_id() { return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6); }
 
 // ------------------------------------------------------------ fused forward
-template <typename T, typename A, int L1, int L>
-__device__ __forceinline__ void fwd_fused_block(const ConvArgs& a, int64_t n, int b,
-                                                const BlockDev& blk, int c) {
+// Slot chunks: consecutive slots whose accumulators fit a register budget of
+// `budget` entries per channel; the chunks of one block run as separate waves
+// of the same workgroup (they share the gathered rows through the caches).
+template <int L1, int L, int budget>
+struct Chunks {
   using S = Slots<L1, L>;
-  constexpr int NS = S::NS;
-  A acc[S::NACC];
+  static constexpr int count() {
+    int n = 0, acc = budget;
+    for (int i = 0; i < S::NS; ++i) {
+      const int sz = 2 * S::arr.p[i].l3 + 1;
+      if (acc + sz > budget) {
+        ++n;
+        acc = 0;
+      }
+      acc += sz;
+    }
+    return n;
+  }
+  static constexpr int NCH = count();
+  struct Arr {
+    int begin[NCH + 1];
+  };
+  static constexpr Arr build() {
+    Arr a{};
+    int n = 0, acc = budget;
+    for (int i = 0; i < S::NS; ++i) {
+      const int sz = 2 * S::arr.p[i].l3 + 1;
+      if (acc + sz > budget) {
+        a.begin[n++] = i;
+        acc = 0;
+      }
+      acc += sz;
+    }
+    a.begin[n] = S::NS;
+    return a;
+  }
+  static constexpr Arr arr = build();
+};
+
+#ifndef CGTP_CONV_ACC_REGS
+#define CGTP_CONV_ACC_REGS 64
+#endif
+// accumulator entries per channel that fit CGTP_CONV_ACC_REGS registers
+template <typename A, int VEC>
+constexpr int conv_budget() {
+  return CGTP_CONV_ACC_REGS / (VEC * int(sizeof(A) / 4)) > 9 ? CGTP_CONV_ACC_REGS / (VEC * int(sizeof(A) / 4))
+                                                              : 9;
+}
+
+// One wave = (receiver n, one slot chunk of x block b, one channel chunk).
+// Lanes form G = 64 / LG groups of LG lanes; group g takes edges e0+g,
+// e0+g+G, ... and lane k of a group owns channels c .. c+VEC-1.
+template <typename T, typename A, int VEC, int L1, int L, int CH>
+__device__ __forceinline__ void fwd_fused_chunk(const ConvArgs& a, int64_t n, const BlockDev& blk,
+                                                int c, bool valid, int g, int G) {
+  using S = Slots<L1, L>;
+  using CK = Chunks<L1, L, conv_budget<A, VEC>()>;
+  constexpr int s0 = CK::arr.begin[CH], s1 = CK::arr.begin[CH + 1];
+  constexpr int acc0 = S::arr.p[s0].acc;
+  constexpr int NACC = (s1 < S::NS ? S::arr.p[s1].acc : S::NACC) - acc0;
+  A acc[NACC][VEC];
 #pragma unroll
-  for (int i = 0; i < S::NACC; ++i) acc[i] = A(0);
-  int pid[NS], woff[NS], coff[NS];
-  const int so = a.slot_off[b];
+  for (int i = 0; i < NACC; ++i)
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    pid[s] = a.slot_paths[so + s];
-    woff[s] = pid[s] >= 0 ? a.paths[pid[s]].w_off : 0;
-    coff[s] = pid[s] >= 0 ? a.paths[pid[s]].coef_off : 0;
+    for (int v = 0; v < VEC; ++v) acc[i][v] = A(0);
+  int pid[s1 - s0], woff[s1 - s0], coff[s1 - s0];
+  const int so = ldc(a.slot_off + a.block);
+#pragma unroll
+  for (int s = 0; s < s1 - s0; ++s) {
+    pid[s] = ldc(a.slot_paths + so + s0 + s);
+    woff[s] = pid[s] >= 0 ? ldc(&a.paths[pid[s]].w_off) : 0;
+    coff[s] = pid[s] >= 0 ? ldc(&a.paths[pid[s]].coef_off) : 0;
   }
   const A* __restrict__ cf = static_cast<const A*>(a.coef);
   const T* __restrict__ X = static_cast<const T*>(a.x);
   const int32_t e0 = a.row_ptr[n], e1 = a.row_ptr[n + 1];
-  for (int32_t e = e0; e < e1; ++e) {
-    const int64_t j = a.src[e];
-    A xb[2 * L1 + 1][1];
+  if (valid) {
+    for (int32_t e = e0 + g; e < e1; e += G) {
+      const int64_t j = a.src[e];
+      A xb[2 * L1 + 1][VEC];
 #pragma unroll
-    for (int m = 0; m < 2 * L1 + 1; ++m) xb[m][0] = to_acc<A>(X[j * a.dim_x + blk.x_off + m * blk.mul + c]);
-    const T* __restrict__ Ye = static_cast<const T*>(a.sh) + int64_t(e) * a.dim_y;
-    const T* __restrict__ we = static_cast<const T*>(a.w) + int64_t(e) * a.W;
-    A ycur[2 * L + 1];
-    static_for<0, NS>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      constexpr SlotT st = S::arr.p[i];
-      constexpr int prev = i > 0 ? i - 1 : 0;
-      constexpr bool first_of_l2 = (i == 0) || (S::arr.p[prev].l2 != st.l2);
-      if constexpr (first_of_l2) {
-        const int yo = a.yoff[st.l2];
-        if (yo >= 0) {
+      for (int m = 0; m < 2 * L1 + 1; ++m) VecIO<T, VEC>::load(X + j * a.dim_x + blk.x_off + m * blk.mul + c, xb[m]);
+      const T* __restrict__ Ye = static_cast<const T*>(a.sh) + int64_t(e) * a.dim_y;
+      const T* __restrict__ we = static_cast<const T*>(a.w) + int64_t(e) * a.W;
+      A ycur[2 * L + 1];
+      static_for<s0, s1>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        constexpr SlotT st = S::arr.p[i];
+        constexpr bool first_of_l2 = (i == s0) || (S::arr.p[i > 0 ? i - 1 : 0].l2 != st.l2);
+        if constexpr (first_of_l2) {
+          const int yo = a.yoff[st.l2];
+          if (yo >= 0) {
 #pragma unroll
-          for (int m = 0; m < 2 * st.l2 + 1; ++m) ycur[m] = to_acc<A>(Ye[yo + m]);
+            for (int m = 0; m < 2 * st.l2 + 1; ++m) ycur[m] = to_acc<A>(Ye[yo + m]);
+          }
         }
-      }
-      if (pid[i] >= 0) {
-        const A wv = to_acc<A>(we[woff[i] + c]);
-        A yb[2 * st.l2 + 1];
+        if (pid[i - s0] >= 0) {
+          A wv[VEC];
+          VecIO<T, VEC>::load(we + woff[i - s0] + c, wv);
+          A yb[2 * st.l2 + 1];
 #pragma unroll
-        for (int m = 0; m < 2 * st.l2 + 1; ++m) yb[m] = ycur[m];
-        A t[2 * st.l3 + 1][1];
-        fwd_core<L1, st.l2, st.l3, 1, A>(xb, yb, cf + coff[i], t);
+          for (int m = 0; m < 2 * st.l2 + 1; ++m) yb[m] = ycur[m];
+          A t[2 * st.l3 + 1][VEC];
+          fwd_core<L1, st.l2, st.l3, VEC, A>(xb, yb, cf + coff[i - s0], t);
 #pragma unroll
-        for (int m = 0; m < 2 * st.l3 + 1; ++m) acc[st.acc + m] = fma(wv, t[m][0], acc[st.acc + m]);
-      }
-    });
+          for (int m = 0; m < 2 * st.l3 + 1; ++m)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v)
+              acc[st.acc - acc0 + m][v] = fma(wv[v], t[m][v], acc[st.acc - acc0 + m][v]);
+        }
+      });
+    }
   }
+  // sum the groups' partial sums (every lane takes part), then group 0 stores
+  const int LG = 64 / G;
+  for (int off = LG; off < 64; off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < NACC; ++i)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[i][v] += __shfl_xor(acc[i][v], off, 64);
+  }
+  if (!valid || g != 0) return;
   T* __restrict__ outn = static_cast<T*>(a.out) + n * a.dim_out;
   const A sc = A(a.scale);
-  static_for<0, NS>([&](auto I) {
+  static_for<s0, s1>([&](auto I) {
     constexpr int i = decltype(I)::value;
     constexpr SlotT st = S::arr.p[i];
-    if (pid[i] >= 0) {
-      const PathDev pd = a.paths[pid[i]];
+    if (pid[i - s0] >= 0) {
+      const PathDev pd = ldc(a.paths + pid[i - s0]);
 #pragma unroll
-      for (int m = 0; m < 2 * st.l3 + 1; ++m) from_acc(outn[pd.out_off + m * pd.mul + c], sc * acc[st.acc + m]);
+      for (int m = 0; m < 2 * st.l3 + 1; ++m) {
+        A o[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) o[v] = sc * acc[st.acc - acc0 + m][v];
+        VecIO<T, VEC>::store(outn + pd.out_off + m * pd.mul + c, o);
+      }
     }
   });
 }
 
-template <typename T, typename A>
+// Work items: (receiver, slot chunk, channel chunk), slot chunks innermost so
+// one workgroup's waves read the same rows.
+template <typename T, typename A, int VEC, int L1, int L>
 __global__ __launch_bounds__(kBlock) void conv_fwd_fused_kernel(ConvArgs a) {
+  using CK = Chunks<L1, L, conv_budget<A, VEC>()>;
   const int64_t item = int64_t(blockIdx.x) * kWaves + conv_wave_id();
-  const int64_t per_node = int64_t(a.nblocks) * a.nchunks;
+  const int64_t per_node = int64_t(CK::NCH) * a.nchunks;
   const int64_t n = item / per_node;
   if (n >= a.N) return;
   const int rem = int(item - n * per_node);
-  const int b = rem / a.nchunks;
-  const int chunk = rem - b * a.nchunks;
-  const BlockDev blk = a.blocks[b];
-  const int c = chunk * 64 + int(threadIdx.x & 63);
-  if (c >= blk.mul) return;
-  static_for<0, kLmax + 1>([&](auto L1c) {
-    constexpr int L1 = decltype(L1c)::value;
-    if (blk.l1 == L1) {
-      static_for<0, kLmax + 1>([&](auto Lc) {
-        constexpr int L = decltype(Lc)::value;
-        if constexpr (Slots<L1, L>::NS > 0) {
-          if (a.L == L) fwd_fused_block<T, A, L1, L>(a, n, b, blk, c);
-        }
-      });
-    }
+  const int cc = rem / CK::NCH;
+  const int ch = rem - cc * CK::NCH;
+  const BlockDev blk = ldc(a.blocks + a.block);
+  const int lane = int(threadIdx.x & 63);
+  const int LG = 1 << a.lg_log2;
+  const int G = 64 >> a.lg_log2;
+  const int g = lane >> a.lg_log2;
+  const int c = (cc * LG + (lane & (LG - 1))) * VEC;
+  const bool valid = c < blk.mul;
+  static_for<0, CK::NCH>([&](auto C) {
+    constexpr int CH = decltype(C)::value;
+    if (ch == CH) fwd_fused_chunk<T, A, VEC, L1, L, CH>(a, n, blk, c, valid, g, G);
   });
 }
 
@@ -228,7 +308,7 @@ __global__ __launch_bounds__(kBlock) void conv_fwd_general_kernel(ConvArgs a) {
   const int rem = int(item - n * per_node);
   const int p = rem / a.nchunks;
   const int chunk = rem - p * a.nchunks;
-  const PathDev pd = a.paths[p];
+  const PathDev pd = ldc(a.paths + p);
   const int c = chunk * 64 + int(threadIdx.x & 63);
   if (c >= pd.mul) return;
   static_for<0, kLmax + 1>([&](auto A1) {
@@ -251,10 +331,38 @@ __global__ __launch_bounds__(kBlock) void conv_fwd_general_kernel(ConvArgs a) {
 
 // ------------------------------------------------------------ typed launchers
 // One translation unit per (kind, storage type): inst/conv_*.hip.
+constexpr int conv_vec(cgtp_dtype d) { return d == CGTP_F64 ? 2 : 4; }
+
+// Waves per receiver for the fused forward of x degree l1 and largest degree L.
 template <typename T>
-void conv_fwd_fused_typed(const ConvArgs& a, dim3 grid, hipStream_t s) {
+int conv_fused_chunks(int l1, int L) {
   using A = typename AccOf<T>::type;
-  hipLaunchKernelGGL((conv_fwd_fused_kernel<T, A>), grid, dim3(kBlock), 0, s, a);
+  constexpr int VEC = std::is_same<T, double>::value ? 2 : 4;
+  int n = 0;
+  static_for<0, kLmax + 1>([&](auto I) {
+    static_for<0, kLmax + 1>([&](auto J) {
+      constexpr int D = decltype(I)::value, M = decltype(J)::value;
+      if constexpr (Slots<D, M>::NS > 0) {
+        if (l1 == D && L == M) n = Chunks<D, M, conv_budget<A, VEC>()>::NCH;
+      }
+    });
+  });
+  return n;
+}
+
+template <typename T>
+void conv_fwd_fused_typed(const ConvArgs& a, int l1, int L, dim3 grid, hipStream_t s) {
+  using A = typename AccOf<T>::type;
+  constexpr int VEC = std::is_same<T, double>::value ? 2 : 4;
+  static_for<0, kLmax + 1>([&](auto I) {
+    static_for<0, kLmax + 1>([&](auto J) {
+      constexpr int D = decltype(I)::value, M = decltype(J)::value;
+      if constexpr (Slots<D, M>::NS > 0) {
+        if (l1 == D && L == M)
+          hipLaunchKernelGGL((conv_fwd_fused_kernel<T, A, VEC, D, M>), grid, dim3(kBlock), 0, s, a);
+      }
+    });
+  });
 }
 template <typename T>
 void conv_fwd_general_typed(const ConvArgs& a, dim3 grid, hipStream_t s) {
@@ -262,8 +370,9 @@ void conv_fwd_general_typed(const ConvArgs& a, dim3 grid, hipStream_t s) {
   hipLaunchKernelGGL((conv_fwd_general_kernel<T, A>), grid, dim3(kBlock), 0, s, a);
 }
 
-#define CGTP_CONV_EXTERN(T)                                                        \
-  extern template void conv_fwd_fused_typed<T>(const ConvArgs&, dim3, hipStream_t); \
-  extern template void conv_fwd_general_typed<T>(const ConvArgs&, dim3, hipStream_t);
+#define CGTP_CONV_EXTERN(T)                                                                   \
+  extern template void conv_fwd_fused_typed<T>(const ConvArgs&, int, int, dim3, hipStream_t); \
+  extern template void conv_fwd_general_typed<T>(const ConvArgs&, dim3, hipStream_t);         \
+  extern template int conv_fused_chunks<T>(int, int);
 
 }  // namespace cgtp

@@ -46,16 +46,34 @@ ConvArgs make_conv_args(cgtp_plan_s* plan, const DevTables& t, const cgtp_graph_
   return a;
 }
 
+bool aligned_to(const void* p, size_t bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
+
 template <typename T>
-void fwd_typed(cgtp_plan_s* plan, const ConvArgs& a, hipStream_t s) {
-  const int64_t per_node = plan->conv_fused ? int64_t(a.nblocks) * a.nchunks : int64_t(a.npaths) * a.nchunks;
-  const int64_t items = a.N * per_node;
-  const dim3 grid(unsigned((items + kWaves - 1) / kWaves));
-  if (plan->conv_fused)
-    conv_fwd_fused_typed<T>(a, grid, s);
-  else
-    conv_fwd_general_typed<T>(a, grid, s);
-  CGTP_CHECK_HIP(hipGetLastError());
+void fwd_typed(cgtp_plan_s* plan, ConvArgs a, hipStream_t s) {
+  const size_t vb = size_t(conv_vec(plan->dtype)) * dtype_size(plan->dtype);
+  const bool fused = plan->conv_fused && plan->vec == conv_vec(plan->dtype) && aligned_to(a.x, vb) &&
+                     aligned_to(a.w, vb) && aligned_to(a.out, vb);
+  if (!fused) {
+    const int64_t items = a.N * int64_t(a.npaths) * a.nchunks;
+    conv_fwd_general_typed<T>(a, dim3(unsigned((items + kWaves - 1) / kWaves)), s);
+    CGTP_CHECK_HIP(hipGetLastError());
+    return;
+  }
+  // one launch per x block, specialised for its degree and the plan's largest degree
+  const int VEC = conv_vec(plan->dtype);
+  for (size_t b = 0; b < plan->blocks.size(); ++b) {
+    const BlockInfo& blk = plan->blocks[b];
+    const int lanes = (blk.mul + VEC - 1) / VEC;
+    int lg = 0;
+    while ((1 << lg) < lanes && lg < 6) ++lg;
+    a.block = int(b);
+    a.lg_log2 = lg;
+    a.nchunks = (lanes + (1 << lg) - 1) >> lg;
+    const int nch = conv_fused_chunks<T>(blk.l1, plan->conv_L);
+    const int64_t items = a.N * int64_t(nch) * a.nchunks;
+    conv_fwd_fused_typed<T>(a, blk.l1, plan->conv_L, dim3(unsigned((items + kWaves - 1) / kWaves)), s);
+    CGTP_CHECK_HIP(hipGetLastError());
+  }
 }
 
 template <typename T>

@@ -60,11 +60,20 @@ struct VecIO<float, VEC> {
     for (int i = 0; i < VEC; ++i) v[i] = o[i];
     *reinterpret_cast<V*>(p) = v;
   }
+  __device__ static __forceinline__ void store_nt(float* p, const float (&o)[VEC]) {
+    V v;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) v[i] = o[i];
+    __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
+  }
 };
 template <>
 struct VecIO<float, 1> {
   __device__ static __forceinline__ void load(const float* p, float (&o)[1]) { o[0] = *p; }
   __device__ static __forceinline__ void store(float* p, const float (&o)[1]) { *p = o[0]; }
+  __device__ static __forceinline__ void store_nt(float* p, const float (&o)[1]) {
+    __builtin_nontemporal_store(o[0], p);
+  }
 };
 
 template <int VEC>
@@ -81,11 +90,20 @@ struct VecIO<double, VEC> {
     for (int i = 0; i < VEC; ++i) v[i] = o[i];
     *reinterpret_cast<V*>(p) = v;
   }
+  __device__ static __forceinline__ void store_nt(double* p, const double (&o)[VEC]) {
+    V v;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) v[i] = o[i];
+    __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
+  }
 };
 template <>
 struct VecIO<double, 1> {
   __device__ static __forceinline__ void load(const double* p, double (&o)[1]) { o[0] = *p; }
   __device__ static __forceinline__ void store(double* p, const double (&o)[1]) { *p = o[0]; }
+  __device__ static __forceinline__ void store_nt(double* p, const double (&o)[1]) {
+    __builtin_nontemporal_store(o[0], p);
+  }
 };
 
 template <int VEC>
@@ -102,12 +120,37 @@ struct VecIO<bf16, VEC> {
     for (int i = 0; i < VEC; ++i) v[i] = f32_to_bf16(o[i]);
     *reinterpret_cast<V*>(p) = v;
   }
+  __device__ static __forceinline__ void store_nt(bf16* p, const float (&o)[VEC]) {
+    V v;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) v[i] = f32_to_bf16(o[i]);
+    __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
+  }
 };
 template <>
 struct VecIO<bf16, 1> {
   __device__ static __forceinline__ void load(const bf16* p, float (&o)[1]) { o[0] = bf16_to_f32(p->bits); }
   __device__ static __forceinline__ void store(bf16* p, const float (&o)[1]) { p->bits = f32_to_bf16(o[0]); }
+  __device__ static __forceinline__ void store_nt(bf16* p, const float (&o)[1]) {
+    __builtin_nontemporal_store(f32_to_bf16(o[0]), &p->bits);
+  }
 };
+
+// Read-only plan data (CG coefficients, path and slot tables) through the
+// constant address space: the same address in every lane becomes one scalar
+// load into SGPRs instead of one vector load per lane.
+template <typename T>
+__device__ __forceinline__ T ldc(const T* p) {
+  static_assert(sizeof(T) % 4 == 0, "ldc reads whole 32-bit words");
+  constexpr int n = int(sizeof(T) / 4);
+  const __attribute__((address_space(4))) uint32_t* q = (const __attribute__((address_space(4))) uint32_t*)(p);
+  uint32_t w[n];
+#pragma unroll
+  for (int i = 0; i < n; ++i) w[i] = q[i];
+  T r;
+  __builtin_memcpy(&r, w, sizeof(T));
+  return r;
+}
 
 // Sum over aligned groups of `width` lanes (width a power of two <= 64);
 // every lane of a group receives the group's total.

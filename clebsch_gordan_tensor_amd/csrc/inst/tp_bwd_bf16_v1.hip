@@ -2,5 +2,5 @@
 #include "../tp_impl.hpp"
 
 namespace cgtp {
-template void tp_bwd_typed<bf16, 1>(const TPArgs&, hipStream_t);
+template void tp_bwd_typed<bf16, 1>(const TPArgs&, int, int, hipStream_t);
 }  // namespace cgtp

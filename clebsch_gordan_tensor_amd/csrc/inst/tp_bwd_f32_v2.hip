@@ -1,0 +1,6 @@
+// Instantiation of the bwd tensor-product kernel for storage type float, 2 channel(s) per lane.
+#include "../tp_impl.hpp"
+
+namespace cgtp {
+template void tp_bwd_typed<float, 2>(const TPArgs&, int, int, hipStream_t);
+}  // namespace cgtp

@@ -320,6 +320,7 @@ cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const ch
   for (const PathInfo& p : plan->paths) lo = std::max(lo, p.l3);
   plan->conv_fused = distinct;
   plan->conv_L = std::max(ly, lo);
+  plan->lm = plan->conv_L;
   if (distinct) {
     const int L = plan->conv_L;
     for (const BlockInfo& b : plan->blocks) {

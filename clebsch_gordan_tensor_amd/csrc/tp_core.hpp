@@ -22,8 +22,8 @@ __device__ __forceinline__ void fwd_core(const A (&xb)[2 * L1 + 1][VEC], const A
     for (int v = 0; v < VEC; ++v) o[m][v] = A(0);
   static_for<0, P::NP>([&](auto I) {
     constexpr PairT pr = P::arr.p[decltype(I)::value];
-    A a = cf[pr.coef] * yb[pr.m2a + L2];
-    if constexpr (pr.n == 2) a = fma(cf[pr.coef + 1], yb[pr.m2b + L2], a);
+    A a = ldc(cf + pr.coef) * yb[pr.m2a + L2];
+    if constexpr (pr.n == 2) a = fma(ldc(cf + pr.coef + 1), yb[pr.m2b + L2], a);
 #pragma unroll
     for (int v = 0; v < VEC; ++v) o[pr.m3 + L3][v] = fma(a, xb[pr.m1 + L1][v], o[pr.m3 + L3][v]);
   });

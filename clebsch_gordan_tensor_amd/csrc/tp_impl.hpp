@@ -24,6 +24,28 @@
 #include "device_util.hpp"
 #include "tp_core.hpp"
 
+// Tuning knobs (compile-time): minimum waves per SIMD requested from the
+// register allocator, and non-temporal stores for the streamed outputs.
+#ifndef CGTP_TP_FWD_WAVES
+#define CGTP_TP_FWD_WAVES 0
+#endif
+#ifndef CGTP_TP_BWD_WAVES
+#define CGTP_TP_BWD_WAVES 0
+#endif
+#ifndef CGTP_NT_STORE
+#define CGTP_NT_STORE 0
+#endif
+#if CGTP_TP_FWD_WAVES > 0
+#define CGTP_FWD_OCC __attribute__((amdgpu_waves_per_eu(CGTP_TP_FWD_WAVES)))
+#else
+#define CGTP_FWD_OCC
+#endif
+#if CGTP_TP_BWD_WAVES > 0
+#define CGTP_BWD_OCC __attribute__((amdgpu_waves_per_eu(CGTP_TP_BWD_WAVES)))
+#else
+#define CGTP_BWD_OCC
+#endif
+
 namespace cgtp {
 
 struct TPArgs {
@@ -49,9 +71,14 @@ struct TPArgs {
   int nblocks;
   int lpr_log2;  // lanes per row = 1 << lpr_log2
   int ngroups;   // channel groups per row = ceil(max_mul / VEC)
+  int block;     // x block of a degree-specialised launch
+  int dy_accum;  // add grad_y to what an earlier launch on the stream wrote
 };
 
-template <typename T, typename A, int VEC>
+// LM: largest l2 and l3 compiled into a kernel (the plan's largest y or
+// output degree); L1 is fixed per kernel, so each kernel only holds the paths
+// one x block can take, which keeps registers and code size small.
+template <typename T, typename A, int VEC, int LM>
 struct TPFwd {
   template <int L1, int L2, int L3>
   __device__ static __forceinline__ void path(const TPArgs& a, const PathDev& pd,
@@ -66,7 +93,10 @@ struct TPFwd {
     for (int m = 0; m < 2 * L3 + 1; ++m) {
 #pragma unroll
       for (int v = 0; v < VEC; ++v) o[m][v] *= wv[v];
-      VecIO<T, VEC>::store(outr + pd.out_off + m * pd.mul + c, o[m]);
+      if constexpr (CGTP_NT_STORE != 0)
+        VecIO<T, VEC>::store_nt(outr + pd.out_off + m * pd.mul + c, o[m]);
+      else
+        VecIO<T, VEC>::store(outr + pd.out_off + m * pd.mul + c, o[m]);
     }
   }
 
@@ -75,12 +105,12 @@ struct TPFwd {
                                              const A (&xb)[2 * L1 + 1][VEC], const T* yr,
                                              const T* wr, T* outr, int c) {
     A yb[2 * L2 + 1];
-    const int yoff = a.paths[p].y_off;
+    const int yoff = ldc(&a.paths[p].y_off);
 #pragma unroll
     for (int m = 0; m < 2 * L2 + 1; ++m) yb[m] = to_acc<A>(yr[yoff + m]);
     for (int q = p; q < pend; ++q) {
-      const PathDev pd = a.paths[q];
-      static_for<0, kLmax + 1>([&](auto L3c) {
+      const PathDev pd = ldc(a.paths + q);
+      static_for<0, LM + 1>([&](auto L3c) {
         constexpr int L3 = decltype(L3c)::value;
         if constexpr (L3 >= (L1 > L2 ? L1 - L2 : L2 - L1) && L3 <= L1 + L2) {
           if (pd.l3 == L3) path<L1, L2, L3>(a, pd, xb, yb, wr, outr, c);
@@ -97,9 +127,9 @@ struct TPFwd {
     for (int m = 0; m < 2 * L1 + 1; ++m) VecIO<T, VEC>::load(xr + blk.x_off + m * blk.mul + c, xb[m]);
     int p = blk.path_begin;
     while (p < blk.path_end) {
-      const int l2 = a.paths[p].l2;
-      const int pend = a.paths[p].i2_end;
-      static_for<0, kLmax + 1>([&](auto L2c) {
+      const int l2 = ldc(&a.paths[p].l2);
+      const int pend = ldc(&a.paths[p].i2_end);
+      static_for<0, LM + 1>([&](auto L2c) {
         constexpr int L2 = decltype(L2c)::value;
         if (l2 == L2) run<L1, L2>(a, p, pend, xb, yr, wr, outr, c);
       });
@@ -108,8 +138,10 @@ struct TPFwd {
   }
 };
 
-template <typename T, typename A, int VEC>
-__global__ __launch_bounds__(kBlock) void tp_fwd_kernel(TPArgs a) {
+// L1 >= 0: one x block (a.block) of degree L1; L1 < 0: every block, degree
+// dispatched at run time (the general kernel, LM = CGTP_LMAX).
+template <typename T, typename A, int VEC, int L1, int LM>
+__global__ __launch_bounds__(kBlock) CGTP_FWD_OCC void tp_fwd_kernel(TPArgs a) {
   const int64_t gt = int64_t(blockIdx.x) * kBlock + threadIdx.x;
   const int64_t row = gt >> a.lpr_log2;
   const int lpr = 1 << a.lpr_log2;
@@ -121,20 +153,25 @@ __global__ __launch_bounds__(kBlock) void tp_fwd_kernel(TPArgs a) {
   T* outr = static_cast<T*>(a.out) + row * a.dim_out;
   for (int grp = lr; grp < a.ngroups; grp += lpr) {
     const int c = grp * VEC;
-    for (int b = 0; b < a.nblocks; ++b) {
-      const BlockDev blk = a.blocks[b];
-      if (c >= blk.mul) continue;
-      static_for<0, kLmax + 1>([&](auto L1c) {
-        constexpr int L1 = decltype(L1c)::value;
-        if (blk.l1 == L1) TPFwd<T, A, VEC>::template block<L1>(a, blk, xr, yr, wr, outr, c);
-      });
+    if constexpr (L1 >= 0) {
+      const BlockDev blk = ldc(a.blocks + a.block);
+      if (c < blk.mul) TPFwd<T, A, VEC, LM>::template block<L1>(a, blk, xr, yr, wr, outr, c);
+    } else {
+      for (int b = 0; b < a.nblocks; ++b) {
+        const BlockDev blk = ldc(a.blocks + b);
+        if (c >= blk.mul) continue;
+        static_for<0, kLmax + 1>([&](auto L1c) {
+          constexpr int D = decltype(L1c)::value;
+          if (blk.l1 == D) TPFwd<T, A, VEC, LM>::template block<D>(a, blk, xr, yr, wr, outr, c);
+        });
+      }
     }
   }
 }
 
 // ------------------------------------------------------------------ backward
 
-template <typename T, typename A, int VEC>
+template <typename T, typename A, int VEC, int LM>
 struct TPBwd {
   template <int L1, int L2, int L3>
   __device__ static __forceinline__ void path(const TPArgs& a, const PathDev& pd,
@@ -165,11 +202,11 @@ struct TPBwd {
     // q[m1] = sum_m3 A[m1,m3] g[m3]   (A = C y);  dy[m2] += C sum_u w x[m1] g[m3]
     static_for<0, P::NP>([&](auto I) {
       constexpr PairT pr = P::arr.p[decltype(I)::value];
-      const A ca = cf[pr.coef];
+      const A ca = ldc(cf + pr.coef);
       A av = ca * yb[pr.m2a + L2];
       A cb = A(0);
       if constexpr (pr.n == 2) {
-        cb = cf[pr.coef + 1];
+        cb = ldc(cf + pr.coef + 1);
         av = fma(cb, yb[pr.m2b + L2], av);
       }
       A s = A(0);
@@ -202,15 +239,15 @@ struct TPBwd {
                                              const T* gr, const T* wr, T* dwr, A* dwa, int c,
                                              A (&dxb)[2 * L1 + 1][VEC], A* lds) {
     A yb[2 * L2 + 1], dyb[2 * L2 + 1];
-    const int yoff = a.paths[p].y_off;
+    const int yoff = ldc(&a.paths[p].y_off);
 #pragma unroll
     for (int m = 0; m < 2 * L2 + 1; ++m) {
       yb[m] = to_acc<A>(yr[yoff + m]);
       dyb[m] = A(0);
     }
     for (int q = p; q < pend; ++q) {
-      const PathDev pd = a.paths[q];
-      static_for<0, kLmax + 1>([&](auto L3c) {
+      const PathDev pd = ldc(a.paths + q);
+      static_for<0, LM + 1>([&](auto L3c) {
         constexpr int L3 = decltype(L3c)::value;
         if constexpr (L3 >= (L1 > L2 ? L1 - L2 : L2 - L1) && L3 <= L1 + L2) {
           if (pd.l3 == L3) path<L1, L2, L3>(a, pd, xb, yb, gr, wr, dwr, dwa, c, dxb, dyb);
@@ -235,9 +272,9 @@ struct TPBwd {
     }
     int p = blk.path_begin;
     while (p < blk.path_end) {
-      const int l2 = a.paths[p].l2;
-      const int pend = a.paths[p].i2_end;
-      static_for<0, kLmax + 1>([&](auto L2c) {
+      const int l2 = ldc(&a.paths[p].l2);
+      const int pend = ldc(&a.paths[p].i2_end);
+      static_for<0, LM + 1>([&](auto L2c) {
         constexpr int L2 = decltype(L2c)::value;
         if (l2 == L2) run<L1, L2>(a, p, pend, xb, yr, gr, wr, dwr, dwa, c, dxb, lds);
       });
@@ -254,8 +291,8 @@ struct TPBwd {
   }
 };
 
-template <typename T, typename A, int VEC>
-__global__ __launch_bounds__(kBlock) void tp_bwd_kernel(TPArgs a) {
+template <typename T, typename A, int VEC, int L1, int LM>
+__global__ __launch_bounds__(kBlock) CGTP_BWD_OCC void tp_bwd_kernel(TPArgs a) {
   extern __shared__ unsigned char smem_raw[];
   A* lds = reinterpret_cast<A*>(smem_raw);  // [dim_y][kBlock], one column per lane
   const int64_t gt = int64_t(blockIdx.x) * kBlock + threadIdx.x;
@@ -277,22 +314,32 @@ __global__ __launch_bounds__(kBlock) void tp_bwd_kernel(TPArgs a) {
     A* dwa = a.dw_ws ? static_cast<A*>(a.dw_ws) + row * a.W : nullptr;
     for (int grp = lr; grp < a.ngroups; grp += lpr) {
       const int c = grp * VEC;
-      for (int b = 0; b < a.nblocks; ++b) {
-        const BlockDev blk = a.blocks[b];
-        if (c >= blk.mul) continue;
-        static_for<0, kLmax + 1>([&](auto L1c) {
-          constexpr int L1 = decltype(L1c)::value;
-          if (blk.l1 == L1)
-            TPBwd<T, A, VEC>::template block<L1>(a, blk, xr, yr, gr, wr, dxr, dxa, dwr, dwa, c, lds);
-        });
+      if constexpr (L1 >= 0) {
+        const BlockDev blk = ldc(a.blocks + a.block);
+        if (c < blk.mul)
+          TPBwd<T, A, VEC, LM>::template block<L1>(a, blk, xr, yr, gr, wr, dxr, dxa, dwr, dwa, c, lds);
+      } else {
+        for (int b = 0; b < a.nblocks; ++b) {
+          const BlockDev blk = ldc(a.blocks + b);
+          if (c >= blk.mul) continue;
+          static_for<0, kLmax + 1>([&](auto L1c) {
+            constexpr int D = decltype(L1c)::value;
+            if (blk.l1 == D)
+              TPBwd<T, A, VEC, LM>::template block<D>(a, blk, xr, yr, gr, wr, dxr, dxa, dwr, dwa, c, lds);
+          });
+        }
       }
     }
   }
-  // grad_y: sum the row's lanes; lane k % lpr writes component k
+  // grad_y: sum the row's lanes; lane k % lpr writes component k (adding to
+  // what the previous x block's launch wrote, in stream order)
   T* dyr = (a.dy && active) ? static_cast<T*>(a.dy) + row * a.dim_y : nullptr;
   for (int k = 0; k < a.dim_y; ++k) {
-    const A v = group_sum(lds[k * kBlock + threadIdx.x], lpr);
-    if (dyr && lr == (k & (lpr - 1))) from_acc(dyr[k], v);
+    A v = group_sum(lds[k * kBlock + threadIdx.x], lpr);
+    if (dyr && lr == (k & (lpr - 1))) {
+      if (a.dy_accum) v += to_acc<A>(dyr[k]);
+      from_acc(dyr[k], v);
+    }
   }
 }
 
@@ -331,21 +378,56 @@ inline dim3 grid_for(int64_t B, int lpr_log2) {
   return dim3(unsigned((B + rows_per_block - 1) / rows_per_block));
 }
 
+// l1 < 0 (and every VEC = 1 build): the general kernel over all x blocks;
+// otherwise the kernel specialised for x degree l1 and largest degree lm.
 template <typename T, int VEC>
-void tp_fwd_typed(const TPArgs& a, hipStream_t s) {
+void tp_fwd_typed(const TPArgs& a, int l1, int lm, hipStream_t s) {
   using A = typename AccOf<T>::type;
-  hipLaunchKernelGGL((tp_fwd_kernel<T, A, VEC>), grid_for(a.B, a.lpr_log2), dim3(kBlock), 0, s, a);
+  const dim3 grid = grid_for(a.B, a.lpr_log2);
+  if constexpr (VEC == 1) {
+    (void)l1;
+    (void)lm;
+    hipLaunchKernelGGL((tp_fwd_kernel<T, A, VEC, -1, kLmax>), grid, dim3(kBlock), 0, s, a);
+  } else {
+    if (l1 < 0) {
+      hipLaunchKernelGGL((tp_fwd_kernel<T, A, VEC, -1, kLmax>), grid, dim3(kBlock), 0, s, a);
+      return;
+    }
+    static_for<0, kLmax + 1>([&](auto I) {
+      static_for<0, kLmax + 1>([&](auto J) {
+        constexpr int D = decltype(I)::value, M = decltype(J)::value;
+        if (l1 == D && lm == M)
+          hipLaunchKernelGGL((tp_fwd_kernel<T, A, VEC, D, M>), grid, dim3(kBlock), 0, s, a);
+      });
+    });
+  }
 }
 
 template <typename T, int VEC>
-void tp_bwd_typed(const TPArgs& a, hipStream_t s) {
+void tp_bwd_typed(const TPArgs& a, int l1, int lm, hipStream_t s) {
   using A = typename AccOf<T>::type;
+  const dim3 grid = grid_for(a.B, a.lpr_log2);
   const size_t lds = size_t(a.dim_y) * kBlock * sizeof(A);
-  hipLaunchKernelGGL((tp_bwd_kernel<T, A, VEC>), grid_for(a.B, a.lpr_log2), dim3(kBlock), lds, s, a);
+  if constexpr (VEC == 1) {
+    (void)l1;
+    (void)lm;
+    hipLaunchKernelGGL((tp_bwd_kernel<T, A, VEC, -1, kLmax>), grid, dim3(kBlock), lds, s, a);
+  } else {
+    if (l1 < 0) {
+      hipLaunchKernelGGL((tp_bwd_kernel<T, A, VEC, -1, kLmax>), grid, dim3(kBlock), lds, s, a);
+      return;
+    }
+    static_for<0, kLmax + 1>([&](auto I) {
+      static_for<0, kLmax + 1>([&](auto J) {
+        constexpr int D = decltype(I)::value, M = decltype(J)::value;
+        if (l1 == D && lm == M)
+          hipLaunchKernelGGL((tp_bwd_kernel<T, A, VEC, D, M>), grid, dim3(kBlock), lds, s, a);
+      });
+    });
+  }
 }
 
-#define CGTP_TP_EXTERN(T, V)                                           \
-  extern template void tp_fwd_typed<T, V>(const TPArgs&, hipStream_t); \
-  extern template void tp_bwd_typed<T, V>(const TPArgs&, hipStream_t);
+#define CGTP_TP_EXTERN_FWD(T, V) extern template void tp_fwd_typed<T, V>(const TPArgs&, int, int, hipStream_t);
+#define CGTP_TP_EXTERN_BWD(T, V) extern template void tp_bwd_typed<T, V>(const TPArgs&, int, int, hipStream_t);
 
 }  // namespace cgtp

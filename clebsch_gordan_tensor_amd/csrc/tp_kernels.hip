@@ -3,12 +3,26 @@
 
 namespace cgtp {
 
-CGTP_TP_EXTERN(float, 1)
-CGTP_TP_EXTERN(float, 4)
-CGTP_TP_EXTERN(bf16, 1)
-CGTP_TP_EXTERN(bf16, 4)
-CGTP_TP_EXTERN(double, 1)
-CGTP_TP_EXTERN(double, 2)
+CGTP_TP_EXTERN_FWD(float, 1)
+CGTP_TP_EXTERN_FWD(float, 4)
+CGTP_TP_EXTERN_FWD(bf16, 1)
+CGTP_TP_EXTERN_FWD(bf16, 4)
+CGTP_TP_EXTERN_FWD(double, 1)
+CGTP_TP_EXTERN_FWD(double, 2)
+CGTP_TP_EXTERN_BWD(float, 1)
+CGTP_TP_EXTERN_BWD(float, 2)
+CGTP_TP_EXTERN_BWD(float, 4)
+CGTP_TP_EXTERN_BWD(bf16, 1)
+CGTP_TP_EXTERN_BWD(bf16, 2)
+CGTP_TP_EXTERN_BWD(bf16, 4)
+CGTP_TP_EXTERN_BWD(double, 1)
+CGTP_TP_EXTERN_BWD(double, 2)
+
+// Channels per lane of the backward kernel for 4-byte and 2-byte storage
+// (the backward keeps more per-channel state than the forward).
+#ifndef CGTP_TP_BWD_VEC
+#define CGTP_TP_BWD_VEC 4
+#endif
 
 // ----------------------------------------------------------------- launchers
 
@@ -64,18 +78,26 @@ void tp_forward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* 
   a.y = y;
   a.w = w;
   a.out = out;
-  switch (plan->dtype) {
-    case CGTP_F32:
-      vec == 1 ? tp_fwd_typed<float, 1>(a, stream) : tp_fwd_typed<float, 4>(a, stream);
-      break;
-    case CGTP_BF16:
-      vec == 1 ? tp_fwd_typed<bf16, 1>(a, stream) : tp_fwd_typed<bf16, 4>(a, stream);
-      break;
-    case CGTP_F64:
-      vec == 1 ? tp_fwd_typed<double, 1>(a, stream) : tp_fwd_typed<double, 2>(a, stream);
-      break;
+  // one launch per x block with the kernel specialised for its degree (the
+  // general kernel in one launch when channels are not vectorised)
+  const int nb = vec == 1 ? 1 : int(plan->blocks.size());
+  for (int b = 0; b < nb; ++b) {
+    a.block = b;
+    const int l1 = vec == 1 ? -1 : plan->blocks[size_t(b)].l1;
+    switch (plan->dtype) {
+      case CGTP_F32:
+        vec == 1 ? tp_fwd_typed<float, 1>(a, l1, plan->lm, stream) : tp_fwd_typed<float, 4>(a, l1, plan->lm, stream);
+        break;
+      case CGTP_BF16:
+        vec == 1 ? tp_fwd_typed<bf16, 1>(a, l1, plan->lm, stream) : tp_fwd_typed<bf16, 4>(a, l1, plan->lm, stream);
+        break;
+      case CGTP_F64:
+        vec == 1 ? tp_fwd_typed<double, 1>(a, l1, plan->lm, stream)
+                 : tp_fwd_typed<double, 2>(a, l1, plan->lm, stream);
+        break;
+    }
+    CGTP_CHECK_HIP(hipGetLastError());
   }
-  CGTP_CHECK_HIP(hipGetLastError());
 }
 
 size_t tp_backward_ws_bytes(const cgtp_plan_s* plan, int64_t B) {
@@ -88,6 +110,7 @@ void tp_backward_rows(cgtp_plan_s* plan, const TPBackwardRows& r, hipStream_t st
   const DevTables& t = plan_tables(plan);
   const size_t es = dtype_size(plan->dtype), as = acc_size(plan->dtype);
   int vec = plan->vec;
+  if (plan->dtype != CGTP_F64 && vec > CGTP_TP_BWD_VEC) vec = CGTP_TP_BWD_VEC;
   if (!aligned(r.x, vec * es) || !aligned(r.w, vec * es) || !aligned(r.g, vec * es) ||
       !aligned(r.dx, vec * es) || !aligned(r.dw, vec * es) || !aligned(r.dx_ws, vec * as) ||
       !aligned(r.dw_ws, vec * as))
@@ -106,18 +129,29 @@ void tp_backward_rows(cgtp_plan_s* plan, const TPBackwardRows& r, hipStream_t st
   a.x_idx = r.x_idx;
   a.g_idx = r.g_idx;
   a.g_scale = r.g_scale;
-  switch (plan->dtype) {
-    case CGTP_F32:
-      vec == 1 ? tp_bwd_typed<float, 1>(a, stream) : tp_bwd_typed<float, 4>(a, stream);
-      break;
-    case CGTP_BF16:
-      vec == 1 ? tp_bwd_typed<bf16, 1>(a, stream) : tp_bwd_typed<bf16, 4>(a, stream);
-      break;
-    case CGTP_F64:
-      vec == 1 ? tp_bwd_typed<double, 1>(a, stream) : tp_bwd_typed<double, 2>(a, stream);
-      break;
+  // one launch per x block (degree-specialised); grad_y accumulates across
+  // the launches in stream order, so its summation order is fixed
+  const int nb = vec == 1 ? 1 : int(plan->blocks.size());
+  const int lm = plan->lm;
+  for (int b = 0; b < nb; ++b) {
+    a.block = b;
+    a.dy_accum = b > 0 ? 1 : 0;
+    const int l1 = vec == 1 ? -1 : plan->blocks[size_t(b)].l1;
+    switch (plan->dtype) {
+      case CGTP_F32:
+        vec == 1 ? tp_bwd_typed<float, 1>(a, l1, lm, stream)
+                 : (vec == 2 ? tp_bwd_typed<float, 2>(a, l1, lm, stream) : tp_bwd_typed<float, 4>(a, l1, lm, stream));
+        break;
+      case CGTP_BF16:
+        vec == 1 ? tp_bwd_typed<bf16, 1>(a, l1, lm, stream)
+                 : (vec == 2 ? tp_bwd_typed<bf16, 2>(a, l1, lm, stream) : tp_bwd_typed<bf16, 4>(a, l1, lm, stream));
+        break;
+      case CGTP_F64:
+        vec == 1 ? tp_bwd_typed<double, 1>(a, l1, lm, stream) : tp_bwd_typed<double, 2>(a, l1, lm, stream);
+        break;
+    }
+    CGTP_CHECK_HIP(hipGetLastError());
   }
-  CGTP_CHECK_HIP(hipGetLastError());
 }
 
 void tp_backward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* y,
