@@ -329,6 +329,214 @@ __global__ __launch_bounds__(kBlock) void conv_fwd_general_kernel(ConvArgs a) {
   });
 }
 
+// ------------------------------------------------------------ fused backward
+#ifndef CGTP_CONV_BWD_VEC
+#define CGTP_CONV_BWD_VEC 4
+#endif
+
+// Extra arguments of the fused backward.
+struct ConvBwdArgs {
+  const void* g;  // grad_out [N][dim_out]
+  void* dsh;      // grad_sh [E][dim_y] (accumulated over x blocks in stream order)
+  void* dw;       // grad_w [E][W]
+  void* dxp;      // grad_x partials [E][dim_x], accumulation type
+  int dy_accum;
+};
+
+// One workgroup = (receiver n, x block b, channel chunk). The block's slice
+// of scale * grad_out[n] is staged in LDS ([slot accumulator row][channel]);
+// lane groups of LG lanes sweep the receiver's edges; per edge they form the
+// transposed products of every path of the block:
+//   q[m1]   = sum_m3 A[m1,m3] g[m3]                      (A = C y)
+//   grad_w  = sum_m1 x[m1] q[m1]                          -> stored per edge
+//   dx_e   += w q[m1]                                     -> per-edge partial
+//   dy[m2] += C sum_u w x[m1] g[m3]                       -> reduced over the group
+template <typename T, typename A, int VEC, int L1, int L>
+__global__ __launch_bounds__(kBlock) void conv_bwd_fused_kernel(ConvArgs a, ConvBwdArgs bw) {
+  using S = Slots<L1, L>;
+  constexpr int NS = S::NS;
+  constexpr int NY = (L + 1) * (L + 1);
+  extern __shared__ unsigned char smem_raw[];
+  A* gl = reinterpret_cast<A*>(smem_raw);
+  const int LG = 1 << a.lg_log2;
+  const int CW = LG * VEC;  // channels per chunk
+  const int64_t n = blockIdx.x / a.nchunks;
+  const int cc = int(blockIdx.x - n * a.nchunks);
+  const BlockDev blk = ldc(a.blocks + a.block);
+  const int U = blk.mul;
+  int pid[NS], woff[NS], coff[NS];
+  const int so = ldc(a.slot_off + a.block);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    pid[s] = ldc(a.slot_paths + so + s);
+    woff[s] = pid[s] >= 0 ? ldc(&a.paths[pid[s]].w_off) : 0;
+    coff[s] = pid[s] >= 0 ? ldc(&a.paths[pid[s]].coef_off) : 0;
+  }
+  // stage scale * grad_out[n] for this block and channel chunk
+  const T* __restrict__ gn = static_cast<const T*>(bw.g) + n * a.dim_out;
+  const A sc = A(a.scale);
+  static_for<0, NS>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    constexpr SlotT st = S::arr.p[i];
+    if (pid[i] >= 0) {
+      const int oo = ldc(&a.paths[pid[i]].out_off);
+      for (int k = threadIdx.x; k < (2 * st.l3 + 1) * CW; k += kBlock) {
+        const int m = k / CW, cl = k - m * CW, c = cc * CW + cl;
+        gl[(st.acc + m) * CW + cl] = c < U ? sc * to_acc<A>(gn[oo + m * U + c]) : A(0);
+      }
+    }
+  });
+  __syncthreads();
+  const int NG = kBlock / LG;
+  const int gi = int(threadIdx.x) / LG, li = int(threadIdx.x) - gi * LG;
+  const int c = cc * CW + li * VEC;
+  const bool valid = c < U;
+  const A* __restrict__ cf = static_cast<const A*>(a.coef);
+  const T* __restrict__ X = static_cast<const T*>(a.x);
+  const int32_t e0 = a.row_ptr[n], e1 = a.row_ptr[n + 1];
+  // every lane of a group runs the same trip count (shuffles below)
+  for (int32_t e = e0 + gi; e < e1; e += NG) {
+    const int64_t j = a.src[e];
+    A xb[2 * L1 + 1][VEC], dxe[2 * L1 + 1][VEC];
+#pragma unroll
+    for (int m = 0; m < 2 * L1 + 1; ++m) {
+      if (valid) VecIO<T, VEC>::load(X + j * a.dim_x + blk.x_off + m * U + c, xb[m]);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        if (!valid) xb[m][v] = A(0);
+        dxe[m][v] = A(0);
+      }
+    }
+    const T* __restrict__ Ye = static_cast<const T*>(a.sh) + int64_t(e) * a.dim_y;
+    T* __restrict__ dwe = static_cast<T*>(bw.dw) + int64_t(e) * a.W;
+    const T* __restrict__ we = static_cast<const T*>(a.w) + int64_t(e) * a.W;
+    A dyl[NY];
+#pragma unroll
+    for (int k = 0; k < NY; ++k) dyl[k] = A(0);
+    A ycur[2 * L + 1];
+    static_for<0, NS>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      constexpr SlotT st = S::arr.p[i];
+      constexpr int L2 = st.l2, L3 = st.l3;
+      constexpr bool first_of_l2 = (i == 0) || (S::arr.p[i > 0 ? i - 1 : 0].l2 != L2);
+      if constexpr (first_of_l2) {
+        const int yo = a.yoff[L2];
+        if (yo >= 0) {
+#pragma unroll
+          for (int m = 0; m < 2 * L2 + 1; ++m) ycur[m] = to_acc<A>(Ye[yo + m]);
+        }
+      }
+      if (pid[i] >= 0) {
+        using P = Pattern<L1, L2, L3>;
+        const A* __restrict__ cp = cf + coff[i];
+        A gb[2 * L3 + 1][VEC];
+#pragma unroll
+        for (int m = 0; m < 2 * L3 + 1; ++m)
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) gb[m][v] = gl[(st.acc + m) * CW + li * VEC + v];
+        A wv[VEC];
+        if (valid) {
+          VecIO<T, VEC>::load(we + woff[i] + c, wv);
+        } else {
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) wv[v] = A(0);
+        }
+        A xw[2 * L1 + 1][VEC], q[2 * L1 + 1][VEC];
+#pragma unroll
+        for (int m = 0; m < 2 * L1 + 1; ++m)
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) {
+            xw[m][v] = xb[m][v] * wv[v];
+            q[m][v] = A(0);
+          }
+        static_for<0, P::NP>([&](auto K) {
+          constexpr PairT pr = P::arr.p[decltype(K)::value];
+          const A ca = ldc(cp + pr.coef);
+          A av = ca * ycur[pr.m2a + L2];
+          A cb = A(0);
+          if constexpr (pr.n == 2) {
+            cb = ldc(cp + pr.coef + 1);
+            av = fma(cb, ycur[pr.m2b + L2], av);
+          }
+          A sdot = A(0);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) {
+            q[pr.m1 + L1][v] = fma(av, gb[pr.m3 + L3][v], q[pr.m1 + L1][v]);
+            sdot = fma(xw[pr.m1 + L1][v], gb[pr.m3 + L3][v], sdot);
+          }
+          dyl[L2 * L2 + L2 + pr.m2a] = fma(ca, sdot, dyl[L2 * L2 + L2 + pr.m2a]);
+          if constexpr (pr.n == 2) dyl[L2 * L2 + L2 + pr.m2b] = fma(cb, sdot, dyl[L2 * L2 + L2 + pr.m2b]);
+        });
+        A d[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) d[v] = A(0);
+#pragma unroll
+        for (int m = 0; m < 2 * L1 + 1; ++m)
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) {
+            d[v] = fma(xb[m][v], q[m][v], d[v]);
+            dxe[m][v] = fma(wv[v], q[m][v], dxe[m][v]);
+          }
+        if (valid && bw.dw) VecIO<T, VEC>::store(dwe + woff[i] + c, d);
+      }
+    });
+    if (valid && bw.dxp) {
+      A* __restrict__ dxr = static_cast<A*>(bw.dxp) + int64_t(e) * a.dim_x + blk.x_off;
+#pragma unroll
+      for (int m = 0; m < 2 * L1 + 1; ++m) VecIO<A, VEC>::store(dxr + m * U + c, dxe[m]);
+    }
+    // grad_sh: sum over the group's channels; lane 0 of the group writes
+    if (!bw.dsh) continue;
+    T* __restrict__ dye = static_cast<T*>(bw.dsh) + int64_t(e) * a.dim_y;
+    static_for<0, L + 1>([&](auto L2c) {
+      constexpr int L2 = decltype(L2c)::value;
+      const int yo = a.yoff[L2];
+      if (yo >= 0) {
+#pragma unroll
+        for (int m = 0; m < 2 * L2 + 1; ++m) {
+          A v = dyl[L2 * L2 + m];
+          for (int off = 1; off < LG; off <<= 1) v += __shfl_xor(v, off, 64);
+          if (li == 0) {
+            if (bw.dy_accum) v += to_acc<A>(dye[yo + m]);
+            from_acc(dye[yo + m], v);
+          }
+        }
+      }
+    });
+  }
+}
+
+template <typename T>
+size_t conv_bwd_fused_lds(int l1, int L, int cw) {
+  using A = typename AccOf<T>::type;
+  size_t r = 0;
+  static_for<0, kLmax + 1>([&](auto I) {
+    static_for<0, kLmax + 1>([&](auto J) {
+      constexpr int D = decltype(I)::value, M = decltype(J)::value;
+      if constexpr (Slots<D, M>::NS > 0) {
+        if (l1 == D && L == M) r = size_t(Slots<D, M>::NACC) * size_t(cw) * sizeof(A);
+      }
+    });
+  });
+  return r;
+}
+
+template <typename T>
+void conv_bwd_fused_typed(const ConvArgs& a, const ConvBwdArgs& b, int l1, int L, dim3 grid, size_t lds,
+                          hipStream_t s) {
+  using A = typename AccOf<T>::type;
+  constexpr int VEC = std::is_same<T, double>::value ? 2 : CGTP_CONV_BWD_VEC;
+  static_for<0, kLmax + 1>([&](auto I) {
+    static_for<0, kLmax + 1>([&](auto J) {
+      constexpr int D = decltype(I)::value, M = decltype(J)::value;
+      if constexpr (Slots<D, M>::NS > 0) {
+        if (l1 == D && L == M)
+          hipLaunchKernelGGL((conv_bwd_fused_kernel<T, A, VEC, D, M>), grid, dim3(kBlock), lds, s, a, b);
+      }
+    });
+  });
+}
+
 // ------------------------------------------------------------ typed launchers
 // One translation unit per (kind, storage type): inst/conv_*.hip.
 constexpr int conv_vec(cgtp_dtype d) { return d == CGTP_F64 ? 2 : 4; }
@@ -373,6 +581,9 @@ void conv_fwd_general_typed(const ConvArgs& a, dim3 grid, hipStream_t s) {
 #define CGTP_CONV_EXTERN(T)                                                                   \
   extern template void conv_fwd_fused_typed<T>(const ConvArgs&, int, int, dim3, hipStream_t); \
   extern template void conv_fwd_general_typed<T>(const ConvArgs&, dim3, hipStream_t);         \
-  extern template int conv_fused_chunks<T>(int, int);
+  extern template int conv_fused_chunks<T>(int, int);                                        \
+  extern template void conv_bwd_fused_typed<T>(const ConvArgs&, const ConvBwdArgs&, int, int, dim3, size_t, \
+                                               hipStream_t);                                   \
+  extern template size_t conv_bwd_fused_lds<T>(int, int, int);
 
 }  // namespace cgtp

@@ -1,4 +1,6 @@
 // Launchers of the message-passing convolution (kernels in conv_impl.hpp).
+#include <vector>
+
 #include "conv_impl.hpp"
 
 namespace cgtp {
@@ -84,6 +86,73 @@ void dx_gather(const cgtp_graph_s* g, const void* part, void* dx, int dim_x, hip
   CGTP_CHECK_HIP(hipGetLastError());
 }
 
+template <typename T>
+void bwd_fused_typed(const ConvArgs& a, const ConvBwdArgs& b, int l1, int L, dim3 grid, size_t lds, hipStream_t s) {
+  conv_bwd_fused_typed<T>(a, b, l1, L, grid, lds, s);
+}
+
+// Receiver-ordered backward; returns false when the plan or the pointers do
+// not fit it (then the row-parallel backward over gathered rows is used).
+bool conv_backward_fused(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x, const void* sh,
+                         const void* w, double scale, const void* grad_out, void* grad_x, void* grad_sh,
+                         void* grad_w, void* ws, hipStream_t s) {
+  const int VEC = plan->dtype == CGTP_F64 ? 2 : CGTP_CONV_BWD_VEC;
+  const size_t vb = size_t(VEC) * dtype_size(plan->dtype);
+  if (!plan->conv_fused || plan->vec % VEC != 0) return false;
+  for (const void* p : {x, w, grad_out, static_cast<const void*>(grad_w)})
+    if (p && !aligned_to(p, vb)) return false;
+  if (grad_x && !aligned_to(ws, size_t(VEC) * acc_size(plan->dtype))) return false;
+  std::vector<int> lgs;
+  std::vector<size_t> ldss;
+  for (const BlockInfo& blk : plan->blocks) {
+    const int lanes = (blk.mul + VEC - 1) / VEC;
+    if (lanes > 64) return false;  // one channel chunk per receiver keeps grad_sh race-free
+    int lg = 0;
+    while ((1 << lg) < lanes) ++lg;
+    size_t lds = 0;
+    switch (plan->dtype) {
+      case CGTP_F32: lds = conv_bwd_fused_lds<float>(blk.l1, plan->conv_L, (1 << lg) * VEC); break;
+      case CGTP_F64: lds = conv_bwd_fused_lds<double>(blk.l1, plan->conv_L, (1 << lg) * VEC); break;
+      case CGTP_BF16: lds = conv_bwd_fused_lds<bf16>(blk.l1, plan->conv_L, (1 << lg) * VEC); break;
+    }
+    if (lds == 0 || lds > 64 * 1024) return false;
+    lgs.push_back(lg);
+    ldss.push_back(lds);
+  }
+  const DevTables& t = plan_tables(plan);
+  ConvArgs a = make_conv_args(plan, t, g);
+  a.x = x;
+  a.sh = sh;
+  a.w = w;
+  a.scale = scale;
+  a.nchunks = 1;
+  ConvBwdArgs b{};
+  b.g = grad_out;
+  b.dsh = grad_sh;
+  b.dw = grad_w;
+  b.dxp = grad_x ? ws : nullptr;
+  for (size_t k = 0; k < plan->blocks.size(); ++k) {
+    a.block = int(k);
+    a.lg_log2 = lgs[k];
+    b.dy_accum = k > 0 ? 1 : 0;
+    const dim3 grid(unsigned(g->N));
+    switch (plan->dtype) {
+      case CGTP_F32: bwd_fused_typed<float>(a, b, plan->blocks[k].l1, plan->conv_L, grid, ldss[k], s); break;
+      case CGTP_F64: bwd_fused_typed<double>(a, b, plan->blocks[k].l1, plan->conv_L, grid, ldss[k], s); break;
+      case CGTP_BF16: bwd_fused_typed<bf16>(a, b, plan->blocks[k].l1, plan->conv_L, grid, ldss[k], s); break;
+    }
+    CGTP_CHECK_HIP(hipGetLastError());
+  }
+  if (grad_x) {
+    switch (plan->dtype) {
+      case CGTP_F32: dx_gather<float>(g, ws, grad_x, int(plan->dim_x), s); break;
+      case CGTP_F64: dx_gather<double>(g, ws, grad_x, int(plan->dim_x), s); break;
+      case CGTP_BF16: dx_gather<bf16>(g, ws, grad_x, int(plan->dim_x), s); break;
+    }
+  }
+  return true;
+}
+
 }  // namespace
 
 void conv_forward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x, const void* sh,
@@ -124,6 +193,7 @@ void conv_backward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* 
       throw Error{CGTP_ERR_WORKSPACE, "conv_backward needs " + std::to_string(need) + " workspace bytes"};
   }
   if (!grad_x && !grad_sh && !grad_w) return;
+  if (conv_backward_fused(plan, g, x, sh, w, scale, grad_out, grad_x, grad_sh, grad_w, ws, s)) return;
   TPBackwardRows r;
   r.rows = g->E;
   r.x = x;
