@@ -42,7 +42,21 @@ def parse():
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 4 GiB device copy (reference for HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def calibrate_copy(torch):
+    """A plain elementwise copy of known size: 4 GiB read + 4 GiB written per launch."""
+    n = 1 << 30
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "elementwise copy", "bytes_read_per_launch": 4 * n,
+                      "bytes_written_per_launch": 4 * n, "launches": 3}), flush=True)
 
 
 def kernel_source_hash(names):
@@ -84,6 +98,11 @@ class KernelTimer:
 
     def mean_ms(self):
         return sum(s.elapsed_time(e) for s, e in self.pairs) / len(self.pairs)
+
+
+def plan_blocks(plan):
+    """x blocks of a plan (one kernel launch each)."""
+    return [t for t in plan.irreps_x.replace(" ", "").split("+") if t]
 
 
 def tp_large_bench(args, torch, cgtp, synth, extra):
@@ -141,7 +160,9 @@ def tp_large_bench(args, torch, cgtp, synth, extra):
     d = kern[dom]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": d["algorithmic_GBs"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": d["frac_of_hbm_peak"], "traffic": d["traffic"],
-                "algorithmic_bytes_per_launch": d["bytes_per_row"] * B, "mean_launch_ms": d["ms"]}
+                "algorithmic_bytes_per_launch": d["bytes_per_row"] * B, "mean_launch_ms": d["ms"],
+                "launch": "one call = %d launches of %s (one per x block, degree-specialised)"
+                          % (len(plan_blocks(plan)), dom)}
     for k in kern.values():
         k.pop("_srcs")
     extra["tp_large_kernels"] = kern
@@ -192,7 +213,13 @@ def conv_bench(args, torch, cgtp, synth, name, steps):
     bf = 4 * (plan.w_numel + plan.dim_y + 1) * E + 4 * (plan.dim_out + plan.dim_x + 1) * N
     bb = 4 * (2 * plan.w_numel + 2 * plan.dim_y + 1) * E + 4 * (plan.dim_out + 2 * plan.dim_x + 1) * N
     msf, msb = tf.mean_ms(), tb.mean_ms()
-    res = dict(N=N, E=E, paths=plan.num_paths,
+    cv = ["conv_impl.hpp", "conv_kernels.hip", "tp_core.hpp", "cg_pattern.h", "device_util.hpp"]
+    tr_f = traffic_for("conv_fwd_fused_kernel", cv, E) if name == "conv_uniform100k" else None
+    tr_b = None
+    if name == "conv_uniform100k":
+        b1, b2 = traffic_for("conv_bwd_fused_kernel", cv, E), traffic_for("dx_gather_kernel", cv, E)
+        tr_b = b1 + b2 if b1 is not None and b2 is not None else None
+    res = dict(N=N, E=E, paths=plan.num_paths, fwd_traffic_bytes=tr_f, bwd_traffic_bytes=tr_b,
                fwd_ms=round(msf, 3), fwd_edges_per_s=E / (msf * 1e-3),
                fwd_algorithmic_GBs=round(bf / (msf * 1e-3) / 1e9, 1),
                fwd_frac_of_hbm_peak=round(bf / (msf * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -242,6 +269,9 @@ def main():
     from clebsch_gordan_tensor_amd import cgtp, synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
     extra = {"device": torch.cuda.get_device_name(0)}
     value, ms_step, roofline, plan = tp_large_bench(args, torch, cgtp, synth, extra)
     if not args.no_conv:
