@@ -173,6 +173,39 @@ def tp_large_bench(args, torch, cgtp, synth, extra):
     return B * args.steps / wall, ms_step, roofline, plan
 
 
+def tp_large_bf16(args, torch, cgtp, synth):
+    """tp_large in bf16 storage (fp32 arithmetic): forward and backward call times."""
+    c = synth.CONFIGS["tp_large"]
+    plan = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"], dtype="bf16", wkind="per_row")
+    B = c["B"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    bf = torch.bfloat16
+    x = torch.randn((B, plan.dim_x), generator=gen, device="cuda").to(bf)
+    w = torch.randn((B, plan.w_numel), generator=gen, device="cuda").to(bf)
+    g = torch.randn((B, plan.dim_out), generator=gen, device="cuda").to(bf)
+    y = torch.randn((B, plan.dim_y), generator=gen, device="cuda").to(bf)
+    out = torch.empty((B, plan.dim_out), device="cuda", dtype=bf)
+    dx, dy, dw = torch.empty_like(x), torch.empty_like(y), torch.empty_like(w)
+    tf, tb = KernelTimer(torch), KernelTimer(torch)
+    for k in range(4):
+        if k == 0:
+            plan.tp_forward(x, y, w, out=out)
+            plan.tp_backward(x, y, w, g, out=(dx, dy, dw))
+        else:
+            tf(lambda: plan.tp_forward(x, y, w, out=out))
+            tb(lambda: plan.tp_backward(x, y, w, g, out=(dx, dy, dw)))
+    torch.cuda.synchronize()
+    by_f = 2 * (plan.dim_x + plan.dim_y + plan.w_numel + plan.dim_out)
+    by_b = 2 * (2 * plan.dim_x + 2 * plan.dim_y + 2 * plan.w_numel + plan.dim_out)
+    f, b = tf.mean_ms(), tb.mean_ms()
+    del x, w, g, y, out, dx, dy, dw
+    torch.cuda.empty_cache()
+    return dict(fwd_ms=round(f, 3), fwd_pairs_per_s=B / (f * 1e-3), fwd_algorithmic_GBs=round(by_f * B / f / 1e6, 1),
+                bwd_ms=round(b, 3), fwd_bwd_pairs_per_s=B / ((f + b) * 1e-3),
+                bwd_algorithmic_GBs=round(by_b * B / b / 1e6, 1), bytes_per_row_fwd=by_f, bytes_per_row_bwd=by_b)
+
+
 def conv_bench(args, torch, cgtp, synth, name, steps):
     """Fused convolution forward + backward on one synthetic workload (extra figures)."""
     import numpy as np
@@ -274,9 +307,10 @@ def main():
         return
     extra = {"device": torch.cuda.get_device_name(0)}
     value, ms_step, roofline, plan = tp_large_bench(args, torch, cgtp, synth, extra)
+    extra["tp_large_bf16"] = tp_large_bf16(args, torch, cgtp, synth)
     if not args.no_conv:
-        extra["conv_uniform100k"] = conv_bench(args, torch, cgtp, synth, "conv_uniform100k",
-                                               max(2, min(args.steps, 5)))
+        for name in ("conv_water1k", "conv_uniform100k"):
+            extra[name] = conv_bench(args, torch, cgtp, synth, name, max(2, min(args.steps, 5)))
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, synth)
     line = {
         "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,

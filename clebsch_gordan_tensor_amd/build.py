@@ -74,6 +74,14 @@ def build(jobs=None, verbose=True, lib=LIB, build_dir=BUILD, defines=()):
     os.replace(tmp, lib)
     if verbose:
         print("  linked", lib, flush=True)
+    if lib == LIB:
+        probe = os.path.join(PKG, "hbm_probe")
+        cmd = [hipcc()] + common_flags(defines) + [os.path.join(CSRC, "tools", "hbm_probe.hip"), "-o", probe]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("probe build failed: %s\n%s" % (" ".join(cmd), r.stderr))
+        if verbose:
+            print("  built", probe, "(HBM bandwidth probe)", flush=True)
     return lib
 
 

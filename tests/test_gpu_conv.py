@@ -237,3 +237,62 @@ def test_conv_uniform100k_full_size_f64_forward():
     check_sampled(L, case, plan, x, Y, w, 1.0 / math.sqrt(case.E / case.N), "f64", backward=False)
     del x, Y, w
     torch.cuda.empty_cache()
+
+
+def test_wide_channels_and_fallback_paths():
+    """320 channels: the fused forward uses two channel chunks per receiver and the
+    backward takes the row-parallel fallback (more than 64 lanes per edge)."""
+    ix, iy, io = "320x0e+320x1o", "0e+1o+2e", "0e+1o+1e+2e"
+    L = Layout(ix, iy, io)
+    case = Case(synth.uniform_box(60, 6.0, 3), 6.0, 2.5)
+    plan = cgtp.Plan(ix, iy, io)
+    x, Y, w, g = small_inputs(L, case, 3, "f32", 2)
+    sc = 0.21
+    out = plan.conv_forward(case.graph, x, Y, w, sc)
+    dx, dY, dw = plan.conv_backward(case.graph, x, Y, w, sc, g)
+    torch.cuda.synchronize()
+    hx, hY, hw, hg = host(x), host(Y), host(w), host(g)
+    assert_close(host(out), oconv.forward(L, case.h_row, case.h_src, hx, hY, hw, sc), out_blocks(L), "f32", "fwd")
+    rdx, rdY, rdw = oconv.backward(L, case.h_row, case.h_src, hx, hY, hw, sc, hg)
+    assert_close(host(dx), rdx, x_blocks(L), "f32", "grad_x")
+    assert_close(host(dY), rdY, y_blocks(L), "f32", "grad_sh")
+    assert_close(host(dw), rdw, w_blocks(L), "f32", "grad_w")
+
+
+def test_misaligned_tensors_take_general_kernels():
+    ix, iy, io = "8x0e+8x1o+8x2e", "0e+1o+2e", "0e+0o+1e+1o+2e+2o"
+    L = Layout(ix, iy, io)
+    case = Case(synth.uniform_box(50, 6.0, 4), 6.0, 2.5)
+    plan = cgtp.Plan(ix, iy, io)
+    x, Y, w, g = small_inputs(L, case, 4, "f32", 2)
+    wb = torch.empty(case.E * L.w_numel + 1, device="cuda")
+    wv = wb[1:].view(case.E, L.w_numel)  # 4-byte offset
+    wv.copy_(w)
+    out = plan.conv_forward(case.graph, x, Y, wv, 1.0)
+    dx, dY, dw = plan.conv_backward(case.graph, x, Y, wv, 1.0, g)
+    torch.cuda.synchronize()
+    hx, hY, hw, hg = host(x), host(Y), host(w), host(g)
+    assert_close(host(out), oconv.forward(L, case.h_row, case.h_src, hx, hY, hw, 1.0), out_blocks(L), "f32", "fwd")
+    rdx, rdY, rdw = oconv.backward(L, case.h_row, case.h_src, hx, hY, hw, 1.0, hg)
+    assert_close(host(dx), rdx, x_blocks(L), "f32", "grad_x")
+    assert_close(host(dw), rdw, w_blocks(L), "f32", "grad_w")
+
+
+def test_conv_error_paths():
+    ix, iy, io = "4x0e+4x1o", "0e+1o", "0e+1o+1e"
+    L = Layout(ix, iy, io)
+    case = Case(synth.uniform_box(30, 5.0, 5), 5.0, 2.0)
+    shared = cgtp.Plan(ix, iy, io, wkind="shared")
+    x = torch.zeros((case.N, L.dim_x), device="cuda")
+    Y = torch.zeros((case.E, L.dim_y), device="cuda")
+    w = torch.zeros((case.E, L.w_numel), device="cuda")
+    with pytest.raises(cgtp.CgtpError) as e:
+        shared.conv_forward(case.graph, x, Y, w, 1.0)
+    assert e.value.status == 3
+    plan = cgtp.Plan(ix, iy, io)
+    small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(cgtp.CgtpError) as e:
+        plan.conv_backward(case.graph, x, Y, w, 1.0, torch.zeros((case.N, L.dim_out), device="cuda"), ws=small_ws)
+    assert e.value.status == 5
+    # the workspace size is the per-edge grad_x partials in the accumulation type
+    assert plan.workspace_size(cgtp.OP_CONV_BACKWARD, graph=case.graph) == case.E * L.dim_x * 4
