@@ -13,8 +13,10 @@ of x, y and w), with every input already resident in HBM. `value` is rows
 Besides the headline line's `roofline` (dominant kernel, algorithmic bytes per
 launch over its mean HIP-event duration against 8 TB/s) and `cpu_baseline`
 (the fp64 oracle on a bounded sample, on the host cores), `extra` carries the
-per-kernel figures and, unless --no-conv, the fused convolution on the
-100,000-point uniform cloud (forward and backward, fp32).
+per-kernel figures and, unless --no-conv, the fused convolution (forward and
+backward, fp32) on the 1000- and 8000-molecule water boxes (the latter with the
+harmonics forward/backward of the force chain) and the 100,000-point uniform
+cloud.
 """
 
 import argparse
@@ -206,8 +208,14 @@ def tp_large_bf16(args, torch, cgtp, synth):
                 bwd_algorithmic_GBs=round(by_b * B / b / 1e6, 1), bytes_per_row_fwd=by_f, bytes_per_row_bwd=by_b)
 
 
-def conv_bench(args, torch, cgtp, synth, name, steps):
-    """Fused convolution forward + backward on one synthetic workload (extra figures)."""
+def conv_bench(args, torch, cgtp, synth, name, steps, forces=False):
+    """Fused convolution forward + backward on one synthetic workload (extra figures).
+
+    With ``forces`` the edge harmonics are recomputed from the edge vectors in the
+    forward and the harmonics backward (grad_sh -> grad wrt edge vectors) follows
+    the convolution backward; both are timed and reported on their own. The
+    radial network's part of the force chain belongs to the caller and is not
+    timed."""
     import numpy as np
     c = synth.CONFIGS[name]
     dev = torch.device("cuda:0")
@@ -234,14 +242,19 @@ def conv_bench(args, torch, cgtp, synth, name, steps):
     out = torch.empty((N, plan.dim_out), device=dev)
     dx, dY, dw = torch.empty_like(x), torch.empty_like(Y), torch.empty_like(w)
     ws = torch.empty(plan.workspace_size(cgtp.OP_CONV_BACKWARD, graph=graph), dtype=torch.uint8, device=dev)
-    tf, tb = KernelTimer(torch), KernelTimer(torch)
+    gvec = torch.empty_like(vec_d)
+    tf, tb, tsf, tsb = KernelTimer(torch), KernelTimer(torch), KernelTimer(torch), KernelTimer(torch)
     for k in range(steps + 1):
         if k == 0:
             plan.conv_forward(graph, x, Y, w, scale, out=out)
             plan.conv_backward(graph, x, Y, w, scale, gout, out=(dx, dY, dw), ws=ws)
         else:
+            if forces:
+                tsf(lambda: cgtp.sh_forward(c["L"], vec_d, out=Y))
             tf(lambda: plan.conv_forward(graph, x, Y, w, scale, out=out))
             tb(lambda: plan.conv_backward(graph, x, Y, w, scale, gout, out=(dx, dY, dw), ws=ws))
+            if forces:
+                tsb(lambda: cgtp.sh_backward(c["L"], vec_d, dY, out=gvec))
     torch.cuda.synchronize()
     bf = 4 * (plan.w_numel + plan.dim_y + 1) * E + 4 * (plan.dim_out + plan.dim_x + 1) * N
     bb = 4 * (2 * plan.w_numel + 2 * plan.dim_y + 1) * E + 4 * (plan.dim_out + 2 * plan.dim_x + 1) * N
@@ -259,7 +272,10 @@ def conv_bench(args, torch, cgtp, synth, name, steps):
                bwd_ms=round(msb, 3), fwd_bwd_edges_per_s=E / ((msf + msb) * 1e-3),
                bwd_algorithmic_GBs=round(bb / (msb * 1e-3) / 1e9, 1),
                fwd_bytes_per_edge=bf / E, bwd_bytes_per_edge=bb / E)
-    del w, dw, ws, x, gout, out, dx, dY, Y, graph
+    if forces:
+        res.update(sh_fwd_ms=round(tsf.mean_ms(), 4), sh_bwd_ms=round(tsb.mean_ms(), 4),
+                   fwd_bwd_forces_edges_per_s=E / ((msf + msb + tsf.mean_ms() + tsb.mean_ms()) * 1e-3))
+    del w, dw, ws, x, gout, out, dx, dY, Y, graph, gvec
     torch.cuda.empty_cache()
     return res
 
@@ -309,8 +325,9 @@ def main():
     value, ms_step, roofline, plan = tp_large_bench(args, torch, cgtp, synth, extra)
     extra["tp_large_bf16"] = tp_large_bf16(args, torch, cgtp, synth)
     if not args.no_conv:
-        for name in ("conv_water1k", "conv_uniform100k"):
-            extra[name] = conv_bench(args, torch, cgtp, synth, name, max(2, min(args.steps, 5)))
+        for name in ("conv_water1k", "conv_water8k", "conv_uniform100k"):
+            extra[name] = conv_bench(args, torch, cgtp, synth, name, max(2, min(args.steps, 5)),
+                                     forces=name == "conv_water8k")
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, synth)
     line = {
         "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,

@@ -74,6 +74,18 @@ constexpr int pattern_coefs(int l1, int l2, int l3) {
   return n;
 }
 
+// Largest coefficient count of one pattern with every degree <= lmax.
+constexpr int max_pattern_coefs(int lmax) {
+  int m = 0;
+  for (int l1 = 0; l1 <= lmax; ++l1)
+    for (int l2 = 0; l2 <= lmax; ++l2)
+      for (int l3 = iabs_c(l1 - l2); l3 <= l1 + l2 && l3 <= lmax; ++l3) {
+        const int n = pattern_coefs(l1, l2, l3);
+        m = n > m ? n : m;
+      }
+  return m;
+}
+
 template <int L1, int L2, int L3>
 struct Pattern {
   static constexpr int NP = pattern_pairs(L1, L2, L3);

@@ -156,6 +156,14 @@ constexpr int conv_budget() {
 // One wave = (receiver n, one slot chunk of x block b, one channel chunk).
 // Lanes form G = 64 / LG groups of LG lanes; group g takes edges e0+g,
 // e0+g+G, ... and lane k of a group owns channels c .. c+VEC-1.
+//
+// The edge loop body has no branches on the plan: a slot the plan does not
+// have still runs, from valid addresses (weights at offset 0 of the edge's row,
+// coefficients from the zero-padded start of the table, harmonics of a missing
+// degree from the table as well) into accumulators that are never stored. So
+// all loads of an edge are independent once its source index is known, and
+// the source indices of up to 64 edges are fetched with one load and handed
+// out with lane shuffles.
 template <typename T, typename A, int VEC, int L1, int L, int CH>
 __device__ __forceinline__ void fwd_fused_chunk(const ConvArgs& a, int64_t n, const BlockDev& blk,
                                                 int c, bool valid, int g, int G) {
@@ -179,15 +187,21 @@ __device__ __forceinline__ void fwd_fused_chunk(const ConvArgs& a, int64_t n, co
   }
   const A* __restrict__ cf = static_cast<const A*>(a.coef);
   const T* __restrict__ X = static_cast<const T*>(a.x);
+  const int lane = int(threadIdx.x & 63);
   const int32_t e0 = a.row_ptr[n], e1 = a.row_ptr[n + 1];
-  if (valid) {
-    for (int32_t e = e0 + g; e < e1; e += G) {
-      const int64_t j = a.src[e];
+  for (int32_t base = e0; base < e1; base += 64) {
+    const int nb = e1 - base < 64 ? e1 - base : 64;  // uniform over the wave
+    const int32_t srcv = lane < nb ? a.src[base + lane] : 0;
+    for (int k0 = 0; k0 < nb; k0 += G) {
+      const int k = k0 + g;
+      const int64_t j = __shfl(srcv, k < nb ? k : 0, 64);
+      if (!valid || k >= nb) continue;
+      const int64_t e = base + k;
       A xb[2 * L1 + 1][VEC];
 #pragma unroll
       for (int m = 0; m < 2 * L1 + 1; ++m) VecIO<T, VEC>::load(X + j * a.dim_x + blk.x_off + m * blk.mul + c, xb[m]);
-      const T* __restrict__ Ye = static_cast<const T*>(a.sh) + int64_t(e) * a.dim_y;
-      const T* __restrict__ we = static_cast<const T*>(a.w) + int64_t(e) * a.W;
+      const T* __restrict__ Ye = static_cast<const T*>(a.sh) + e * a.dim_y;
+      const T* __restrict__ we = static_cast<const T*>(a.w) + e * a.W;
       A ycur[2 * L + 1];
       static_for<s0, s1>([&](auto I) {
         constexpr int i = decltype(I)::value;
@@ -195,25 +209,22 @@ __device__ __forceinline__ void fwd_fused_chunk(const ConvArgs& a, int64_t n, co
         constexpr bool first_of_l2 = (i == s0) || (S::arr.p[i > 0 ? i - 1 : 0].l2 != st.l2);
         if constexpr (first_of_l2) {
           const int yo = a.yoff[st.l2];
-          if (yo >= 0) {
+          const T* __restrict__ yp = yo >= 0 ? Ye + yo : static_cast<const T*>(a.coef);
 #pragma unroll
-            for (int m = 0; m < 2 * st.l2 + 1; ++m) ycur[m] = to_acc<A>(Ye[yo + m]);
-          }
+          for (int m = 0; m < 2 * st.l2 + 1; ++m) ycur[m] = to_acc<A>(yp[m]);
         }
-        if (pid[i - s0] >= 0) {
-          A wv[VEC];
-          VecIO<T, VEC>::load(we + woff[i - s0] + c, wv);
-          A yb[2 * st.l2 + 1];
+        A wv[VEC];
+        VecIO<T, VEC>::load(we + woff[i - s0] + c, wv);
+        A yb[2 * st.l2 + 1];
 #pragma unroll
-          for (int m = 0; m < 2 * st.l2 + 1; ++m) yb[m] = ycur[m];
-          A t[2 * st.l3 + 1][VEC];
-          fwd_core<L1, st.l2, st.l3, VEC, A>(xb, yb, cf + coff[i - s0], t);
+        for (int m = 0; m < 2 * st.l2 + 1; ++m) yb[m] = ycur[m];
+        A t[2 * st.l3 + 1][VEC];
+        fwd_core<L1, st.l2, st.l3, VEC, A>(xb, yb, cf + coff[i - s0], t);
 #pragma unroll
-          for (int m = 0; m < 2 * st.l3 + 1; ++m)
+        for (int m = 0; m < 2 * st.l3 + 1; ++m)
 #pragma unroll
-            for (int v = 0; v < VEC; ++v)
-              acc[st.acc - acc0 + m][v] = fma(wv[v], t[m][v], acc[st.acc - acc0 + m][v]);
-        }
+          for (int v = 0; v < VEC; ++v)
+            acc[st.acc - acc0 + m][v] = fma(wv[v], t[m][v], acc[st.acc - acc0 + m][v]);
       });
     }
   }
@@ -357,9 +368,10 @@ __global__ __launch_bounds__(kBlock) void conv_bwd_fused_kernel(ConvArgs a, Conv
   constexpr int NS = S::NS;
   constexpr int NY = (L + 1) * (L + 1);
   extern __shared__ unsigned char smem_raw[];
-  A* gl = reinterpret_cast<A*>(smem_raw);
   const int LG = 1 << a.lg_log2;
   const int CW = LG * VEC;  // channels per chunk
+  A* gl = reinterpret_cast<A*>(smem_raw);  // [S::NACC][CW]
+  A* dsl = gl + S::NACC * CW;              // [64][dim_y]
   const int64_t n = blockIdx.x / a.nchunks;
   const int cc = int(blockIdx.x - n * a.nchunks);
   const BlockDev blk = ldc(a.blocks + a.block);
@@ -394,115 +406,140 @@ __global__ __launch_bounds__(kBlock) void conv_bwd_fused_kernel(ConvArgs a, Conv
   const A* __restrict__ cf = static_cast<const A*>(a.coef);
   const T* __restrict__ X = static_cast<const T*>(a.x);
   const int32_t e0 = a.row_ptr[n], e1 = a.row_ptr[n + 1];
-  // every lane of a group runs the same trip count (shuffles below)
-  for (int32_t e = e0 + gi; e < e1; e += NG) {
-    const int64_t j = a.src[e];
-    A xb[2 * L1 + 1][VEC], dxe[2 * L1 + 1][VEC];
-#pragma unroll
-    for (int m = 0; m < 2 * L1 + 1; ++m) {
-      if (valid) VecIO<T, VEC>::load(X + j * a.dim_x + blk.x_off + m * U + c, xb[m]);
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        if (!valid) xb[m][v] = A(0);
-        dxe[m][v] = A(0);
-      }
+  const int lane = int(threadIdx.x & 63);
+  const int cl = valid ? c : 0;  // lanes past the channels load channel 0 and use zeros
+  // Source indices of up to 64 edges come with one load and are handed out by
+  // lane shuffles. The trip counts are uniform over the workgroup and a
+  // group's lanes share their edge (grad_sh is reduced within the group).
+  // Loads of an edge do not wait on the plan's branches: x and sh at the top,
+  // the weights of slot i+1 issued before slot i is computed.
+  for (int32_t base = e0; base < e1; base += 64) {
+    const int nb = e1 - base < 64 ? e1 - base : 64;
+    const int32_t srcv = lane < nb ? a.src[base + lane] : 0;
+    // grad_sh of the batch's edges: [nb][dim_y] in LDS, starting from what the
+    // previous x block's launch wrote (stream order) or from zero
+    if (bw.dsh) {
+      const T* __restrict__ dsb = static_cast<const T*>(bw.dsh) + int64_t(base) * a.dim_y;
+      for (int t = threadIdx.x; t < nb * a.dim_y; t += kBlock) dsl[t] = bw.dy_accum ? to_acc<A>(dsb[t]) : A(0);
     }
-    const T* __restrict__ Ye = static_cast<const T*>(a.sh) + int64_t(e) * a.dim_y;
-    T* __restrict__ dwe = static_cast<T*>(bw.dw) + int64_t(e) * a.W;
-    const T* __restrict__ we = static_cast<const T*>(a.w) + int64_t(e) * a.W;
-    A dyl[NY];
+    __syncthreads();
+    for (int k0 = 0; k0 < nb; k0 += NG) {
+      const int kk = k0 + gi;
+      const int64_t j = __shfl(srcv, kk < nb ? kk : 0, 64);
+      if (kk >= nb) continue;
+      const int64_t e = base + kk;
+      A xb[2 * L1 + 1][VEC], dxe[2 * L1 + 1][VEC];
 #pragma unroll
-    for (int k = 0; k < NY; ++k) dyl[k] = A(0);
-    A ycur[2 * L + 1];
-    static_for<0, NS>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      constexpr SlotT st = S::arr.p[i];
-      constexpr int L2 = st.l2, L3 = st.l3;
-      constexpr bool first_of_l2 = (i == 0) || (S::arr.p[i > 0 ? i - 1 : 0].l2 != L2);
-      if constexpr (first_of_l2) {
+      for (int m = 0; m < 2 * L1 + 1; ++m) {
+        VecIO<T, VEC>::load(X + j * a.dim_x + blk.x_off + m * U + cl, xb[m]);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          xb[m][v] = valid ? xb[m][v] : A(0);
+          dxe[m][v] = A(0);
+        }
+      }
+      const T* __restrict__ Ye = static_cast<const T*>(a.sh) + e * a.dim_y;
+      T* __restrict__ dwe = static_cast<T*>(bw.dw) + e * a.W;
+      const T* __restrict__ we = static_cast<const T*>(a.w) + e * a.W;
+      A dyl[NY];
+#pragma unroll
+      for (int k = 0; k < NY; ++k) dyl[k] = A(0);
+      A ycur[2 * L + 1];
+      A wnx[VEC];
+      VecIO<T, VEC>::load(we + woff[0] + cl, wnx);
+      static_for<0, NS>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        constexpr SlotT st = S::arr.p[i];
+        constexpr int L2 = st.l2, L3 = st.l3;
+        constexpr bool first_of_l2 = (i == 0) || (S::arr.p[i > 0 ? i - 1 : 0].l2 != L2);
+        if constexpr (first_of_l2) {
+          const int yo = a.yoff[L2];
+          const T* __restrict__ yp = yo >= 0 ? Ye + yo : static_cast<const T*>(a.coef);
+#pragma unroll
+          for (int m = 0; m < 2 * L2 + 1; ++m) ycur[m] = to_acc<A>(yp[m]);
+        }
+        A wv[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) wv[v] = valid ? wnx[v] : A(0);
+        if constexpr (i + 1 < NS) VecIO<T, VEC>::load(we + woff[i + 1] + cl, wnx);
+        if (pid[i] >= 0) {
+          using P = Pattern<L1, L2, L3>;
+          const A* __restrict__ cp = cf + coff[i];
+          A gb[2 * L3 + 1][VEC];
+#pragma unroll
+          for (int m = 0; m < 2 * L3 + 1; ++m)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) gb[m][v] = gl[(st.acc + m) * CW + li * VEC + v];
+          // pairs are m1-major: q[m1] = sum_m3 A[m1,m3] g[m3] is folded into
+          // grad_w and the grad_x partial after the last pair of its m1
+          A d[VEC], q[VEC], xw[VEC];
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) d[v] = A(0);
+          static_for<0, P::NP>([&](auto K) {
+            constexpr int kp = decltype(K)::value;
+            constexpr PairT pr = P::arr.p[kp];
+            constexpr bool first = kp == 0 || P::arr.p[kp > 0 ? kp - 1 : 0].m1 != pr.m1;
+            constexpr bool last = kp == P::NP - 1 || P::arr.p[kp + 1 < P::NP ? kp + 1 : kp].m1 != pr.m1;
+            if constexpr (first) {
+#pragma unroll
+              for (int v = 0; v < VEC; ++v) {
+                xw[v] = xb[pr.m1 + L1][v] * wv[v];
+                q[v] = A(0);
+              }
+            }
+            const A ca = ldc(cp + pr.coef);
+            A av = ca * ycur[pr.m2a + L2];
+            A cb = A(0);
+            if constexpr (pr.n == 2) {
+              cb = ldc(cp + pr.coef + 1);
+              av = fma(cb, ycur[pr.m2b + L2], av);
+            }
+            A sdot = A(0);
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+              q[v] = fma(av, gb[pr.m3 + L3][v], q[v]);
+              sdot = fma(xw[v], gb[pr.m3 + L3][v], sdot);
+            }
+            dyl[L2 * L2 + L2 + pr.m2a] = fma(ca, sdot, dyl[L2 * L2 + L2 + pr.m2a]);
+            if constexpr (pr.n == 2) dyl[L2 * L2 + L2 + pr.m2b] = fma(cb, sdot, dyl[L2 * L2 + L2 + pr.m2b]);
+            if constexpr (last) {
+#pragma unroll
+              for (int v = 0; v < VEC; ++v) {
+                d[v] = fma(xb[pr.m1 + L1][v], q[v], d[v]);
+                dxe[pr.m1 + L1][v] = fma(wv[v], q[v], dxe[pr.m1 + L1][v]);
+              }
+            }
+          });
+          if (valid && bw.dw) VecIO<T, VEC>::store(dwe + woff[i] + c, d);
+        }
+      });
+      if (valid && bw.dxp) {
+        A* __restrict__ dxr = static_cast<A*>(bw.dxp) + e * a.dim_x + blk.x_off;
+#pragma unroll
+        for (int m = 0; m < 2 * L1 + 1; ++m) VecIO<A, VEC>::store(dxr + m * U + c, dxe[m]);
+      }
+      // grad_sh: sum over the group's channels into the batch tile
+      if (!bw.dsh) continue;
+      static_for<0, L + 1>([&](auto L2c) {
+        constexpr int L2 = decltype(L2c)::value;
         const int yo = a.yoff[L2];
         if (yo >= 0) {
 #pragma unroll
-          for (int m = 0; m < 2 * L2 + 1; ++m) ycur[m] = to_acc<A>(Ye[yo + m]);
+          for (int m = 0; m < 2 * L2 + 1; ++m) {
+            A v = dyl[L2 * L2 + m];
+            for (int off = 1; off < LG; off <<= 1) v += __shfl_xor(v, off, 64);
+            if (li == 0) dsl[kk * a.dim_y + yo + m] += v;
+          }
         }
-      }
-      if (pid[i] >= 0) {
-        using P = Pattern<L1, L2, L3>;
-        const A* __restrict__ cp = cf + coff[i];
-        A gb[2 * L3 + 1][VEC];
-#pragma unroll
-        for (int m = 0; m < 2 * L3 + 1; ++m)
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) gb[m][v] = gl[(st.acc + m) * CW + li * VEC + v];
-        A wv[VEC];
-        if (valid) {
-          VecIO<T, VEC>::load(we + woff[i] + c, wv);
-        } else {
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) wv[v] = A(0);
-        }
-        A xw[2 * L1 + 1][VEC], q[2 * L1 + 1][VEC];
-#pragma unroll
-        for (int m = 0; m < 2 * L1 + 1; ++m)
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) {
-            xw[m][v] = xb[m][v] * wv[v];
-            q[m][v] = A(0);
-          }
-        static_for<0, P::NP>([&](auto K) {
-          constexpr PairT pr = P::arr.p[decltype(K)::value];
-          const A ca = ldc(cp + pr.coef);
-          A av = ca * ycur[pr.m2a + L2];
-          A cb = A(0);
-          if constexpr (pr.n == 2) {
-            cb = ldc(cp + pr.coef + 1);
-            av = fma(cb, ycur[pr.m2b + L2], av);
-          }
-          A sdot = A(0);
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) {
-            q[pr.m1 + L1][v] = fma(av, gb[pr.m3 + L3][v], q[pr.m1 + L1][v]);
-            sdot = fma(xw[pr.m1 + L1][v], gb[pr.m3 + L3][v], sdot);
-          }
-          dyl[L2 * L2 + L2 + pr.m2a] = fma(ca, sdot, dyl[L2 * L2 + L2 + pr.m2a]);
-          if constexpr (pr.n == 2) dyl[L2 * L2 + L2 + pr.m2b] = fma(cb, sdot, dyl[L2 * L2 + L2 + pr.m2b]);
-        });
-        A d[VEC];
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) d[v] = A(0);
-#pragma unroll
-        for (int m = 0; m < 2 * L1 + 1; ++m)
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) {
-            d[v] = fma(xb[m][v], q[m][v], d[v]);
-            dxe[m][v] = fma(wv[v], q[m][v], dxe[m][v]);
-          }
-        if (valid && bw.dw) VecIO<T, VEC>::store(dwe + woff[i] + c, d);
-      }
-    });
-    if (valid && bw.dxp) {
-      A* __restrict__ dxr = static_cast<A*>(bw.dxp) + int64_t(e) * a.dim_x + blk.x_off;
-#pragma unroll
-      for (int m = 0; m < 2 * L1 + 1; ++m) VecIO<A, VEC>::store(dxr + m * U + c, dxe[m]);
+      });
     }
-    // grad_sh: sum over the group's channels; lane 0 of the group writes
-    if (!bw.dsh) continue;
-    T* __restrict__ dye = static_cast<T*>(bw.dsh) + int64_t(e) * a.dim_y;
-    static_for<0, L + 1>([&](auto L2c) {
-      constexpr int L2 = decltype(L2c)::value;
-      const int yo = a.yoff[L2];
-      if (yo >= 0) {
-#pragma unroll
-        for (int m = 0; m < 2 * L2 + 1; ++m) {
-          A v = dyl[L2 * L2 + m];
-          for (int off = 1; off < LG; off <<= 1) v += __shfl_xor(v, off, 64);
-          if (li == 0) {
-            if (bw.dy_accum) v += to_acc<A>(dye[yo + m]);
-            from_acc(dye[yo + m], v);
-          }
-        }
-      }
-    });
+    // the batch's grad_sh rows leave in one coalesced pass
+    __syncthreads();
+    if (bw.dsh) {
+      T* __restrict__ dsb = static_cast<T*>(bw.dsh) + int64_t(base) * a.dim_y;
+      for (int t = threadIdx.x; t < nb * a.dim_y; t += kBlock) from_acc(dsb[t], dsl[t]);
+    }
+    __syncthreads();  // the tile is refilled by the next batch
   }
 }
 

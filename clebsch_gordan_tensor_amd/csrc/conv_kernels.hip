@@ -115,7 +115,9 @@ bool conv_backward_fused(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x
       case CGTP_F64: lds = conv_bwd_fused_lds<double>(blk.l1, plan->conv_L, (1 << lg) * VEC); break;
       case CGTP_BF16: lds = conv_bwd_fused_lds<bf16>(blk.l1, plan->conv_L, (1 << lg) * VEC); break;
     }
-    if (lds == 0 || lds > 64 * 1024) return false;
+    if (lds == 0) return false;
+    lds += size_t(64) * size_t(plan->dim_y) * acc_size(plan->dtype);  // grad_sh tile of 64 edges
+    if (lds > 64 * 1024) return false;
     lgs.push_back(lg);
     ldss.push_back(lds);
   }

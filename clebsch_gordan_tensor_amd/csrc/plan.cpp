@@ -353,15 +353,22 @@ const DevTables& plan_tables(cgtp_plan_s* plan) {
     bd.push_back(BlockDev{b.l1, b.mul, b.x_off, b.path_begin, b.path_end, 0, 0, 0});
   DevTables t;
   const bool f64 = plan->dtype == CGTP_F64;
-  const size_t cbytes = f64 ? plan->coef64.size() * 8 : plan->coef32.size() * 4;
+  // The device table is zero-padded to at least one whole pattern of the
+  // largest degrees, so a kernel may run a pattern from offset 0 for a slot
+  // the plan does not have (its results are discarded).
+  const size_t ncoef = std::max<size_t>(plan->coef64.size(), size_t(max_pattern_coefs(kLmax)));
+  std::vector<double> c64(plan->coef64);
+  std::vector<float> c32(plan->coef32);
+  c64.resize(ncoef, 0.0);
+  c32.resize(ncoef, 0.0f);
+  const size_t cbytes = f64 ? ncoef * 8 : ncoef * 4;
   try {
     CGTP_CHECK_HIP(hipMalloc(&t.paths, pd.size() * sizeof(PathDev)));
     CGTP_CHECK_HIP(hipMalloc(&t.blocks, bd.size() * sizeof(BlockDev)));
-    CGTP_CHECK_HIP(hipMalloc(&t.coef, std::max<size_t>(cbytes, 16)));
+    CGTP_CHECK_HIP(hipMalloc(&t.coef, cbytes));
     CGTP_CHECK_HIP(hipMemcpy(t.paths, pd.data(), pd.size() * sizeof(PathDev), hipMemcpyHostToDevice));
     CGTP_CHECK_HIP(hipMemcpy(t.blocks, bd.data(), bd.size() * sizeof(BlockDev), hipMemcpyHostToDevice));
-    CGTP_CHECK_HIP(hipMemcpy(t.coef, f64 ? static_cast<const void*>(plan->coef64.data())
-                                         : static_cast<const void*>(plan->coef32.data()),
+    CGTP_CHECK_HIP(hipMemcpy(t.coef, f64 ? static_cast<const void*>(c64.data()) : static_cast<const void*>(c32.data()),
                              cbytes, hipMemcpyHostToDevice));
     if (plan->conv_fused) {
       CGTP_CHECK_HIP(hipMalloc(&t.slot_paths, plan->slot_paths.size() * 4 + 4));

@@ -191,17 +191,25 @@ struct TPBwd {
     }
     A wv[VEC];
     VecIO<T, VEC>::load(wr + pd.w_off + c, wv);
-    A xw[2 * L1 + 1][VEC], q[2 * L1 + 1][VEC];
+    // Pairs come m1-major, so q[m1] = sum_m3 A[m1,m3] g[m3] (A = C y) is
+    // complete after the last pair of its m1: it is folded into dw and dx
+    // there, and only one m1's q and x*w are live at a time.
+    //   dy[m2] += C sum_u w x[m1] g[m3];  dw = sum_m1 x[m1] q[m1];  dx[m1] += w q[m1]
+    A d[VEC], q[VEC], xw[VEC];
 #pragma unroll
-    for (int m = 0; m < 2 * L1 + 1; ++m)
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        xw[m][v] = xb[m][v] * wv[v];
-        q[m][v] = A(0);
-      }
-    // q[m1] = sum_m3 A[m1,m3] g[m3]   (A = C y);  dy[m2] += C sum_u w x[m1] g[m3]
+    for (int v = 0; v < VEC; ++v) d[v] = A(0);
     static_for<0, P::NP>([&](auto I) {
-      constexpr PairT pr = P::arr.p[decltype(I)::value];
+      constexpr int i = decltype(I)::value;
+      constexpr PairT pr = P::arr.p[i];
+      constexpr bool first = i == 0 || P::arr.p[i > 0 ? i - 1 : 0].m1 != pr.m1;
+      constexpr bool last = i == P::NP - 1 || P::arr.p[i + 1 < P::NP ? i + 1 : i].m1 != pr.m1;
+      if constexpr (first) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          xw[v] = xb[pr.m1 + L1][v] * wv[v];
+          q[v] = A(0);
+        }
+      }
       const A ca = ldc(cf + pr.coef);
       A av = ca * yb[pr.m2a + L2];
       A cb = A(0);
@@ -212,23 +220,19 @@ struct TPBwd {
       A s = A(0);
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
-        q[pr.m1 + L1][v] = fma(av, gb[pr.m3 + L3][v], q[pr.m1 + L1][v]);
-        s = fma(xw[pr.m1 + L1][v], gb[pr.m3 + L3][v], s);
+        q[v] = fma(av, gb[pr.m3 + L3][v], q[v]);
+        s = fma(xw[v], gb[pr.m3 + L3][v], s);
       }
       dyb[pr.m2a + L2] = fma(ca, s, dyb[pr.m2a + L2]);
       if constexpr (pr.n == 2) dyb[pr.m2b + L2] = fma(cb, s, dyb[pr.m2b + L2]);
-    });
-    // dw = sum_m1 x[m1] q[m1];  dx[m1] += w q[m1]
-    A d[VEC];
+      if constexpr (last) {
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) d[v] = A(0);
-#pragma unroll
-    for (int m = 0; m < 2 * L1 + 1; ++m)
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        d[v] = fma(xb[m][v], q[m][v], d[v]);
-        dxb[m][v] = fma(wv[v], q[m][v], dxb[m][v]);
+        for (int v = 0; v < VEC; ++v) {
+          d[v] = fma(xb[pr.m1 + L1][v], q[v], d[v]);
+          dxb[pr.m1 + L1][v] = fma(wv[v], q[v], dxb[pr.m1 + L1][v]);
+        }
       }
+    });
     if (dwr) VecIO<T, VEC>::store(dwr + pd.w_off + c, d);
     if (dwa) VecIO<A, VEC>::store(dwa + pd.w_off + c, d);
   }

@@ -23,6 +23,9 @@ CGTP_TP_EXTERN_BWD(double, 2)
 #ifndef CGTP_TP_BWD_VEC
 #define CGTP_TP_BWD_VEC 4
 #endif
+#ifndef CGTP_TP_BWD_VEC_BF16
+#define CGTP_TP_BWD_VEC_BF16 4
+#endif
 
 // ----------------------------------------------------------------- launchers
 
@@ -110,7 +113,8 @@ void tp_backward_rows(cgtp_plan_s* plan, const TPBackwardRows& r, hipStream_t st
   const DevTables& t = plan_tables(plan);
   const size_t es = dtype_size(plan->dtype), as = acc_size(plan->dtype);
   int vec = plan->vec;
-  if (plan->dtype != CGTP_F64 && vec > CGTP_TP_BWD_VEC) vec = CGTP_TP_BWD_VEC;
+  const int max_vec = plan->dtype == CGTP_BF16 ? CGTP_TP_BWD_VEC_BF16 : CGTP_TP_BWD_VEC;
+  if (plan->dtype != CGTP_F64 && vec > max_vec) vec = max_vec;
   if (!aligned(r.x, vec * es) || !aligned(r.w, vec * es) || !aligned(r.g, vec * es) ||
       !aligned(r.dx, vec * es) || !aligned(r.dw, vec * es) || !aligned(r.dx_ws, vec * as) ||
       !aligned(r.dw_ws, vec * as))

@@ -14,6 +14,7 @@ and ``src`` are the CSR arrays of ``graph.csr_from_coo``.
 
 import numpy as np
 
+from . import sh as _sh
 from . import tp
 from .graph import dst_of_csr
 
@@ -57,3 +58,23 @@ def avg_neighbors_scale(N, E):
     """1 / sqrt(E / N): the sqrt(num_neighbors) normalisation of [V2106] with the
     average degree of the built graph."""
     return 1.0 / np.sqrt(E / N) if E > 0 else 1.0
+
+
+def edge_vector_grad(lmax, vec, grad_sh, grad_r):
+    """Gradient with respect to the edge vectors (the force chain).
+
+    [V2106] "Fixed-topology compilation": position gradients pass through the
+    edge vectors, their lengths, the radial basis and the harmonics, with the
+    edge set held fixed. The harmonics see only the direction of vec and the
+    radial network only its length r = |vec|, so for cotangents grad_sh of
+    Y = real_sh(vec) and grad_r of r:
+
+      d/dvec = real_sh_grad(vec, grad_sh) + grad_r * vec / |vec|
+
+    grad_r is the radial network's vector-Jacobian product of the weight
+    cotangent (computed by the caller's radial network).
+    """
+    vec = np.asarray(vec, np.float64)
+    r = np.linalg.norm(vec, axis=1)
+    rs = np.where(r == 0.0, 1.0, r)
+    return _sh.real_sh_grad(lmax, vec, grad_sh) + (np.asarray(grad_r, np.float64) / rs)[:, None] * vec

@@ -5,7 +5,9 @@ of 1000 molecules, water box of 8000, 100,000 uniform points) run at full size
 in the benchmark's launch configuration and are checked on sampled receivers
 (forward, grad_sh, grad_w) and sampled senders (grad_x) against the oracle.
 Also: empty edge lists, isolated nodes, the general (non-fused) kernel, bitwise
-determinism and rotation equivariance of the GPU output.
+determinism and rotation equivariance of the GPU output, and the force chain
+(gradient with respect to the edge vectors: the library's harmonics backward of
+grad_sh plus the radial network's chain of grad_w, which the caller owns).
 """
 
 import math
@@ -296,3 +298,90 @@ def test_conv_error_paths():
     assert e.value.status == 5
     # the workspace size is the per-edge grad_x partials in the accumulation type
     assert plan.workspace_size(cgtp.OP_CONV_BACKWARD, graph=case.graph) == case.E * L.dim_x * 4
+
+
+def radial_chain(vec_d, r_cut, W1, W2, dw, chunk=1 << 18):
+    """Caller-side radial network: d/dvec of sum(dw * w(|vec|)) by torch autograd."""
+    out = torch.empty_like(vec_d)
+    for a in range(0, vec_d.shape[0], chunk):
+        v = vec_d[a:a + chunk].detach().requires_grad_(True)
+        wv = synth.radial_weights_torch(v.norm(dim=1), r_cut, W1, W2)
+        (gv,) = torch.autograd.grad(wv, v, dw[a:a + chunk])
+        out[a:a + chunk] = gv
+    return out
+
+
+def force_chain_case(name, small=None, seed=0):
+    """Harmonics from the edge vectors by the library, weights by the radial network,
+    convolution forward and backward, then the edge-vector gradient."""
+    if small is None:
+        c = synth.CONFIGS[name]
+        ix, iy, io, lmax, rc = c["irreps_x"], c["irreps_y"], c["irreps_out"], c["L"], c["r_cut"]
+        case = Case(synth.positions_for(c, seed), c["box"], rc)
+        hidden = 64
+    else:
+        (ix, iy, io, lmax), (n, box, rc) = small
+        case = Case(synth.uniform_box(n, box, seed), box, rc)
+        hidden = 16
+    L = Layout(ix, iy, io)
+    plan = cgtp.Plan(ix, iy, io)
+    vec32 = case.vec.astype(np.float32)
+    vd = torch.from_numpy(vec32).cuda()
+    W1, W2 = synth.mlp_params(8, hidden, L.w_numel, seed)
+    tW1, tW2 = torch.from_numpy(W1).float().cuda(), torch.from_numpy(W2).float().cuda()
+    Y = cgtp.sh_forward(lmax, vd)
+    w = torch.empty((case.E, L.w_numel), device="cuda")
+    with torch.no_grad():
+        for a in range(0, case.E, 1 << 19):
+            w[a:a + (1 << 19)] = synth.radial_weights_torch(vd[a:a + (1 << 19)].norm(dim=1), rc, tW1, tW2)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    x = torch.randn((case.N, L.dim_x), generator=gen, device="cuda")
+    g = torch.randn((case.N, L.dim_out), generator=gen, device="cuda")
+    sc = oconv.avg_neighbors_scale(case.N, case.E)
+    out = plan.conv_forward(case.graph, x, Y, w, sc)
+    dx, dY, dw = plan.conv_backward(case.graph, x, Y, w, sc, g)
+    gvec = cgtp.sh_backward(lmax, vd, dY) + radial_chain(vd, rc, tW1, tW2, dw)
+    torch.cuda.synchronize()
+    return L, case, lmax, rc, W1, W2, sc, vec32, x, w, g, out, dx, gvec
+
+
+def oracle_force_chain(L, lmax, rc, W1, W2, vec, hw, hg_e, src_x):
+    """Oracle side for a set of edges: harmonics from the vectors, TP backward,
+    radial chain in fp64, then the edge-vector gradient."""
+    hv = np.asarray(vec, np.float64)
+    hY = osh.real_sh(lmax, hv)
+    _, rdY, rdw = otp.backward(L, src_x, hY, hw, hg_e)
+    gr = synth.radial_weights_backward_np(np.linalg.norm(hv, axis=1), rc, W1, W2, rdw)
+    return hY, oconv.edge_vector_grad(lmax, hv, rdY, gr)
+
+
+def test_force_chain_small_graph_full():
+    small = (("4x0e+4x1o+4x2e", "0e+1o+2e", "0e+0o+1e+1o+2e+2o", 2), (40, 9.0, 3.2))
+    L, case, lmax, rc, W1, W2, sc, vec32, x, w, g, out, dx, gvec = force_chain_case(None, small, seed=3)
+    assert case.E > 100
+    hx, hw, hg = host(x), host(w), host(g)
+    hY, ref = oracle_force_chain(L, lmax, rc, W1, W2, vec32, hw, sc * hg[case.h_dst], hx[case.h_src])
+    assert_close(host(out), oconv.forward(L, case.h_row, case.h_src, hx, hY, hw, sc), out_blocks(L), "f32",
+                 "forward with library harmonics")
+    rdx, _, _ = oconv.backward(L, case.h_row, case.h_src, hx, hY, hw, sc, hg)
+    assert_close(host(dx), rdx, x_blocks(L), "f32", "grad_x")
+    assert_close(host(gvec), ref, [(0, 3)], "f32", "edge-vector gradient")
+
+
+def test_conv_water8k_forces_full_size():
+    """The 8000-molecule water box with forces, at full size, on sampled receivers' edges."""
+    L, case, lmax, rc, W1, W2, sc, vec32, x, w, g, out, dx, gvec = force_chain_case("conv_water8k")
+    rng = np.random.default_rng(2)
+    nodes = np.sort(rng.choice(case.N, 32, replace=False))
+    eidx = np.concatenate([np.arange(case.h_row[n], case.h_row[n + 1]) for n in nodes])
+    ei = torch.from_numpy(eidx).cuda()
+    hx, hg = host(x), host(g)
+    hY, ref = oracle_force_chain(L, lmax, rc, W1, W2, vec32[eidx], host(w[ei]),
+                                 sc * hg[case.h_dst[eidx]], hx[case.h_src[eidx]])
+    assert_close(host(gvec[ei]), ref, [(0, 3)], "f32", "sampled edge-vector gradient")
+    sub_row = np.concatenate([[0], np.cumsum(case.h_row[nodes + 1] - case.h_row[nodes])])
+    rout = oconv.forward(L, sub_row, case.h_src[eidx], hx, hY, host(w[ei]), sc)
+    assert_close(host(out[torch.from_numpy(nodes).cuda()]), rout, out_blocks(L), "f32", "sampled forward")
+    del w, out, dx, gvec
+    torch.cuda.empty_cache()

@@ -193,3 +193,35 @@ def test_radial_backward_matches_fd():
     h = 1e-6
     fd = ((synth.radial_weights_np(r + h, 5.0, W1, W2) - synth.radial_weights_np(r - h, 5.0, W1, W2)) * dw).sum(1) / (2 * h)
     assert np.abs(an - fd).max() < 1e-7
+
+
+def test_force_chain_matches_fd():
+    """Edge-vector gradient (harmonics + radial network) vs central differences of
+    f(vec) = <g, conv(x, Y(vec), w(|vec|))>."""
+    L = Layout(IX, IY, IO)
+    pos, box, rc, src, dst, vec = small_system(5)
+    N = pos.shape[0]
+    row_ptr, s, perm = graph.csr_from_coo(N, src, dst)
+    vec = vec[perm]
+    x = synth.gaussian((N, L.dim_x), 5, synth.S_X)
+    g = synth.gaussian((N, L.dim_out), 5, synth.S_G)
+    W1, W2 = synth.mlp_params(8, 16, L.w_numel, 5)
+    sc = 0.6
+
+    def f(v):
+        r = np.linalg.norm(v, axis=1)
+        return np.sum(g * conv.forward(L, row_ptr, s, x, sh.real_sh(2, v), synth.radial_weights_np(r, rc, W1, W2), sc))
+
+    r = np.linalg.norm(vec, axis=1)
+    w = synth.radial_weights_np(r, rc, W1, W2)
+    _, dY, dw = conv.backward(L, row_ptr, s, x, sh.real_sh(2, vec), w, sc, g)
+    gv = conv.edge_vector_grad(2, vec, dY, synth.radial_weights_backward_np(r, rc, W1, W2, dw))
+    h = 1e-6
+    rng = np.random.default_rng(2)
+    for _ in range(8):
+        e, k = rng.integers(0, vec.shape[0]), rng.integers(0, 3)
+        vp, vm = vec.copy(), vec.copy()
+        vp[e, k] += h
+        vm[e, k] -= h
+        fd = (f(vp) - f(vm)) / (2 * h)
+        assert gv[e, k] == pytest.approx(fd, rel=1e-6, abs=1e-7)
