@@ -86,6 +86,7 @@ struct ConvArgs {
   const int32_t* slot_off;
   const int32_t* row_ptr;
   const int32_t* src;
+  const int32_t* order;  // receiver schedule (a locality order of the nodes)
   const void* x;
   const void* sh;
   const void* w;
@@ -100,8 +101,19 @@ struct ConvArgs {
 };
 
 constexpr int kWaves = kBlock / 64;
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
 
 __device__ __forceinline__ int conv_wave_id() { return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6); }
+
+// Workgroups are handed to the XCDs round-robin (workgroup w runs on XCD
+// w mod 8). Renumber them so that each XCD takes one contiguous range of the
+// receiver schedule: receivers that are close in the schedule share source
+// rows, and those reads then meet in the same L2.
+__device__ __forceinline__ int64_t xcd_block() {
+  const int64_t P = gridDim.x, w = blockIdx.x;
+  const int64_t q = P / kXcds, r = P % kXcds, x = w % kXcds, i = w / kXcds;
+  return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
 
 // ------------------------------------------------------------ fused forward
 // Slot chunks: consecutive slots whose accumulators fit a register budget of
@@ -260,11 +272,12 @@ __device__ __forceinline__ void fwd_fused_chunk(const ConvArgs& a, int64_t n, co
 template <typename T, typename A, int VEC, int L1, int L>
 __global__ __launch_bounds__(kBlock) void conv_fwd_fused_kernel(ConvArgs a) {
   using CK = Chunks<L1, L, conv_budget<A, VEC>()>;
-  const int64_t item = int64_t(blockIdx.x) * kWaves + conv_wave_id();
+  const int64_t item = xcd_block() * kWaves + conv_wave_id();
   const int64_t per_node = int64_t(CK::NCH) * a.nchunks;
-  const int64_t n = item / per_node;
-  if (n >= a.N) return;
-  const int rem = int(item - n * per_node);
+  const int64_t pos = item / per_node;
+  if (pos >= a.N) return;
+  const int rem = int(item - pos * per_node);
+  const int64_t n = a.order[pos];
   const int cc = rem / CK::NCH;
   const int ch = rem - cc * CK::NCH;
   const BlockDev blk = ldc(a.blocks + a.block);
@@ -312,11 +325,12 @@ __device__ __forceinline__ void fwd_general_path(const ConvArgs& a, int64_t n, c
 
 template <typename T, typename A>
 __global__ __launch_bounds__(kBlock) void conv_fwd_general_kernel(ConvArgs a) {
-  const int64_t item = int64_t(blockIdx.x) * kWaves + conv_wave_id();
+  const int64_t item = xcd_block() * kWaves + conv_wave_id();
   const int64_t per_node = int64_t(a.npaths) * a.nchunks;
-  const int64_t n = item / per_node;
-  if (n >= a.N) return;
-  const int rem = int(item - n * per_node);
+  const int64_t pos = item / per_node;
+  if (pos >= a.N) return;
+  const int rem = int(item - pos * per_node);
+  const int64_t n = a.order[pos];
   const int p = rem / a.nchunks;
   const int chunk = rem - p * a.nchunks;
   const PathDev pd = ldc(a.paths + p);
@@ -372,8 +386,10 @@ __global__ __launch_bounds__(kBlock) void conv_bwd_fused_kernel(ConvArgs a, Conv
   const int CW = LG * VEC;  // channels per chunk
   A* gl = reinterpret_cast<A*>(smem_raw);  // [S::NACC][CW]
   A* dsl = gl + S::NACC * CW;              // [64][dim_y]
-  const int64_t n = blockIdx.x / a.nchunks;
-  const int cc = int(blockIdx.x - n * a.nchunks);
+  const int64_t wg = xcd_block();
+  const int64_t pos = wg / a.nchunks;
+  const int cc = int(wg - pos * a.nchunks);
+  const int64_t n = a.order[pos];
   const BlockDev blk = ldc(a.blocks + a.block);
   const int U = blk.mul;
   int pid[NS], woff[NS], coff[NS];

@@ -35,6 +35,7 @@ ConvArgs make_conv_args(cgtp_plan_s* plan, const DevTables& t, const cgtp_graph_
   a.slot_off = t.slot_off;
   a.row_ptr = g->row_ptr;
   a.src = g->src;
+  a.order = g->order;
   a.N = g->N;
   a.dim_x = int(plan->dim_x);
   a.dim_y = int(plan->dim_y);

@@ -10,6 +10,7 @@ struct cgtp_graph_s {
   int32_t* col_ptr = nullptr;  // owned: transpose (edges grouped by source)
   int32_t* eid = nullptr;      // CSR position of each source-ordered edge
   int32_t* dst = nullptr;      // owned: destination of each CSR edge
+  int32_t* order = nullptr;    // owned: receiver schedule, a permutation of [0, N)
   int device = 0;
 };
 

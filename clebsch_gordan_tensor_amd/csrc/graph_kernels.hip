@@ -15,6 +15,36 @@
 
 #include "graph.hpp"
 
+// Receiver schedule for the convolution kernels: a breadth-first order over
+// the CSR (the neighbours of a receiver are its sources), components taken in
+// index order. Receivers that are close in this order share many sources, so
+// kernels that walk it (each XCD one contiguous range) read a source row into
+// L2 once for several receivers. Results do not depend on the schedule: every
+// receiver is summed by one owner in CSR order.
+static std::vector<int32_t> receiver_schedule(int64_t N, const std::vector<int32_t>& row_ptr,
+                                              const std::vector<int32_t>& src) {
+  std::vector<int32_t> order;
+  order.reserve(size_t(N));
+  std::vector<char> seen(size_t(N), 0);
+  for (int64_t start = 0; start < N; ++start) {
+    if (seen[size_t(start)]) continue;
+    seen[size_t(start)] = 1;
+    size_t head = order.size();
+    order.push_back(int32_t(start));
+    while (head < order.size()) {
+      const int32_t u = order[head++];
+      for (int32_t e = row_ptr[size_t(u)]; e < row_ptr[size_t(u) + 1]; ++e) {
+        const int32_t v = src[size_t(e)];
+        if (!seen[size_t(v)]) {
+          seen[size_t(v)] = 1;
+          order.push_back(v);
+        }
+      }
+    }
+  }
+  return order;
+}
+
 namespace cgtp {
 
 namespace {
@@ -248,10 +278,24 @@ cgtp_graph_s* graph_create(int64_t N, int64_t E, const int32_t* row_ptr, const i
       throw Error{CGTP_ERR_INDEX, "graph_create: invalid CSR (flags " + std::to_string(bad) +
                                       "): need row_ptr[0]=0, non-decreasing, row_ptr[N]=E, src in [0,N)"};
   }
+  std::vector<int32_t> order;
+  {
+    std::vector<int32_t> hrp(static_cast<size_t>(N + 1));
+    std::vector<int32_t> hsrc(static_cast<size_t>(E));
+    CGTP_CHECK_HIP(hipMemcpyAsync(hrp.data(), row_ptr, size_t(N + 1) * 4, hipMemcpyDeviceToHost, s));
+    if (E > 0) CGTP_CHECK_HIP(hipMemcpyAsync(hsrc.data(), src, size_t(E) * 4, hipMemcpyDeviceToHost, s));
+    CGTP_CHECK_HIP(hipStreamSynchronize(s));
+    order = receiver_schedule(N, hrp, hsrc);
+  }
   CGTP_CHECK_HIP(hipMalloc(&g->col_ptr, size_t(N + 1) * 4));
+  if (hipMalloc(&g->order, size_t(N) * 4 + 4) != hipSuccess) {
+    (void)hipFree(g->col_ptr);
+    throw Error{CGTP_ERR_ALLOC, "graph_create: device allocation failed"};
+  }
   if (E > 0) {
     if (hipMalloc(&g->eid, size_t(E) * 4) != hipSuccess || hipMalloc(&g->dst, size_t(E) * 4) != hipSuccess) {
       (void)hipFree(g->col_ptr);
+      (void)hipFree(g->order);
       (void)hipFree(g->eid);
       throw Error{CGTP_ERR_ALLOC, "graph_create: device allocation failed"};
     }
@@ -263,6 +307,8 @@ cgtp_graph_s* graph_create(int64_t N, int64_t E, const int32_t* row_ptr, const i
       hipLaunchKernelGGL(src_count, dim3(blocks_for(E, 256)), dim3(256), 0, s, src, counts.as<int32_t>(), E);
       CGTP_CHECK_HIP(hipGetLastError());
     }
+    if (N > 0)
+      CGTP_CHECK_HIP(hipMemcpyAsync(g->order, order.data(), size_t(N) * 4, hipMemcpyHostToDevice, s));
     exclusive_scan_i32(counts.as<int32_t>(), g->col_ptr, N, s);
     if (E > 0) {
       DevBuf fill(size_t(N) * 4 + 4), ts(size_t(E) * 4), tp(size_t(E) * 4);
@@ -279,6 +325,7 @@ cgtp_graph_s* graph_create(int64_t N, int64_t E, const int32_t* row_ptr, const i
     CGTP_CHECK_HIP(hipStreamSynchronize(s));
   } catch (...) {
     (void)hipFree(g->col_ptr);
+    (void)hipFree(g->order);
     (void)hipFree(g->eid);
     (void)hipFree(g->dst);
     throw;
@@ -291,6 +338,7 @@ void graph_destroy(cgtp_graph_s* g) {
   const bool have = hipGetDevice(&cur) == hipSuccess;
   if (hipSetDevice(g->device) == hipSuccess) {
     (void)hipFree(g->col_ptr);
+    (void)hipFree(g->order);
     (void)hipFree(g->eid);
     (void)hipFree(g->dst);
   }

@@ -150,8 +150,12 @@ cgtp_status cgtp_csr_from_coo(int64_t N, int64_t E, const int32_t* src, const in
  * the handle): validates row_ptr (row_ptr[0] = 0, non-decreasing,
  * row_ptr[N] = E) and src (in [0, N)), and builds the source-ordered
  * transpose used by the backward pass (owned by the handle; edges grouped by
- * source, in CSR-position order). Synchronises the stream once.
- * Errors: INDEX on invalid arrays. */
+ * source, in CSR-position order). It also copies the two arrays to the host
+ * once to build a receiver schedule (breadth-first order over the graph) that
+ * the convolution kernels walk so that receivers sharing sources run close
+ * together; results do not depend on it (each receiver is still summed by one
+ * owner in CSR order). Synchronises the stream.
+ * Errors: INDEX on invalid arrays, ALLOC if device memory runs out. */
 cgtp_status cgtp_graph_create(int64_t N, int64_t E, const int32_t* row_ptr, const int32_t* src,
                               void* stream, cgtp_graph* out);
 cgtp_status cgtp_graph_destroy(cgtp_graph graph);
