@@ -23,13 +23,9 @@ struct AccOf<double> {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// Round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
+// Round to nearest, ties to even (gfx950 converts in hardware: two values per
+// v_cvt_pk_bf16_f32; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 
 template <typename A>
 __device__ __forceinline__ A to_acc(float v) { return A(v); }
