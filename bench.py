@@ -2,6 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload tp_large]
                     [--no-conv] [--no-cpu-baseline]
+    python bench.py --profile WORKLOAD      (a few calls of every operation, for rocprofv3)
+    python bench.py --calibrate-copy        (a plain copy of known size, for the byte counters)
 
 Workload (default tp_large): 1,048,576 rows of x = 128x(0e+1o+2e+3o), y = the
 real spherical harmonics (L = 3) of random unit vectors, per-row weights for
@@ -11,16 +13,15 @@ of x, y and w), with every input already resident in HBM. `value` is rows
 ("pairs") per second of whole steps.
 
 Besides the headline line's `roofline` (dominant kernel, algorithmic bytes per
-launch over its mean HIP-event duration against 8 TB/s) and `cpu_baseline`
-(the fp64 oracle on a bounded sample, on the host cores), `extra` carries the
-per-kernel figures and, unless --no-conv, the fused convolution (forward and
-backward, fp32) on the 1000- and 8000-molecule water boxes (the latter with the
-harmonics forward/backward of the force chain) and the 100,000-point uniform
-cloud.
+call over its mean HIP-event duration against 8 TB/s) and `cpu_baseline` (the
+fp64 oracle on a bounded sample, on the host cores), `extra` carries the
+per-kernel figures, the same workload in bf16 storage and, unless --no-conv,
+the fused convolution (forward and backward, fp32) on the 1000- and
+8000-molecule water boxes (the latter with the harmonics forward/backward of
+the force chain) and the 100,000-point uniform cloud.
 """
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -33,6 +34,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "TP pairs/s + conv edges/s (fwd, fwd+bwd) as HBM GB/s and % of MI355X peak"
 PROFILES = os.path.join(ROOT, "profiles")
+WORKLOADS = ["tp_large", "tp_large_bf16", "conv_water1k", "conv_water8k", "conv_uniform100k"]
 
 
 def parse():
@@ -46,6 +48,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 4 GiB device copy (reference for HBM byte counters) and exit")
+    ap.add_argument("--profile", choices=WORKLOADS, default=None,
+                    help="only run a few calls of every operation of one workload (for rocprofv3) and exit")
     return ap.parse_args()
 
 
@@ -61,25 +65,18 @@ def calibrate_copy(torch):
                       "bytes_written_per_launch": 4 * n, "launches": 3}), flush=True)
 
 
-def kernel_source_hash(names):
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "clebsch_gordan_tensor_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-def traffic_for(kernel, src_files, per_launch_units):
-    """HBM bytes per launch from the committed counter summary, or None when the
-    kernel sources changed since the counters were taken."""
+def traffic_for(kernel, workload, units):
+    """HBM bytes of one call from the committed counter summary, or None when the
+    kernel's sources changed since the counters were taken."""
+    from clebsch_gordan_tensor_amd.profsum import source_hash
     path = os.path.join(PROFILES, "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f).get(kernel)
-    if not rec or rec.get("source_hash") != kernel_source_hash(src_files):
+        rec = json.load(f).get("%s@%s" % (kernel, workload))
+    if not rec or rec.get("source_hash") != source_hash(rec["sources"]):
         return None
-    return rec["bytes_per_unit"] * per_launch_units
+    return rec["bytes_per_unit"] * units
 
 
 class KernelTimer:
@@ -102,37 +99,152 @@ class KernelTimer:
         return sum(s.elapsed_time(e) for s, e in self.pairs) / len(self.pairs)
 
 
-def plan_blocks(plan):
-    """x blocks of a plan (one kernel launch each)."""
-    return [t for t in plan.irreps_x.replace(" ", "").split("+") if t]
+# ------------------------------------------------------------------ workloads
 
+class TPWorkload:
+    """tp_large: 2^20 rows, per-row weights; fp32 (with the harmonics of the row
+    directions computed in the step) or bf16 storage (harmonics drawn directly)."""
+
+    def __init__(self, torch, cgtp, synth, dtype):
+        c = synth.CONFIGS["tp_large"]
+        self.torch, self.cgtp, self.dtype = torch, cgtp, dtype
+        self.plan = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"], dtype=dtype, wkind="per_row")
+        self.irreps_x = c["irreps_x"]
+        self.B = B = c["B"]
+        p = self.plan
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(0)
+        td = torch.float32 if dtype == "f32" else torch.bfloat16
+        self.x = torch.randn((B, p.dim_x), generator=gen, device="cuda").to(td)
+        self.w = torch.randn((B, p.w_numel), generator=gen, device="cuda").to(td)
+        self.g = torch.randn((B, p.dim_out), generator=gen, device="cuda").to(td)
+        if dtype == "f32":
+            v = torch.randn((B, 3), generator=gen, device="cuda")
+            self.v = v / v.norm(dim=1, keepdim=True)
+            self.y = torch.empty((B, p.dim_y), device="cuda")
+            cgtp.sh_forward(3, self.v, out=self.y)
+        else:
+            self.v = None
+            self.y = torch.randn((B, p.dim_y), generator=gen, device="cuda").to(td)
+        self.out = torch.empty((B, p.dim_out), device="cuda", dtype=td)
+        self.dx, self.dy, self.dw = torch.empty_like(self.x), torch.empty_like(self.y), torch.empty_like(self.w)
+        self.es = 4 if dtype == "f32" else 2
+
+    def sh(self):
+        if self.v is not None:
+            self.cgtp.sh_forward(3, self.v, out=self.y)
+
+    def fwd(self):
+        self.plan.tp_forward(self.x, self.y, self.w, out=self.out)
+
+    def bwd(self):
+        self.plan.tp_backward(self.x, self.y, self.w, self.g, out=(self.dx, self.dy, self.dw))
+
+    def bytes_fwd(self):  # per row: x, y, w read, out written
+        p = self.plan
+        return self.es * (p.dim_x + p.dim_y + p.w_numel + p.dim_out)
+
+    def bytes_bwd(self):  # per row: x, y, w, grad_out read, grad x, y, w written
+        p = self.plan
+        return self.es * (2 * p.dim_x + 2 * p.dim_y + 2 * p.w_numel + p.dim_out)
+
+
+class ConvWorkload:
+    """One convolution workload at full size, fp32: graph, harmonics and radial
+    weights built as the benchmark description states (weights by the caller's
+    radial network, not timed), then forward / backward calls."""
+
+    def __init__(self, torch, cgtp, synth, name):
+        import numpy as np
+        c = synth.CONFIGS[name]
+        self.torch, self.cgtp, self.c = torch, cgtp, c
+        dev = torch.device("cuda:0")
+        self.plan = p = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"], dtype="f32", wkind="per_row")
+        pos = synth.positions_for(c, 0)
+        src, dst, vec = synth.radius_graph(pos, c["box"], c["r_cut"])
+        self.N, self.E = N, E = pos.shape[0], src.shape[0]
+        row_ptr, src_s, perm = cgtp.csr_from_coo(N, torch.from_numpy(src.astype(np.int32)).to(dev),
+                                                 torch.from_numpy(dst.astype(np.int32)).to(dev))
+        self.row_ptr, self.src_s = row_ptr, src_s
+        self.graph = cgtp.Graph(N, row_ptr, src_s)
+        self.vec = torch.from_numpy(vec).to(dev)[perm.long()].float().contiguous()
+        self.Y = cgtp.sh_forward(c["L"], self.vec)
+        W1, W2 = synth.mlp_params(8, 64, p.w_numel, 0)
+        W1, W2 = torch.from_numpy(W1).float().to(dev), torch.from_numpy(W2).float().to(dev)
+        r = self.vec.norm(dim=1)
+        self.w = torch.empty((E, p.w_numel), device=dev)
+        for a in range(0, E, 1 << 20):
+            self.w[a:a + (1 << 20)] = synth.radial_weights_torch(r[a:a + (1 << 20)], c["r_cut"], W1, W2)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(0)
+        self.x = torch.randn((N, p.dim_x), generator=gen, device=dev)
+        self.gout = torch.randn((N, p.dim_out), generator=gen, device=dev)
+        self.scale = 1.0 / math.sqrt(E / N)
+        self.out = torch.empty((N, p.dim_out), device=dev)
+        self.dx, self.dY, self.dw = torch.empty_like(self.x), torch.empty_like(self.Y), torch.empty_like(self.w)
+        self.ws = torch.empty(p.workspace_size(cgtp.OP_CONV_BACKWARD, graph=self.graph), dtype=torch.uint8,
+                              device=dev)
+        self.gvec = torch.empty_like(self.vec)
+
+    def sh_fwd(self):
+        self.cgtp.sh_forward(self.c["L"], self.vec, out=self.Y)
+
+    def fwd(self):
+        self.plan.conv_forward(self.graph, self.x, self.Y, self.w, self.scale, out=self.out)
+
+    def bwd(self):
+        self.plan.conv_backward(self.graph, self.x, self.Y, self.w, self.scale, self.gout,
+                                out=(self.dx, self.dY, self.dw), ws=self.ws)
+
+    def sh_bwd(self):
+        self.cgtp.sh_backward(self.c["L"], self.vec, self.dY, out=self.gvec)
+
+    def bytes_fwd(self):  # w, sh, src read per edge; x read and out written per node; row_ptr
+        p = self.plan
+        return 4 * (p.w_numel + p.dim_y + 1) * self.E + 4 * (p.dim_out + p.dim_x + 1) * self.N
+
+    def bytes_bwd(self):  # + grad w, grad sh written per edge; grad_out read, grad x written per node
+        p = self.plan
+        return 4 * (2 * p.w_numel + 2 * p.dim_y + 1) * self.E + 4 * (p.dim_out + 2 * p.dim_x + 1) * self.N
+
+
+def make_workload(torch, cgtp, synth, name):
+    if name == "tp_large":
+        return TPWorkload(torch, cgtp, synth, "f32")
+    if name == "tp_large_bf16":
+        return TPWorkload(torch, cgtp, synth, "bf16")
+    return ConvWorkload(torch, cgtp, synth, name)
+
+
+def profile(torch, cgtp, synth, name):
+    """Three calls of every operation of one workload (the first one warms up)."""
+    wl = make_workload(torch, cgtp, synth, name)
+    ops = [wl.sh, wl.fwd, wl.bwd] if name.startswith("tp") else [wl.sh_fwd, wl.fwd, wl.bwd, wl.sh_bwd]
+    for _ in range(3):
+        for op in ops:
+            op()
+    torch.cuda.synchronize()
+    units = wl.B if name.startswith("tp") else wl.E
+    print(json.dumps({"profiled": name, "calls": 3, "units": units,
+                      "unit": "row" if name.startswith("tp") else "edge"}), flush=True)
+
+
+# ------------------------------------------------------------------ benches
 
 def tp_large_bench(args, torch, cgtp, synth, extra):
-    c = synth.CONFIGS["tp_large"]
-    plan = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"], dtype="f32", wkind="per_row")
-    B = c["B"]
-    dev = torch.device("cuda:0")
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(0)
-    x = torch.randn((B, plan.dim_x), generator=gen, device=dev)
-    w = torch.randn((B, plan.w_numel), generator=gen, device=dev)
-    g = torch.randn((B, plan.dim_out), generator=gen, device=dev)
-    v = torch.randn((B, 3), generator=gen, device=dev)
-    v = v / v.norm(dim=1, keepdim=True)
-    y = torch.empty((B, plan.dim_y), device=dev)
-    out = torch.empty((B, plan.dim_out), device=dev)
-    dx, dy, dw = torch.empty_like(x), torch.empty_like(y), torch.empty_like(w)
+    wl = TPWorkload(torch, cgtp, synth, "f32")
+    B = wl.B
     t_sh, t_fwd, t_bwd = KernelTimer(torch), KernelTimer(torch), KernelTimer(torch)
 
     def step(timed):
         if timed:
-            t_sh(lambda: cgtp.sh_forward(3, v, out=y))
-            t_fwd(lambda: plan.tp_forward(x, y, w, out=out))
-            t_bwd(lambda: plan.tp_backward(x, y, w, g, out=(dx, dy, dw)))
+            t_sh(wl.sh)
+            t_fwd(wl.fwd)
+            t_bwd(wl.bwd)
         else:
-            cgtp.sh_forward(3, v, out=y)
-            plan.tp_forward(x, y, w, out=out)
-            plan.tp_backward(x, y, w, g, out=(dx, dy, dw))
+            wl.sh()
+            wl.fwd()
+            wl.bwd()
 
     for _ in range(args.warmup):
         step(False)
@@ -144,68 +256,52 @@ def tp_large_bench(args, torch, cgtp, synth, extra):
     wall = time.perf_counter() - t0
     ms_step = 1000.0 * wall / args.steps
 
-    by_fwd = 4 * (plan.dim_x + plan.dim_y + plan.w_numel + plan.dim_out)          # 105,536 B/row
-    by_bwd = 4 * (2 * plan.dim_x + 2 * plan.dim_y + 2 * plan.w_numel + plan.dim_out)  # 131,200 B/row
-    by_sh = 4 * (3 + plan.dim_y)
     kern = {}
-    for name, t, bpr, srcs in (
-            ("tp_fwd_kernel", t_fwd, by_fwd, ["tp_impl.hpp", "tp_core.hpp", "cg_pattern.h", "device_util.hpp"]),
-            ("tp_bwd_kernel", t_bwd, by_bwd, ["tp_impl.hpp", "tp_core.hpp", "cg_pattern.h", "device_util.hpp"]),
-            ("sh_fwd_kernel", t_sh, by_sh, ["sh_kernels.hip", "device_util.hpp"])):
+    for name, t, bpr in (("tp_fwd_kernel", t_fwd, wl.bytes_fwd()),   # 105,536 B/row
+                         ("tp_bwd_kernel", t_bwd, wl.bytes_bwd()),   # 131,200 B/row
+                         ("sh_fwd_kernel", t_sh, 4 * (3 + wl.plan.dim_y))):
         ms = t.mean_ms()
         gbs = bpr * B / (ms * 1e-3) / 1e9
         kern[name] = dict(ms=round(ms, 4), bytes_per_row=bpr, algorithmic_GBs=round(gbs, 1),
                           frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4), rows_per_s=B / (ms * 1e-3),
-                          traffic=traffic_for(name, srcs, B))
-        kern[name]["_srcs"] = srcs
+                          traffic=traffic_for(name, "tp_large", B))
     dom = max(("tp_fwd_kernel", "tp_bwd_kernel"), key=lambda k: kern[k]["ms"])
     d = kern[dom]
+    nblk = len([t for t in wl.irreps_x.split("+") if t])
     roofline = {"bound": "hbm", "kernel": dom, "achieved": d["algorithmic_GBs"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": d["frac_of_hbm_peak"], "traffic": d["traffic"],
                 "algorithmic_bytes_per_launch": d["bytes_per_row"] * B, "mean_launch_ms": d["ms"],
-                "launch": "one call = %d launches of %s (one per x block, degree-specialised)"
-                          % (len(plan_blocks(plan)), dom)}
-    for k in kern.values():
-        k.pop("_srcs")
+                "launch": "one call = %d launches of %s (one per x block, degree-specialised), timed as one"
+                          % (nblk, dom)}
     extra["tp_large_kernels"] = kern
     extra["tp_large_fwd_pairs_per_s"] = kern["tp_fwd_kernel"]["rows_per_s"]
     extra["tp_large_fwd_bwd_pairs_per_s"] = B / ((kern["tp_fwd_kernel"]["ms"] + kern["tp_bwd_kernel"]["ms"]) * 1e-3)
-    del x, w, g, v, y, out, dx, dy, dw
+    plan = wl.plan
+    del wl
     torch.cuda.empty_cache()
     return B * args.steps / wall, ms_step, roofline, plan
 
 
 def tp_large_bf16(args, torch, cgtp, synth):
     """tp_large in bf16 storage (fp32 arithmetic): forward and backward call times."""
-    c = synth.CONFIGS["tp_large"]
-    plan = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"], dtype="bf16", wkind="per_row")
-    B = c["B"]
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(0)
-    bf = torch.bfloat16
-    x = torch.randn((B, plan.dim_x), generator=gen, device="cuda").to(bf)
-    w = torch.randn((B, plan.w_numel), generator=gen, device="cuda").to(bf)
-    g = torch.randn((B, plan.dim_out), generator=gen, device="cuda").to(bf)
-    y = torch.randn((B, plan.dim_y), generator=gen, device="cuda").to(bf)
-    out = torch.empty((B, plan.dim_out), device="cuda", dtype=bf)
-    dx, dy, dw = torch.empty_like(x), torch.empty_like(y), torch.empty_like(w)
+    wl = TPWorkload(torch, cgtp, synth, "bf16")
+    B = wl.B
     tf, tb = KernelTimer(torch), KernelTimer(torch)
-    for k in range(4):
-        if k == 0:
-            plan.tp_forward(x, y, w, out=out)
-            plan.tp_backward(x, y, w, g, out=(dx, dy, dw))
-        else:
-            tf(lambda: plan.tp_forward(x, y, w, out=out))
-            tb(lambda: plan.tp_backward(x, y, w, g, out=(dx, dy, dw)))
+    wl.fwd()
+    wl.bwd()
+    for _ in range(3):
+        tf(wl.fwd)
+        tb(wl.bwd)
     torch.cuda.synchronize()
-    by_f = 2 * (plan.dim_x + plan.dim_y + plan.w_numel + plan.dim_out)
-    by_b = 2 * (2 * plan.dim_x + 2 * plan.dim_y + 2 * plan.w_numel + plan.dim_out)
+    by_f, by_b = wl.bytes_fwd(), wl.bytes_bwd()
     f, b = tf.mean_ms(), tb.mean_ms()
-    del x, w, g, y, out, dx, dy, dw
+    del wl
     torch.cuda.empty_cache()
     return dict(fwd_ms=round(f, 3), fwd_pairs_per_s=B / (f * 1e-3), fwd_algorithmic_GBs=round(by_f * B / f / 1e6, 1),
                 bwd_ms=round(b, 3), fwd_bwd_pairs_per_s=B / ((f + b) * 1e-3),
-                bwd_algorithmic_GBs=round(by_b * B / b / 1e6, 1), bytes_per_row_fwd=by_f, bytes_per_row_bwd=by_b)
+                bwd_algorithmic_GBs=round(by_b * B / b / 1e6, 1), bytes_per_row_fwd=by_f, bytes_per_row_bwd=by_b,
+                fwd_traffic_bytes=traffic_for("tp_fwd_kernel", "tp_large_bf16", B),
+                bwd_traffic_bytes=traffic_for("tp_bwd_kernel", "tp_large_bf16", B))
 
 
 def conv_bench(args, torch, cgtp, synth, name, steps, forces=False):
@@ -216,56 +312,25 @@ def conv_bench(args, torch, cgtp, synth, name, steps, forces=False):
     the convolution backward; both are timed and reported on their own. The
     radial network's part of the force chain belongs to the caller and is not
     timed."""
-    import numpy as np
-    c = synth.CONFIGS[name]
-    dev = torch.device("cuda:0")
-    plan = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"], dtype="f32", wkind="per_row")
-    pos = synth.positions_for(c, 0)
-    src, dst, vec = synth.radius_graph(pos, c["box"], c["r_cut"])
-    N, E = pos.shape[0], src.shape[0]
-    row_ptr, src_s, perm = cgtp.csr_from_coo(N, torch.from_numpy(src.astype(np.int32)).to(dev),
-                                             torch.from_numpy(dst.astype(np.int32)).to(dev))
-    graph = cgtp.Graph(N, row_ptr, src_s)
-    vec_d = torch.from_numpy(vec).to(dev)[perm.long()].float().contiguous()
-    Y = cgtp.sh_forward(c["L"], vec_d)
-    W1, W2 = synth.mlp_params(8, 64, plan.w_numel, 0)
-    W1, W2 = torch.from_numpy(W1).float().to(dev), torch.from_numpy(W2).float().to(dev)
-    r = vec_d.norm(dim=1)
-    w = torch.empty((E, plan.w_numel), device=dev)
-    for a in range(0, E, 1 << 20):
-        w[a:a + (1 << 20)] = synth.radial_weights_torch(r[a:a + (1 << 20)], c["r_cut"], W1, W2)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(0)
-    x = torch.randn((N, plan.dim_x), generator=gen, device=dev)
-    gout = torch.randn((N, plan.dim_out), generator=gen, device=dev)
-    scale = 1.0 / math.sqrt(E / N)
-    out = torch.empty((N, plan.dim_out), device=dev)
-    dx, dY, dw = torch.empty_like(x), torch.empty_like(Y), torch.empty_like(w)
-    ws = torch.empty(plan.workspace_size(cgtp.OP_CONV_BACKWARD, graph=graph), dtype=torch.uint8, device=dev)
-    gvec = torch.empty_like(vec_d)
+    wl = ConvWorkload(torch, cgtp, synth, name)
+    E, N = wl.E, wl.N
     tf, tb, tsf, tsb = KernelTimer(torch), KernelTimer(torch), KernelTimer(torch), KernelTimer(torch)
-    for k in range(steps + 1):
-        if k == 0:
-            plan.conv_forward(graph, x, Y, w, scale, out=out)
-            plan.conv_backward(graph, x, Y, w, scale, gout, out=(dx, dY, dw), ws=ws)
-        else:
-            if forces:
-                tsf(lambda: cgtp.sh_forward(c["L"], vec_d, out=Y))
-            tf(lambda: plan.conv_forward(graph, x, Y, w, scale, out=out))
-            tb(lambda: plan.conv_backward(graph, x, Y, w, scale, gout, out=(dx, dY, dw), ws=ws))
-            if forces:
-                tsb(lambda: cgtp.sh_backward(c["L"], vec_d, dY, out=gvec))
+    wl.fwd()
+    wl.bwd()
+    for _ in range(steps):
+        if forces:
+            tsf(wl.sh_fwd)
+        tf(wl.fwd)
+        tb(wl.bwd)
+        if forces:
+            tsb(wl.sh_bwd)
     torch.cuda.synchronize()
-    bf = 4 * (plan.w_numel + plan.dim_y + 1) * E + 4 * (plan.dim_out + plan.dim_x + 1) * N
-    bb = 4 * (2 * plan.w_numel + 2 * plan.dim_y + 1) * E + 4 * (plan.dim_out + 2 * plan.dim_x + 1) * N
+    bf, bb = wl.bytes_fwd(), wl.bytes_bwd()
     msf, msb = tf.mean_ms(), tb.mean_ms()
-    cv = ["conv_impl.hpp", "conv_kernels.hip", "tp_core.hpp", "cg_pattern.h", "device_util.hpp"]
-    tr_f = traffic_for("conv_fwd_fused_kernel", cv, E) if name == "conv_uniform100k" else None
-    tr_b = None
-    if name == "conv_uniform100k":
-        b1, b2 = traffic_for("conv_bwd_fused_kernel", cv, E), traffic_for("dx_gather_kernel", cv, E)
-        tr_b = b1 + b2 if b1 is not None and b2 is not None else None
-    res = dict(N=N, E=E, paths=plan.num_paths, fwd_traffic_bytes=tr_f, bwd_traffic_bytes=tr_b,
+    b1, b2 = traffic_for("conv_bwd_fused_kernel", name, E), traffic_for("dx_gather_kernel", name, E)
+    res = dict(N=N, E=E, paths=wl.plan.num_paths,
+               fwd_traffic_bytes=traffic_for("conv_fwd_fused_kernel", name, E),
+               bwd_traffic_bytes=b1 + b2 if b1 is not None and b2 is not None else None,
                fwd_ms=round(msf, 3), fwd_edges_per_s=E / (msf * 1e-3),
                fwd_algorithmic_GBs=round(bf / (msf * 1e-3) / 1e9, 1),
                fwd_frac_of_hbm_peak=round(bf / (msf * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -275,14 +340,13 @@ def conv_bench(args, torch, cgtp, synth, name, steps, forces=False):
     if forces:
         res.update(sh_fwd_ms=round(tsf.mean_ms(), 4), sh_bwd_ms=round(tsb.mean_ms(), 4),
                    fwd_bwd_forces_edges_per_s=E / ((msf + msb + tsf.mean_ms() + tsb.mean_ms()) * 1e-3))
-    del w, dw, ws, x, gout, out, dx, dY, Y, graph, gvec
+    del wl
     torch.cuda.empty_cache()
     return res
 
 
 def cpu_baseline(args, synth):
     """The oracle as it stands, tp_large fwd+bwd on a bounded row sample."""
-    import numpy as np
     from oracle import sh as osh
     from oracle import tp as otp
     from oracle.irreps import Layout
@@ -320,6 +384,9 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         calibrate_copy(torch)
+        return
+    if args.profile:
+        profile(torch, cgtp, synth, args.profile)
         return
     extra = {"device": torch.cuda.get_device_name(0)}
     value, ms_step, roofline, plan = tp_large_bench(args, torch, cgtp, synth, extra)
