@@ -30,21 +30,26 @@
 #define CGTP_TP_FWD_WAVES 0
 #endif
 #ifndef CGTP_TP_BWD_WAVES
-#define CGTP_TP_BWD_WAVES 0
+#define CGTP_TP_BWD_WAVES 3
 #endif
 #ifndef CGTP_NT_STORE
 #define CGTP_NT_STORE 0
+#endif
+// Backward grad_x accumulators of the degree-specialised kernels in the
+// lane's own LDS slots (1) instead of registers (0). With them out of the
+// register file, the degree-specialised kernels with 4- and 2-byte storage
+// and largest degree <= 3 ask the allocator for CGTP_TP_BWD_WAVES waves per
+// SIMD (tp_large fp32 backward 27.7 -> 25.6 ms, bf16 23.2 -> 20.0 ms against
+// registers and no request); the others make no request.
+#ifndef CGTP_TP_BWD_DX_LDS
+#define CGTP_TP_BWD_DX_LDS 1
 #endif
 #if CGTP_TP_FWD_WAVES > 0
 #define CGTP_FWD_OCC __attribute__((amdgpu_waves_per_eu(CGTP_TP_FWD_WAVES)))
 #else
 #define CGTP_FWD_OCC
 #endif
-#if CGTP_TP_BWD_WAVES > 0
-#define CGTP_BWD_OCC __attribute__((amdgpu_waves_per_eu(CGTP_TP_BWD_WAVES)))
-#else
-#define CGTP_BWD_OCC
-#endif
+
 
 namespace cgtp {
 
@@ -171,14 +176,55 @@ __global__ __launch_bounds__(kBlock) CGTP_FWD_OCC void tp_fwd_kernel(TPArgs a) {
 
 // ------------------------------------------------------------------ backward
 
+// N rows of VEC accumulators owned by one lane: in registers, or in the
+// lane's private LDS slots (layout [row][thread][VEC], no sharing, no sync).
+template <typename A, int VEC, int N, bool IN_LDS>
+struct RowAcc {
+  A r[N][VEC];
+  __device__ __forceinline__ explicit RowAcc(A*) {
+#pragma unroll
+    for (int m = 0; m < N; ++m)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) r[m][v] = A(0);
+  }
+  __device__ __forceinline__ void fma_row(int m, const A (&w)[VEC], const A (&q)[VEC]) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) r[m][v] = fma(w[v], q[v], r[m][v]);
+  }
+  __device__ __forceinline__ void get(int m, A (&o)[VEC]) const {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) o[v] = r[m][v];
+  }
+};
+template <typename A, int VEC, int N>
+struct RowAcc<A, VEC, N, true> {
+  A* p;  // this lane's row 0
+  __device__ __forceinline__ explicit RowAcc(A* base) : p(base + threadIdx.x * VEC) {
+#pragma unroll
+    for (int m = 0; m < N; ++m)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) p[m * kBlock * VEC + v] = A(0);
+  }
+  __device__ __forceinline__ void fma_row(int m, const A (&w)[VEC], const A (&q)[VEC]) {
+    A t[VEC];
+    get(m, t);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) p[m * kBlock * VEC + v] = fma(w[v], q[v], t[v]);
+  }
+  __device__ __forceinline__ void get(int m, A (&o)[VEC]) const {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) o[v] = p[m * kBlock * VEC + v];
+  }
+};
+
 template <typename T, typename A, int VEC, int LM>
 struct TPBwd {
-  template <int L1, int L2, int L3>
+  template <int L1, int L2, int L3, typename DX>
   __device__ static __forceinline__ void path(const TPArgs& a, const PathDev& pd,
                                               const A (&xb)[2 * L1 + 1][VEC],
                                               const A (&yb)[2 * L2 + 1], const T* gr,
                                               const T* wr, T* dwr, A* dwa, int c,
-                                              A (&dxb)[2 * L1 + 1][VEC], A (&dyb)[2 * L2 + 1]) {
+                                              DX& dxb, A (&dyb)[2 * L2 + 1]) {
     using P = Pattern<L1, L2, L3>;
     const A* __restrict__ cf = static_cast<const A*>(a.coef) + pd.coef_off;
     const A gs = A(a.g_scale);
@@ -227,21 +273,19 @@ struct TPBwd {
       if constexpr (pr.n == 2) dyb[pr.m2b + L2] = fma(cb, s, dyb[pr.m2b + L2]);
       if constexpr (last) {
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-          d[v] = fma(xb[pr.m1 + L1][v], q[v], d[v]);
-          dxb[pr.m1 + L1][v] = fma(wv[v], q[v], dxb[pr.m1 + L1][v]);
-        }
+        for (int v = 0; v < VEC; ++v) d[v] = fma(xb[pr.m1 + L1][v], q[v], d[v]);
+        dxb.fma_row(pr.m1 + L1, wv, q);
       }
     });
     if (dwr) VecIO<T, VEC>::store(dwr + pd.w_off + c, d);
     if (dwa) VecIO<A, VEC>::store(dwa + pd.w_off + c, d);
   }
 
-  template <int L1, int L2>
+  template <int L1, int L2, typename DX>
   __device__ static __forceinline__ void run(const TPArgs& a, int p, int pend,
                                              const A (&xb)[2 * L1 + 1][VEC], const T* yr,
                                              const T* gr, const T* wr, T* dwr, A* dwa, int c,
-                                             A (&dxb)[2 * L1 + 1][VEC], A* lds) {
+                                             DX& dxb, A* lds) {
     A yb[2 * L2 + 1], dyb[2 * L2 + 1];
     const int yoff = ldc(&a.paths[p].y_off);
 #pragma unroll
@@ -263,17 +307,15 @@ struct TPBwd {
     for (int m = 0; m < 2 * L2 + 1; ++m) lds[(yoff + m) * kBlock + threadIdx.x] += dyb[m];
   }
 
-  template <int L1>
+  // dx_lds: grad_x rows in this lane's LDS slots after the grad_y columns
+  template <int L1, bool DX_LDS>
   __device__ static __forceinline__ void block(const TPArgs& a, const BlockDev& blk, const T* xr,
                                                const T* yr, const T* gr, const T* wr, T* dxr,
                                                A* dxa, T* dwr, A* dwa, int c, A* lds) {
-    A xb[2 * L1 + 1][VEC], dxb[2 * L1 + 1][VEC];
+    A xb[2 * L1 + 1][VEC];
 #pragma unroll
-    for (int m = 0; m < 2 * L1 + 1; ++m) {
-      VecIO<T, VEC>::load(xr + blk.x_off + m * blk.mul + c, xb[m]);
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) dxb[m][v] = A(0);
-    }
+    for (int m = 0; m < 2 * L1 + 1; ++m) VecIO<T, VEC>::load(xr + blk.x_off + m * blk.mul + c, xb[m]);
+    RowAcc<A, VEC, 2 * L1 + 1, DX_LDS> dxb(lds + a.dim_y * kBlock);
     int p = blk.path_begin;
     while (p < blk.path_end) {
       const int l2 = ldc(&a.paths[p].l2);
@@ -284,19 +326,26 @@ struct TPBwd {
       });
       p = pend;
     }
-    if (dxr) {
 #pragma unroll
-      for (int m = 0; m < 2 * L1 + 1; ++m) VecIO<T, VEC>::store(dxr + blk.x_off + m * blk.mul + c, dxb[m]);
-    }
-    if (dxa) {
-#pragma unroll
-      for (int m = 0; m < 2 * L1 + 1; ++m) VecIO<A, VEC>::store(dxa + blk.x_off + m * blk.mul + c, dxb[m]);
+    for (int m = 0; m < 2 * L1 + 1; ++m) {
+      A o[VEC];
+      dxb.get(m, o);
+      if (dxr) VecIO<T, VEC>::store(dxr + blk.x_off + m * blk.mul + c, o);
+      if (dxa) VecIO<A, VEC>::store(dxa + blk.x_off + m * blk.mul + c, o);
     }
   }
 };
 
+// (requested only where the spill it costs stays small: largest degree <= 3)
+template <typename T, int L1, int LM>
+struct BwdWaves {
+  static constexpr int value =
+      (L1 >= 0 && LM <= 3 && sizeof(T) <= 4 && CGTP_TP_BWD_WAVES > 1) ? CGTP_TP_BWD_WAVES : 1;
+};
+
 template <typename T, typename A, int VEC, int L1, int LM>
-__global__ __launch_bounds__(kBlock) CGTP_BWD_OCC void tp_bwd_kernel(TPArgs a) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BwdWaves<T, L1, LM>::value)))
+void tp_bwd_kernel(TPArgs a) {
   extern __shared__ unsigned char smem_raw[];
   A* lds = reinterpret_cast<A*>(smem_raw);  // [dim_y][kBlock], one column per lane
   const int64_t gt = int64_t(blockIdx.x) * kBlock + threadIdx.x;
@@ -321,7 +370,8 @@ __global__ __launch_bounds__(kBlock) CGTP_BWD_OCC void tp_bwd_kernel(TPArgs a) {
       if constexpr (L1 >= 0) {
         const BlockDev blk = ldc(a.blocks + a.block);
         if (c < blk.mul)
-          TPBwd<T, A, VEC, LM>::template block<L1>(a, blk, xr, yr, gr, wr, dxr, dxa, dwr, dwa, c, lds);
+          TPBwd<T, A, VEC, LM>::template block<L1, CGTP_TP_BWD_DX_LDS != 0>(a, blk, xr, yr, gr, wr, dxr, dxa,
+                                                                           dwr, dwa, c, lds);
       } else {
         for (int b = 0; b < a.nblocks; ++b) {
           const BlockDev blk = ldc(a.blocks + b);
@@ -329,7 +379,7 @@ __global__ __launch_bounds__(kBlock) CGTP_BWD_OCC void tp_bwd_kernel(TPArgs a) {
           static_for<0, kLmax + 1>([&](auto L1c) {
             constexpr int D = decltype(L1c)::value;
             if (blk.l1 == D)
-              TPBwd<T, A, VEC, LM>::template block<D>(a, blk, xr, yr, gr, wr, dxr, dxa, dwr, dwa, c, lds);
+              TPBwd<T, A, VEC, LM>::template block<D, false>(a, blk, xr, yr, gr, wr, dxr, dxa, dwr, dwa, c, lds);
           });
         }
       }
@@ -411,7 +461,8 @@ template <typename T, int VEC>
 void tp_bwd_typed(const TPArgs& a, int l1, int lm, hipStream_t s) {
   using A = typename AccOf<T>::type;
   const dim3 grid = grid_for(a.B, a.lpr_log2);
-  const size_t lds = size_t(a.dim_y) * kBlock * sizeof(A);
+  const size_t lds = size_t(a.dim_y) * kBlock * sizeof(A) +
+                     (CGTP_TP_BWD_DX_LDS && VEC > 1 && l1 >= 0 ? size_t(2 * l1 + 1) * kBlock * VEC * sizeof(A) : 0);
   if constexpr (VEC == 1) {
     (void)l1;
     (void)lm;
