@@ -241,13 +241,7 @@ __device__ __forceinline__ void fwd_fused_chunk(const ConvArgs& a, int64_t n, co
     }
   }
   // sum the groups' partial sums (every lane takes part), then group 0 stores
-  const int LG = 64 / G;
-  for (int off = LG; off < 64; off <<= 1) {
-#pragma unroll
-    for (int i = 0; i < NACC; ++i)
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) acc[i][v] += __shfl_xor(acc[i][v], off, 64);
-  }
+  xor_sum_n<NACC * VEC>(reinterpret_cast<A (&)[NACC * VEC]>(acc), 64 / G, 64);
   if (!valid || g != 0) return;
   T* __restrict__ outn = static_cast<T*>(a.out) + n * a.dim_out;
   const A sc = A(a.scale);
@@ -536,18 +530,17 @@ __global__ __launch_bounds__(kBlock) void conv_bwd_fused_kernel(ConvArgs a, Conv
       }
       // grad_sh: sum over the group's channels into the batch tile
       if (!bw.dsh) continue;
-      static_for<0, L + 1>([&](auto L2c) {
-        constexpr int L2 = decltype(L2c)::value;
-        const int yo = a.yoff[L2];
-        if (yo >= 0) {
+      xor_sum_n<NY>(dyl, 1, LG);
+      if (li == 0) {
+        static_for<0, L + 1>([&](auto L2c) {
+          constexpr int L2 = decltype(L2c)::value;
+          const int yo = a.yoff[L2];
+          if (yo >= 0) {
 #pragma unroll
-          for (int m = 0; m < 2 * L2 + 1; ++m) {
-            A v = dyl[L2 * L2 + m];
-            for (int off = 1; off < LG; off <<= 1) v += __shfl_xor(v, off, 64);
-            if (li == 0) dsl[kk * a.dim_y + yo + m] += v;
+            for (int m = 0; m < 2 * L2 + 1; ++m) dsl[kk * a.dim_y + yo + m] += dyl[L2 * L2 + m];
           }
-        }
-      });
+        });
+      }
     }
     // the batch's grad_sh rows leave in one coalesced pass
     __syncthreads();

@@ -148,12 +148,33 @@ __device__ __forceinline__ T ldc(const T* p) {
   return r;
 }
 
-// Sum over aligned groups of `width` lanes (width a power of two <= 64);
-// every lane of a group receives the group's total.
-template <typename A>
-__device__ __forceinline__ A group_sum(A v, int width) {
-  for (int off = 1; off < width; off <<= 1) v += __shfl_xor(v, off, 64);
-  return v;
+// Value of v in lane (this lane ^ off) of the wave, for a precomputed byte
+// address (lane ^ off) * 4; the source lane must be active.
+__device__ __forceinline__ float lane_fetch(float v, int addr) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(v)));
+}
+__device__ __forceinline__ double lane_fetch(double v, int addr) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_ds_bpermute(addr, int(b & 0xffffffffll));
+  const int hi = __builtin_amdgcn_ds_bpermute(addr, int(b >> 32));
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+
+// Butterfly sums of N values over lane strides off_begin, 2*off_begin, ...
+// < off_end (powers of two <= 64): with [1, G) every aligned group of G lanes
+// ends with its total in all its lanes. The N exchanges of a step are issued
+// together, so a step costs one exchange latency, not N.
+template <int N, typename A>
+__device__ __forceinline__ void xor_sum_n(A (&v)[N], int off_begin, int off_end) {
+  const int lane = int(threadIdx.x & 63);
+  for (int off = off_begin; off < off_end; off <<= 1) {
+    const int addr = (lane ^ off) << 2;
+    A t[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) t[k] = lane_fetch(v[k], addr);
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] += t[k];
+  }
 }
 
 }  // namespace cgtp

@@ -388,11 +388,20 @@ void tp_bwd_kernel(TPArgs a) {
   // grad_y: sum the row's lanes; lane k % lpr writes component k (adding to
   // what the previous x block's launch wrote, in stream order)
   T* dyr = (a.dy && active) ? static_cast<T*>(a.dy) + row * a.dim_y : nullptr;
-  for (int k = 0; k < a.dim_y; ++k) {
-    A v = group_sum(lds[k * kBlock + threadIdx.x], lpr);
-    if (dyr && lr == (k & (lpr - 1))) {
-      if (a.dy_accum) v += to_acc<A>(dyr[k]);
-      from_acc(dyr[k], v);
+  constexpr int NYB = 8;  // components reduced together
+  for (int k0 = 0; k0 < a.dim_y; k0 += NYB) {
+    A v[NYB];
+#pragma unroll
+    for (int k = 0; k < NYB; ++k) v[k] = k0 + k < a.dim_y ? lds[(k0 + k) * kBlock + threadIdx.x] : A(0);
+    xor_sum_n<NYB>(v, 1, lpr);
+#pragma unroll
+    for (int k = 0; k < NYB; ++k) {
+      const int kk = k0 + k;
+      if (kk < a.dim_y && dyr && lr == (kk & (lpr - 1))) {
+        A o = v[k];
+        if (a.dy_accum) o += to_acc<A>(dyr[kk]);
+        from_acc(dyr[kk], o);
+      }
     }
   }
 }
