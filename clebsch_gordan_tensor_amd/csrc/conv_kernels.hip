@@ -12,18 +12,42 @@ CGTP_CONV_EXTERN(bf16)
 namespace {
 
 // ------------------------------------------------------- backward helpers
-template <typename T, typename A>
+// grad_x[n] = sum of the per-edge partials of n's outgoing edges, in
+// CSR-position order (the transpose). One wave = (node, run of 64*V
+// channels), V channels per lane; the partial rows of eight edges are loaded
+// before they are added, still in that order.
+template <typename T, typename A, int V>
 __global__ __launch_bounds__(kBlock) void dx_gather_kernel(const int32_t* __restrict__ col_ptr,
                                                            const int32_t* __restrict__ eid,
                                                            const A* __restrict__ part, T* __restrict__ dx,
-                                                           int dim_x) {
-  const int64_t n = blockIdx.x;
+                                                           int64_t N, int dim_x, int nchunk) {
+  const int64_t item = int64_t(blockIdx.x) * kWaves + conv_wave_id();
+  const int64_t n = item / nchunk;
+  if (n >= N) return;
+  const int k = (int(item - n * nchunk) * 64 + int(threadIdx.x & 63)) * V;
+  if (k >= dim_x) return;
   const int32_t t0 = col_ptr[n], t1 = col_ptr[n + 1];
-  for (int k = threadIdx.x; k < dim_x; k += kBlock) {
-    A s = A(0);
-    for (int32_t t = t0; t < t1; ++t) s += part[int64_t(eid[t]) * dim_x + k];
-    from_acc(dx[n * dim_x + k], s);
+  A s[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) s[v] = A(0);
+  constexpr int U = 8;
+  int32_t t = t0;
+  for (; t + U <= t1; t += U) {
+    A r[U][V];
+#pragma unroll
+    for (int u = 0; u < U; ++u) VecIO<A, V>::load(part + int64_t(eid[t + u]) * dim_x + k, r[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int v = 0; v < V; ++v) s[v] += r[u][v];
   }
+  for (; t < t1; ++t) {
+    A r[V];
+    VecIO<A, V>::load(part + int64_t(eid[t]) * dim_x + k, r);
+#pragma unroll
+    for (int v = 0; v < V; ++v) s[v] += r[v];
+  }
+  VecIO<T, V>::store(dx + n * dim_x + k, s);
 }
 
 ConvArgs make_conv_args(cgtp_plan_s* plan, const DevTables& t, const cgtp_graph_s* g) {
@@ -82,8 +106,19 @@ void fwd_typed(cgtp_plan_s* plan, ConvArgs a, hipStream_t s) {
 template <typename T>
 void dx_gather(const cgtp_graph_s* g, const void* part, void* dx, int dim_x, hipStream_t s) {
   using A = typename AccOf<T>::type;
-  hipLaunchKernelGGL((dx_gather_kernel<T, A>), dim3(unsigned(g->N)), dim3(kBlock), 0, s, g->col_ptr, g->eid,
-                     static_cast<const A*>(part), static_cast<T*>(dx), dim_x);
+  constexpr int V = sizeof(A) == 8 ? 2 : 4;  // 16-byte partial loads
+  const bool vec = dim_x % V == 0 && aligned_to(part, V * sizeof(A)) && aligned_to(dx, V * sizeof(T));
+  const int width = vec ? V : 1;
+  const int nchunk = (dim_x + 64 * width - 1) / (64 * width);
+  const unsigned grid = unsigned((g->N * nchunk + kWaves - 1) / kWaves);
+  const A* p = static_cast<const A*>(part);
+  T* o = static_cast<T*>(dx);
+  if (vec)
+    hipLaunchKernelGGL((dx_gather_kernel<T, A, V>), dim3(grid), dim3(kBlock), 0, s, g->col_ptr, g->eid, p, o, g->N,
+                       dim_x, nchunk);
+  else
+    hipLaunchKernelGGL((dx_gather_kernel<T, A, 1>), dim3(grid), dim3(kBlock), 0, s, g->col_ptr, g->eid, p, o, g->N,
+                       dim_x, nchunk);
   CGTP_CHECK_HIP(hipGetLastError());
 }
 
