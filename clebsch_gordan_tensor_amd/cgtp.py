@@ -51,6 +51,13 @@ _SIGS = {
     "cgtp_workspace_size": ([_vp, _vp, _c_i64, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "cgtp_sh_forward": ([ctypes.c_int, ctypes.c_int, _c_i64, _vp, _vp, _vp], ctypes.c_int),
     "cgtp_sh_backward": ([ctypes.c_int, ctypes.c_int, _c_i64, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "cgtp_linear_create": ([ctypes.c_char_p, ctypes.c_char_p, ctypes.c_int, ctypes.POINTER(_vp)], ctypes.c_int),
+    "cgtp_linear_destroy": ([_vp], ctypes.c_int),
+    "cgtp_linear_query": ([_vp, _c_i64p, _c_i64p, _c_i64p, _c_i64p], ctypes.c_int),
+    "cgtp_linear_paths": ([_vp, _c_i32p], ctypes.c_int),
+    "cgtp_linear_forward": ([_vp, _c_i64, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "cgtp_linear_backward": ([_vp, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+    "cgtp_linear_workspace_size": ([_vp, _c_i64, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -233,6 +240,76 @@ class Plan:
                                        _ptr(grad_out), _ptr(res[0]), _ptr(res[1]), _ptr(res[2]),
                                        _ptr(ws) if nws else _vp(0), ws.numel() if nws else 0,
                                        _stream(x)), "cgtp_conv_backward")
+        return tuple(res)
+
+
+class Linear:
+    """An equivariant linear map irreps_in -> irreps_out (cgtp_linear_create)."""
+
+    def __init__(self, irreps_in, irreps_out, dtype="f32"):
+        self.irreps_in, self.irreps_out = irreps_in, irreps_out
+        self.dtype_code = _DT[dtype]
+        h = _vp()
+        _check(_lib.cgtp_linear_create(irreps_in.encode(), irreps_out.encode(), self.dtype_code, ctypes.byref(h)),
+               "cgtp_linear_create")
+        self._h = h
+        v = [ctypes.c_int64() for _ in range(4)]
+        _check(_lib.cgtp_linear_query(h, *[ctypes.byref(a) for a in v]), "cgtp_linear_query")
+        self.dim_in, self.dim_out, self.num_paths, self.w_numel = (a.value for a in v)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.cgtp_linear_destroy(h)
+            self._h = None
+
+    @property
+    def torch_dtype(self):
+        return _torch_dtype(self.dtype_code)
+
+    def paths(self):
+        t = np.zeros((self.num_paths, 5), np.int32)
+        _check(_lib.cgtp_linear_paths(self._h, t.ctypes.data_as(_c_i32p)), "cgtp_linear_paths")
+        return t
+
+    def workspace_size(self, B):
+        n = ctypes.c_size_t()
+        _check(_lib.cgtp_linear_workspace_size(self._h, B, ctypes.byref(n)), "cgtp_linear_workspace_size")
+        return n.value
+
+    def forward(self, x, w, out=None):
+        torch = _torch()
+        B = x.shape[0]
+        dt = self.torch_dtype
+        _need(x, (B, self.dim_in), dt, "x")
+        _need(w, (self.w_numel,), dt, "w")
+        if out is None:
+            out = torch.empty((B, self.dim_out), dtype=dt, device=x.device)
+        _need(out, (B, self.dim_out), dt, "out")
+        _check(_lib.cgtp_linear_forward(self._h, B, _ptr(x), _ptr(w), _ptr(out), _stream(x)), "cgtp_linear_forward")
+        return out
+
+    def backward(self, x, w, grad_out, need=(True, True), out=(None, None), ws=None):
+        torch = _torch()
+        B = x.shape[0]
+        dt = self.torch_dtype
+        _need(x, (B, self.dim_in), dt, "x")
+        _need(w, (self.w_numel,), dt, "w")
+        _need(grad_out, (B, self.dim_out), dt, "grad_out")
+        shapes = [(B, self.dim_in), (self.w_numel,)]
+        res = []
+        for k in range(2):
+            if not need[k]:
+                res.append(None)
+                continue
+            t = out[k] if out[k] is not None else torch.empty(shapes[k], dtype=dt, device=x.device)
+            res.append(_need(t, shapes[k], dt, "grad"))
+        nws = self.workspace_size(B) if need[1] else 0
+        if nws and ws is None:
+            ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
+        _check(_lib.cgtp_linear_backward(self._h, B, _ptr(x), _ptr(w), _ptr(grad_out), _ptr(res[0]), _ptr(res[1]),
+                                         _ptr(ws) if nws else _vp(0), ws.numel() if nws else 0, _stream(x)),
+               "cgtp_linear_backward")
         return tuple(res)
 
 

@@ -7,6 +7,7 @@
 
 #include "common.hpp"
 #include "graph.hpp"
+#include "linear.hpp"
 
 namespace cgtp {
 
@@ -245,6 +246,80 @@ cgtp_status cgtp_sh_backward(int lmax, cgtp_dtype dtype, int64_t n, const void* 
     if (n == 0) return;
     need(vec && grad_sh && grad_vec, "NULL tensor");
     sh_backward_launch(lmax, dtype, n, vec, grad_sh, grad_vec, as_stream(stream));
+  });
+}
+
+cgtp_status cgtp_linear_create(const char* irreps_in, const char* irreps_out, cgtp_dtype dtype,
+                               cgtp_linear* out) {
+  return guarded([&] {
+    need(out != nullptr, "NULL out");
+    *out = nullptr;
+    *out = build_linear(irreps_in, irreps_out, dtype);
+  });
+}
+
+cgtp_status cgtp_linear_destroy(cgtp_linear lin) {
+  return guarded([&] {
+    if (!lin) return;
+    free_linear_tables(lin);
+    delete lin;
+  });
+}
+
+cgtp_status cgtp_linear_query(cgtp_linear lin, int64_t* dim_in, int64_t* dim_out, int64_t* num_paths,
+                              int64_t* w_numel) {
+  return guarded([&] {
+    need(lin != nullptr, "NULL linear");
+    if (dim_in) *dim_in = lin->dim_in;
+    if (dim_out) *dim_out = lin->dim_out;
+    if (num_paths) *num_paths = int64_t(lin->paths.size());
+    if (w_numel) *w_numel = lin->w_numel;
+  });
+}
+
+cgtp_status cgtp_linear_paths(cgtp_linear lin, int32_t* t) {
+  return guarded([&] {
+    need(lin != nullptr && t != nullptr, "NULL argument");
+    for (size_t k = 0; k < lin->paths.size(); ++k) {
+      const auto& p = lin->paths[k];
+      const int32_t row[5] = {p.i, p.o, p.l, p.mu, p.mv};
+      std::memcpy(t + 5 * k, row, sizeof(row));
+    }
+  });
+}
+
+cgtp_status cgtp_linear_forward(cgtp_linear lin, int64_t B, const void* x, const void* w, void* out,
+                                void* stream) {
+  return guarded([&] {
+    need(lin != nullptr, "NULL linear");
+    need(B >= 0, "B < 0");
+    if (B == 0 || lin->dim_out == 0) return;
+    need(out && (lin->dim_in == 0 || x) && (lin->w_numel == 0 || w), "NULL tensor");
+    linear_forward_launch(lin, B, x, w, out, as_stream(stream));
+  });
+}
+
+cgtp_status cgtp_linear_backward(cgtp_linear lin, int64_t B, const void* x, const void* w,
+                                 const void* grad_out, void* grad_x, void* grad_w, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  return guarded([&] {
+    need(lin != nullptr, "NULL linear");
+    need(B >= 0, "B < 0");
+    if (grad_x && (B == 0 || lin->dim_in == 0)) grad_x = nullptr;
+    if (!grad_x && !grad_w) return;
+    need(B == 0 || lin->dim_out == 0 || grad_out, "NULL grad_out");
+    need(!grad_x || w, "NULL w");
+    need(!grad_w || B == 0 || x, "NULL x");
+    if (grad_w && linear_backward_ws_bytes(lin, B) > 0) need(ws != nullptr, "NULL workspace");
+    linear_backward_launch(lin, B, x, w, grad_out, grad_x, grad_w, ws, ws_bytes, as_stream(stream));
+  });
+}
+
+cgtp_status cgtp_linear_workspace_size(cgtp_linear lin, int64_t B, size_t* bytes) {
+  return guarded([&] {
+    need(lin != nullptr && bytes != nullptr, "NULL argument");
+    need(B >= 0, "B < 0");
+    *bytes = linear_backward_ws_bytes(lin, B);
   });
 }
 

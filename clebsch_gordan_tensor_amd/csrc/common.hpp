@@ -95,6 +95,8 @@ struct cgtp_plan_s {
 namespace cgtp {
 
 // Planner (plan.cpp).
+// "MxLp + ..." -> blocks, order kept (CGTP_ERR_PARSE on malformed strings).
+std::vector<Irrep> irreps_from_string(const char* s);
 cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const char* mode,
                         cgtp_dtype dtype, cgtp_wkind wkind);
 // Real CG block by the ladder construction, [2l1+1][2l2+1][2l3+1], fp64.

@@ -1,0 +1,390 @@
+// Equivariant linear map (channel mixing) on the matrix cores.
+//
+// What is computed: linear mixing of channels within each irrep type, one of
+// the core operations listed in "E3J: An Efficient and Open-Source Backend for
+// Euclidean Equivariant Operations on GPU and TPU", appendix A.3 (the weights
+// of such learnable layers: MolSSI e3nn course, lesson 03b):
+//   out[z, o, m, v] = sum over paths p = (i, o) of sum_u x[z, i, m, u] W_p[u, v]
+// for every (input block i, output block o) with the same l and parity, W_p
+// stored [u][v] row-major, paths input-major. For one path and one m this is
+// the product of a [rows x u] matrix (row stride dim_in) with W_p: a dense
+// contraction, so it runs on v_mfma_f32_16x16x4_f32 (fp32 products and sums;
+// bf16 storage is widened exactly to fp32 on load).
+//
+// Forward and grad_x share one kernel over "jobs": a job is a run of at most
+// 128 output columns of one block and one m, fed by one or more terms (an A
+// block of the row times a weight matrix read with given strides). A
+// workgroup takes 64 rows of one job; a wave 16 rows x 128 columns (8 MFMA
+// tiles). grad_W = x^T g summed over rows and m: a workgroup takes one row
+// chunk of one (path, 128 x 128 weight tile), a wave 32 weight rows x 128
+// columns; per-chunk partials are added over the chunks in a fixed order by a
+// second kernel (no atomics, bitwise reproducible).
+//
+// MFMA lane layout (checked on the device): lane l supplies A[l % 16][l / 16]
+// and B[l / 16][l % 16] and holds D[4 (l / 16) + r][l % 16], r = 0..3. Within
+// a 16-wide slice of the contraction, lane slot k = l / 16 of step j takes
+// contraction index 4k + j, so each lane reads 4 consecutive A values at once.
+#include <algorithm>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <vector>
+
+#include "device_util.hpp"
+#include "linear.hpp"
+
+namespace cgtp {
+
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+struct LinTerm {  // C[row, n] += sum_k A[row, a_off + k] * W[b_off + k * b_sk + (b_n0 + n) * b_sn]
+  int32_t a_off, K, b_off, b_sk, b_sn, pad0, pad1, pad2;
+};
+struct LinJob {  // output columns c_off .. c_off + n_len of every row; terms t0 .. t1
+  int32_t c_off, n_len, b_n0, t0, t1, pad0, pad1, pad2;
+};
+struct LinDW {  // weight tile [u0, u0 + 128) x [v0, v0 + 128) of one path
+  int32_t x_off, mu, g_off, mv, nm, w_off, u0, v0;
+};
+
+constexpr int kLinThreads = 256;
+constexpr int kLinRows = 64;   // rows per workgroup of the row kernel
+constexpr int kLinCols = 128;  // columns per job
+constexpr int kLinURows = 128;  // weight rows per workgroup of the grad_W kernel
+
+template <typename T>
+__device__ __forceinline__ float ld1(const T* p) {
+  return to_acc<float>(*p);
+}
+
+template <typename T, bool AVEC>
+__global__ __launch_bounds__(kLinThreads) void lin_rows_kernel(const T* __restrict__ A, int64_t lda,
+                                                             const T* __restrict__ W, T* __restrict__ C,
+                                                             int64_t ldcr, int64_t rows,
+                                                             const LinJob* __restrict__ jobs,
+                                                             const LinTerm* __restrict__ terms) {
+  const LinJob jb = ldc(jobs + blockIdx.y);
+  const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
+  const int li = lane & 15, lk = lane >> 4;
+  const int64_t r0 = int64_t(blockIdx.x) * kLinRows + wave * 16;
+  const int64_t arow = r0 + li;
+  const bool row_ok = arow < rows;
+  v4f acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int t = jb.t0; t < jb.t1; ++t) {
+    const LinTerm tm = ldc(terms + t);
+    const T* __restrict__ ar = A + (row_ok ? arow : int64_t(0)) * lda + tm.a_off;
+    const T* __restrict__ wb = W + tm.b_off + int64_t(jb.b_n0) * tm.b_sn;
+    for (int k0 = 0; k0 < tm.K; k0 += 16) {
+      const int ka = k0 + 4 * lk;
+      float a[4];
+      if (AVEC && row_ok && ka + 3 < tm.K) {
+        VecIO<T, 4>::load(ar + ka, a);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = (row_ok && ka + j < tm.K) ? ld1(ar + ka + j) : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kb = ka + j;
+        const T* __restrict__ wk = wb + int64_t(kb) * tm.b_sk;
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+          const int n = tt * 16 + li;
+          const float b = (kb < tm.K && n < jb.n_len) ? ld1(wk + int64_t(n) * tm.b_sn) : 0.f;
+          acc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b, acc[tt], 0, 0, 0);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt) {
+    const int n = tt * 16 + li;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = r0 + 4 * lk + r;
+      if (row < rows && n < jb.n_len) from_acc(C[row * ldcr + jb.c_off + n], acc[tt][r]);
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kLinThreads) void lin_dw_kernel(const T* __restrict__ X, int64_t ldx,
+                                                           const T* __restrict__ G, int64_t ldg,
+                                                           float* __restrict__ part, int64_t w_numel,
+                                                           int64_t rows, int64_t rows_per_chunk,
+                                                           const LinDW* __restrict__ jobs) {
+  const LinDW jb = ldc(jobs + blockIdx.y);
+  const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
+  const int li = lane & 15, lk = lane >> 4;
+  const int64_t z0 = int64_t(blockIdx.x) * rows_per_chunk;
+  const int64_t z1 = z0 + rows_per_chunk < rows ? z0 + rows_per_chunk : rows;
+  const int ub = jb.u0 + 32 * wave;
+  v4f acc[2][8];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[s][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  if (ub < jb.mu) {
+    for (int m = 0; m < jb.nm; ++m) {
+      for (int64_t z = z0; z < z1; z += 4) {
+        const int64_t zr = z + lk;  // this lane's contraction slot is a row
+        const bool ok = zr < z1;
+        const T* __restrict__ xr = X + (ok ? zr : z0) * ldx + jb.x_off + int64_t(m) * jb.mu;
+        const T* __restrict__ gr = G + (ok ? zr : z0) * ldg + jb.g_off + int64_t(m) * jb.mv;
+        float a[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int u = ub + 16 * s + li;
+          a[s] = (ok && u < jb.mu) ? ld1(xr + u) : 0.f;
+        }
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+          const int v = jb.v0 + 16 * tt + li;
+          const float b = (ok && v < jb.mv) ? ld1(gr + v) : 0.f;
+#pragma unroll
+          for (int s = 0; s < 2; ++s) acc[s][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b, acc[s][tt], 0, 0, 0);
+        }
+      }
+    }
+  }
+  float* __restrict__ pc = part + int64_t(blockIdx.x) * w_numel + jb.w_off;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int u = ub + 16 * s + 4 * lk + r, v = jb.v0 + 16 * tt + li;
+        if (u < jb.mu && v < jb.mv) pc[int64_t(u) * jb.mv + v] = acc[s][tt][r];
+      }
+}
+
+// grad_W[j] = sum over chunks c (ascending) of part[c][j]
+template <typename T>
+__global__ __launch_bounds__(kLinThreads) void lin_colsum_kernel(const float* __restrict__ part, T* __restrict__ out,
+                                                               int64_t nchunks, int64_t w_numel) {
+  const int64_t j = int64_t(blockIdx.x) * kLinThreads + threadIdx.x;
+  if (j >= w_numel) return;
+  float s = 0.f;
+  for (int64_t c = 0; c < nchunks; ++c) s += part[c * w_numel + j];
+  from_acc(out[j], s);
+}
+
+struct LinTables {
+  LinJob* fjobs = nullptr;
+  LinTerm* fterms = nullptr;
+  LinJob* xjobs = nullptr;
+  LinTerm* xterms = nullptr;
+  LinDW* wjobs = nullptr;
+  int nf = 0, nx = 0, nw = 0;
+  bool avec_f = true, avec_x = true;  // 4-aligned A offsets (row strides checked per call)
+};
+
+std::mutex g_lin_mu;
+std::map<std::pair<const cgtp_linear_s*, int>, LinTables> g_lin_tables;
+
+template <typename X>
+X* upload(const std::vector<X>& v) {
+  X* p = nullptr;
+  CGTP_CHECK_HIP(hipMalloc(&p, std::max<size_t>(v.size(), 1) * sizeof(X)));
+  if (!v.empty()) CGTP_CHECK_HIP(hipMemcpy(p, v.data(), v.size() * sizeof(X), hipMemcpyHostToDevice));
+  return p;
+}
+
+const LinTables& lin_tables(const cgtp_linear_s* lin) {
+  int dev = 0;
+  CGTP_CHECK_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(g_lin_mu);
+  auto it = g_lin_tables.find({lin, dev});
+  if (it != g_lin_tables.end()) return it->second;
+  LinTables t;
+  std::vector<LinJob> fj, xj;
+  std::vector<LinTerm> ft, xt;
+  std::vector<LinDW> wj;
+  // forward: output block o, component m, column run n0
+  for (size_t o = 0; o < lin->O.size(); ++o) {
+    const int mv = lin->O[o].mul, nm = 2 * lin->O[o].l + 1;
+    for (int m = 0; m < nm; ++m)
+      for (int n0 = 0; n0 < mv; n0 += kLinCols) {
+        LinJob j{int32_t(lin->out_off[o] + int64_t(m) * mv + n0), std::min(kLinCols, mv - n0), n0,
+                 int32_t(ft.size()), 0, 0, 0, 0};
+        for (const auto& p : lin->paths)
+          if (p.o == int(o)) {
+            const int64_t a_off = lin->in_off[size_t(p.i)] + int64_t(m) * p.mu;
+            ft.push_back(LinTerm{int32_t(a_off), p.mu, int32_t(p.w_off), p.mv, 1, 0, 0, 0});
+            t.avec_f = t.avec_f && a_off % 4 == 0;
+          }
+        j.t1 = int32_t(ft.size());
+        fj.push_back(j);
+      }
+  }
+  // grad_x: input block i, component m, column run n0; B[k = v][n = u] = W_p[u][v]
+  for (size_t i = 0; i < lin->I.size(); ++i) {
+    const int mu = lin->I[i].mul, nm = 2 * lin->I[i].l + 1;
+    for (int m = 0; m < nm; ++m)
+      for (int n0 = 0; n0 < mu; n0 += kLinCols) {
+        LinJob j{int32_t(lin->in_off[i] + int64_t(m) * mu + n0), std::min(kLinCols, mu - n0), n0,
+                 int32_t(xt.size()), 0, 0, 0, 0};
+        for (const auto& p : lin->paths)
+          if (p.i == int(i)) {
+            const int64_t a_off = lin->out_off[size_t(p.o)] + int64_t(m) * p.mv;
+            xt.push_back(LinTerm{int32_t(a_off), p.mv, int32_t(p.w_off), 1, p.mv, 0, 0, 0});
+            t.avec_x = t.avec_x && a_off % 4 == 0;
+          }
+        j.t1 = int32_t(xt.size());
+        xj.push_back(j);
+      }
+  }
+  // grad_W: path, weight tile
+  for (const auto& p : lin->paths)
+    for (int u0 = 0; u0 < p.mu; u0 += kLinURows)
+      for (int v0 = 0; v0 < p.mv; v0 += kLinCols)
+        wj.push_back(LinDW{int32_t(lin->in_off[size_t(p.i)]), p.mu, int32_t(lin->out_off[size_t(p.o)]), p.mv,
+                           2 * p.l + 1, int32_t(p.w_off), u0, v0});
+  t.fjobs = upload(fj);
+  t.fterms = upload(ft);
+  t.xjobs = upload(xj);
+  t.xterms = upload(xt);
+  t.wjobs = upload(wj);
+  t.nf = int(fj.size());
+  t.nx = int(xj.size());
+  t.nw = int(wj.size());
+  return g_lin_tables.emplace(std::make_pair(lin, dev), t).first->second;
+}
+
+bool aligned16(const void* p, size_t bytes) { return reinterpret_cast<uintptr_t>(p) % bytes == 0; }
+
+int64_t dw_rows_per_chunk(int64_t B) {
+  int64_t r = std::max<int64_t>(1024, (B + 511) / 512);
+  return (r + 3) / 4 * 4;
+}
+int64_t dw_chunks(int64_t B) { return B == 0 ? 0 : (B + dw_rows_per_chunk(B) - 1) / dw_rows_per_chunk(B); }
+
+template <typename T>
+void rows_launch(const T* A, int64_t lda, const T* W, T* C, int64_t ldc, int64_t rows, const LinJob* jobs,
+                 const LinTerm* terms, int njobs, bool avec, hipStream_t s) {
+  if (rows == 0 || njobs == 0) return;
+  const dim3 grid(unsigned((rows + kLinRows - 1) / kLinRows), unsigned(njobs));
+  if (avec)
+    hipLaunchKernelGGL((lin_rows_kernel<T, true>), grid, dim3(kLinThreads), 0, s, A, lda, W, C, ldc, rows, jobs,
+                       terms);
+  else
+    hipLaunchKernelGGL((lin_rows_kernel<T, false>), grid, dim3(kLinThreads), 0, s, A, lda, W, C, ldc, rows, jobs,
+                       terms);
+  CGTP_CHECK_HIP(hipGetLastError());
+}
+
+template <typename T>
+void forward_typed(const cgtp_linear_s* lin, int64_t B, const void* x, const void* w, void* out, hipStream_t s) {
+  const LinTables& t = lin_tables(lin);
+  const bool avec = t.avec_f && lin->dim_in % 4 == 0 && aligned16(x, 4 * sizeof(T));
+  rows_launch<T>(static_cast<const T*>(x), lin->dim_in, static_cast<const T*>(w), static_cast<T*>(out), lin->dim_out,
+                 B, t.fjobs, t.fterms, t.nf, avec, s);
+}
+
+template <typename T>
+void backward_typed(const cgtp_linear_s* lin, int64_t B, const void* x, const void* w, const void* g, void* dx,
+                    void* dw, void* ws, hipStream_t s) {
+  const LinTables& t = lin_tables(lin);
+  if (dx) {
+    const bool avec = t.avec_x && lin->dim_out % 4 == 0 && aligned16(g, 4 * sizeof(T));
+    rows_launch<T>(static_cast<const T*>(g), lin->dim_out, static_cast<const T*>(w), static_cast<T*>(dx),
+                   lin->dim_in, B, t.xjobs, t.xterms, t.nx, avec, s);
+  }
+  if (dw && lin->w_numel > 0) {
+    const int64_t nch = dw_chunks(B);
+    float* part = static_cast<float*>(ws);
+    if (nch > 0 && t.nw > 0) {
+      hipLaunchKernelGGL((lin_dw_kernel<T>), dim3(unsigned(nch), unsigned(t.nw)), dim3(kLinThreads), 0, s,
+                         static_cast<const T*>(x), lin->dim_in, static_cast<const T*>(g), lin->dim_out, part,
+                         lin->w_numel, B, dw_rows_per_chunk(B), t.wjobs);
+      CGTP_CHECK_HIP(hipGetLastError());
+    }
+    hipLaunchKernelGGL((lin_colsum_kernel<T>), dim3(unsigned((lin->w_numel + kLinThreads - 1) / kLinThreads)),
+                       dim3(kLinThreads), 0, s, part, static_cast<T*>(dw), nch, lin->w_numel);
+    CGTP_CHECK_HIP(hipGetLastError());
+  }
+}
+
+}  // namespace
+
+cgtp_linear_s* build_linear(const char* irreps_in, const char* irreps_out, cgtp_dtype dtype) {
+  if (dtype == CGTP_F64) throw Error{CGTP_ERR_UNSUPPORTED, "linear: fp64 is not supported (fp32, bf16)"};
+  if (dtype != CGTP_F32 && dtype != CGTP_BF16) throw Error{CGTP_ERR_INVALID_ARG, "bad dtype"};
+  auto lin = std::make_unique<cgtp_linear_s>();
+  lin->I = irreps_from_string(irreps_in);
+  lin->O = irreps_from_string(irreps_out);
+  lin->dtype = dtype;
+  int64_t o = 0;
+  for (const Irrep& r : lin->I) {
+    lin->in_off.push_back(o);
+    o += int64_t(r.mul) * (2 * r.l + 1);
+  }
+  lin->dim_in = o;
+  o = 0;
+  for (const Irrep& r : lin->O) {
+    lin->out_off.push_back(o);
+    o += int64_t(r.mul) * (2 * r.l + 1);
+  }
+  lin->dim_out = o;
+  int64_t w = 0;
+  for (size_t i = 0; i < lin->I.size(); ++i)
+    for (size_t k = 0; k < lin->O.size(); ++k)
+      if (lin->I[i].l == lin->O[k].l && lin->I[i].p == lin->O[k].p) {
+        lin->paths.push_back({int(i), int(k), lin->I[i].l, lin->I[i].mul, lin->O[k].mul, w});
+        w += int64_t(lin->I[i].mul) * lin->O[k].mul;
+      }
+  lin->w_numel = w;
+  if (lin->dim_in > INT32_MAX || lin->dim_out > INT32_MAX || w > INT32_MAX)
+    throw Error{CGTP_ERR_UNSUPPORTED, "linear: row or weights too large for 32-bit offsets"};
+  return lin.release();
+}
+
+void free_linear_tables(const cgtp_linear_s* lin) {
+  std::lock_guard<std::mutex> lock(g_lin_mu);
+  int cur = 0;
+  const bool have = hipGetDevice(&cur) == hipSuccess;
+  for (auto it = g_lin_tables.begin(); it != g_lin_tables.end();) {
+    if (it->first.first == lin) {
+      if (hipSetDevice(it->first.second) == hipSuccess) {
+        (void)hipFree(it->second.fjobs);
+        (void)hipFree(it->second.fterms);
+        (void)hipFree(it->second.xjobs);
+        (void)hipFree(it->second.xterms);
+        (void)hipFree(it->second.wjobs);
+      }
+      it = g_lin_tables.erase(it);
+    } else {
+      ++it;
+    }
+  }
+  if (have) (void)hipSetDevice(cur);
+}
+
+void linear_forward_launch(const cgtp_linear_s* lin, int64_t B, const void* x, const void* w, void* out,
+                           hipStream_t s) {
+  if (lin->dtype == CGTP_BF16)
+    forward_typed<bf16>(lin, B, x, w, out, s);
+  else
+    forward_typed<float>(lin, B, x, w, out, s);
+}
+
+void linear_backward_launch(const cgtp_linear_s* lin, int64_t B, const void* x, const void* w, const void* g,
+                            void* dx, void* dw, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (dw && ws_bytes < linear_backward_ws_bytes(lin, B))
+    throw Error{CGTP_ERR_WORKSPACE, "linear backward: workspace too small"};
+  if (lin->dtype == CGTP_BF16)
+    backward_typed<bf16>(lin, B, x, w, g, dx, dw, ws, s);
+  else
+    backward_typed<float>(lin, B, x, w, g, dx, dw, ws, s);
+}
+
+size_t linear_backward_ws_bytes(const cgtp_linear_s* lin, int64_t B) {
+  return size_t(dw_chunks(B)) * size_t(lin->w_numel) * sizeof(float);
+}
+
+}  // namespace cgtp

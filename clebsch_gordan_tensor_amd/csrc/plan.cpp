@@ -123,6 +123,11 @@ std::complex<double> U(int l, int m, int M) {
 
 }  // namespace
 
+std::vector<Irrep> irreps_from_string(const char* s) {
+  if (!s) throw Error{CGTP_ERR_INVALID_ARG, "null irreps"};
+  return parse_irreps(s);
+}
+
 std::vector<double> real_cg_ladder(int l1, int l2, int l3) {
   const int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1, n3 = 2 * l3 + 1;
   const std::vector<double> Cc = complex_cg_ladder(l1, l2, l3);

@@ -78,6 +78,7 @@ typedef enum { CGTP_OP_TP_BACKWARD = 1, CGTP_OP_CONV_BACKWARD = 2 } cgtp_op;
 
 typedef struct cgtp_plan_s* cgtp_plan;
 typedef struct cgtp_graph_s* cgtp_graph;
+typedef struct cgtp_linear_s* cgtp_linear;
 
 /* Largest degree compiled into the kernels for x, y and output blocks. */
 #define CGTP_LMAX 4
@@ -201,6 +202,42 @@ cgtp_status cgtp_sh_forward(int lmax, cgtp_dtype dtype, int64_t n, const void* v
 /* grad_vec[n][3] = d/dvec of sum(grad_sh * Y(vec/|vec|)); zero for a zero vec. */
 cgtp_status cgtp_sh_backward(int lmax, cgtp_dtype dtype, int64_t n, const void* vec,
                              const void* grad_sh, void* grad_vec, void* stream);
+
+/* ------------------------------------------------- equivariant linear map */
+
+/* Channel mixing within irrep types (E3J appendix A.3 lists linear mixing
+ * among the core operations; course lesson 03b on the weights of learnable
+ * layers). Every (input block i, output block o) with the same l and parity
+ * is a path p with a weight matrix W_p [u_i][v_o] (row-major), paths ordered
+ * input-major; for every row z and component m of the block:
+ *   out[z, o, m, v] = sum over paths p = (i, o) of sum_u x[z, i, m, u] W_p[u, v]
+ * No normalisation factor. Output blocks that no input reaches are zero.
+ * Rows of x [B][dim_in] and out [B][dim_out] are ir_mul blocks as above; w is
+ * one shared weight vector [w_numel] = the W_p concatenated in path order.
+ * A fully connected ("uvw") tensor product with y of multiplicity 1 is this
+ * map applied to the path outputs of cgtp_tp_forward with unit weights.
+ * Runs on the matrix cores (fp32 MFMA: fp32 products and sums; bf16 storage
+ * is widened exactly to fp32). dtype: CGTP_F32 or CGTP_BF16 (CGTP_F64 ->
+ * UNSUPPORTED). Errors: PARSE, UNSUPPORTED, INVALID_ARG. */
+cgtp_status cgtp_linear_create(const char* irreps_in, const char* irreps_out, cgtp_dtype dtype,
+                               cgtp_linear* out);
+cgtp_status cgtp_linear_destroy(cgtp_linear lin);
+/* Row sizes, path count and weight count (any pointer may be NULL). */
+cgtp_status cgtp_linear_query(cgtp_linear lin, int64_t* dim_in, int64_t* dim_out, int64_t* num_paths,
+                              int64_t* w_numel);
+/* Host table [num_paths][5]: i, o, l, u_i, v_o. */
+cgtp_status cgtp_linear_paths(cgtp_linear lin, int32_t* host_table);
+/* out [B][dim_out] from x [B][dim_in] and w [w_numel]. B = 0 is a no-op. */
+cgtp_status cgtp_linear_forward(cgtp_linear lin, int64_t B, const void* x, const void* w, void* out,
+                                void* stream);
+/* Reverse mode: grad_x [B][dim_in] = sum_p g_o W_p^T; grad_w [w_numel] = sum
+ * over rows and m of x_i^T g_o per path, summed over row chunks in a fixed
+ * order from partials kept in ws (cgtp_linear_workspace_size bytes; needed
+ * only with grad_w). NULL grad pointers are skipped. Errors: WORKSPACE. */
+cgtp_status cgtp_linear_backward(cgtp_linear lin, int64_t B, const void* x, const void* w,
+                                 const void* grad_out, void* grad_x, void* grad_w, void* ws, size_t ws_bytes,
+                                 void* stream);
+cgtp_status cgtp_linear_workspace_size(cgtp_linear lin, int64_t B, size_t* bytes);
 
 #ifdef __cplusplus
 }

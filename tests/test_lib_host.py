@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 25
     for n in names:
         assert hasattr(cgtp._lib, n), n
     assert sorted(cgtp.EXPORTED) == names
@@ -107,3 +107,28 @@ def test_workspace_sizes():
     # per-row partials + one partial per 256-row chunk, fp32
     assert ps.workspace_size(cgtp.OP_TP_BACKWARD, 4096) == (4096 + 16) * 480 * 4
     assert ps.workspace_size(cgtp.OP_TP_BACKWARD, 0) == 0
+
+
+# ------------------------------------------------------------ linear map plans
+
+@pytest.mark.parametrize("ii,io", [("2x1o+3x1o+1x0e+2x2e", "4x1o+2x0e+1x2o+3x2e"),
+                                   ("128x0e+128x1o+128x2e+128x3o", "128x0e+128x1o+128x2e+128x3o"),
+                                   ("7x0e", "3x0o")])
+def test_linear_paths_equal_oracle(ii, io):
+    from oracle.linear import LinearLayout
+    lin = cgtp.Linear(ii, io)
+    LL = LinearLayout(ii, io)
+    assert (lin.dim_in, lin.dim_out, lin.num_paths, lin.w_numel) == (LL.dim_in, LL.dim_out, len(LL.paths), LL.w_numel)
+    want = [[p["i"], p["o"], p["l"], p["mu"], p["mv"]] for p in LL.paths]
+    assert lin.paths().tolist() == want
+
+
+def test_linear_errors():
+    ERR_INVALID, ERR_PARSE, ERR_UNSUPPORTED = 1, 2, 3
+    assert status_of(lambda: cgtp.Linear("2x1q", "1x1o")) == ERR_PARSE
+    assert status_of(lambda: cgtp.Linear("2x1o", "1x1o", dtype="f64")) == ERR_UNSUPPORTED
+    assert cgtp._lib.cgtp_linear_create(None, None, 0, None) == ERR_INVALID
+    lin = cgtp.Linear("4x0e+2x1o", "3x0e")
+    assert lin.workspace_size(0) == 0
+    assert lin.workspace_size(1000) == 12 * 4          # one row chunk of partials
+    assert lin.workspace_size(10 ** 6) > 0
