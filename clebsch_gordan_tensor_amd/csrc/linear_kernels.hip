@@ -14,7 +14,7 @@
 // Forward and grad_x share one kernel over "jobs": a job is a run of at most
 // 128 output columns of one block and one m, fed by one or more terms (an A
 // block of the row times a weight matrix read with given strides). A
-// workgroup takes 64 rows of one job; a wave 16 rows x 128 columns (8 MFMA
+// workgroup takes 128 rows of one job; a wave 32 rows x 128 columns (16 MFMA
 // tiles). grad_W = x^T g summed over rows and m: a workgroup takes one row
 // chunk of one (path, 128 x 128 weight tile), a wave 32 weight rows x 128
 // columns; per-chunk partials are added over the chunks in a fixed order by a
@@ -50,7 +50,7 @@ struct LinDW {  // weight tile [u0, u0 + 128) x [v0, v0 + 128) of one path
 };
 
 constexpr int kLinThreads = 256;
-constexpr int kLinRows = 64;   // rows per workgroup of the row kernel
+constexpr int kLinRows = 128;  // rows per workgroup of the row kernel (4 waves x 32)
 constexpr int kLinCols = 128;  // columns per job
 constexpr int kLinURows = 128;  // weight rows per workgroup of the grad_W kernel
 
@@ -59,56 +59,106 @@ __device__ __forceinline__ float ld1(const T* p) {
   return to_acc<float>(*p);
 }
 
+// B (the weight matrix of a term) goes through LDS in chunks of 32
+// contraction rows x 128 columns, double-buffered: the next chunk's global
+// loads are in flight while the MFMAs run on the current one.
+constexpr int kKC = 32;          // contraction rows per B chunk
+constexpr int kBP = kLinCols + 4;  // padded LDS row (lanes of 4 k-slots land in different banks)
+
 template <typename T, bool AVEC>
 __global__ __launch_bounds__(kLinThreads) void lin_rows_kernel(const T* __restrict__ A, int64_t lda,
                                                              const T* __restrict__ W, T* __restrict__ C,
                                                              int64_t ldcr, int64_t rows,
                                                              const LinJob* __restrict__ jobs,
                                                              const LinTerm* __restrict__ terms) {
+  __shared__ float bs[2][kKC * kBP];
   const LinJob jb = ldc(jobs + blockIdx.y);
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
   const int li = lane & 15, lk = lane >> 4;
-  const int64_t r0 = int64_t(blockIdx.x) * kLinRows + wave * 16;
-  const int64_t arow = r0 + li;
-  const bool row_ok = arow < rows;
-  v4f acc[8];
+  const int64_t r0 = int64_t(blockIdx.x) * kLinRows + wave * 32;  // two 16-row tiles per wave
+  int64_t arow[2];
+  bool row_ok[2];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < 2; ++s) {
+    arow[s] = r0 + 16 * s + li;
+    row_ok[s] = arow[s] < rows;
+  }
+  v4f acc[2][8];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[s][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  constexpr int PER = kKC * kLinCols / kLinThreads;  // staged values per thread and chunk
   for (int t = jb.t0; t < jb.t1; ++t) {
     const LinTerm tm = ldc(terms + t);
-    const T* __restrict__ ar = A + (row_ok ? arow : int64_t(0)) * lda + tm.a_off;
     const T* __restrict__ wb = W + tm.b_off + int64_t(jb.b_n0) * tm.b_sn;
-    for (int k0 = 0; k0 < tm.K; k0 += 16) {
-      const int ka = k0 + 4 * lk;
-      float a[4];
-      if (AVEC && row_ok && ka + 3 < tm.K) {
-        VecIO<T, 4>::load(ar + ka, a);
-      } else {
+    const bool kfast = tm.b_sk == 1;  // transposed weights: walk k fastest for contiguous reads
+    const int nch = (tm.K + kKC - 1) / kKC;
+    float pre[PER];
+    auto fetch = [&](int c) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a[j] = (row_ok && ka + j < tm.K) ? ld1(ar + ka + j) : 0.f;
+      for (int q = 0; q < PER; ++q) {
+        const int e = int(threadIdx.x) + q * kLinThreads;
+        const int kk = kfast ? (e % kKC) : (e / kLinCols), n = kfast ? (e / kKC) : (e % kLinCols);
+        const int k = c * kKC + kk;
+        pre[q] = (k < tm.K && n < jb.n_len) ? ld1(wb + int64_t(k) * tm.b_sk + int64_t(n) * tm.b_sn) : 0.f;
       }
+    };
+    auto stash = [&](int buf) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kb = ka + j;
-        const T* __restrict__ wk = wb + int64_t(kb) * tm.b_sk;
+      for (int q = 0; q < PER; ++q) {
+        const int e = int(threadIdx.x) + q * kLinThreads;
+        const int kk = kfast ? (e % kKC) : (e / kLinCols), n = kfast ? (e / kKC) : (e % kLinCols);
+        bs[buf][kk * kBP + n] = pre[q];
+      }
+    };
+    __syncthreads();  // the previous term's last chunk is consumed
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+      if (c + 1 < nch) fetch(c + 1);
+      const float* __restrict__ bc = bs[c & 1];
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-          const int n = tt * 16 + li;
-          const float b = (kb < tm.K && n < jb.n_len) ? ld1(wk + int64_t(n) * tm.b_sn) : 0.f;
-          acc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b, acc[tt], 0, 0, 0);
+      for (int k16 = 0; k16 < kKC; k16 += 16) {
+        const int ka = c * kKC + k16 + 4 * lk;
+        float a[2][4];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const T* __restrict__ ar = A + (row_ok[s] ? arow[s] : int64_t(0)) * lda + tm.a_off;
+          if (AVEC && row_ok[s] && ka + 3 < tm.K) {
+            VecIO<T, 4>::load(ar + ka, a[s]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a[s][j] = (row_ok[s] && ka + j < tm.K) ? ld1(ar + ka + j) : 0.f;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float* __restrict__ br = bc + (k16 + 4 * lk + j) * kBP + li;
+#pragma unroll
+          for (int tt = 0; tt < 8; ++tt) {
+            const float b = br[tt * 16];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) acc[s][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s][j], b, acc[s][tt], 0, 0, 0);
+          }
         }
       }
+      if (c + 1 < nch) stash((c + 1) & 1);
+      __syncthreads();
     }
   }
 #pragma unroll
-  for (int tt = 0; tt < 8; ++tt) {
-    const int n = tt * 16 + li;
+  for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = r0 + 4 * lk + r;
-      if (row < rows && n < jb.n_len) from_acc(C[row * ldcr + jb.c_off + n], acc[tt][r]);
+    for (int tt = 0; tt < 8; ++tt) {
+      const int n = tt * 16 + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = r0 + 16 * s + 4 * lk + r;
+        if (row < rows && n < jb.n_len) from_acc(C[row * ldcr + jb.c_off + n], acc[s][tt][r]);
+      }
     }
-  }
 }
 
 template <typename T>
@@ -129,25 +179,34 @@ __global__ __launch_bounds__(kLinThreads) void lin_dw_kernel(const T* __restrict
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[s][t] = v4f{0.f, 0.f, 0.f, 0.f};
   if (ub < jb.mu) {
+    constexpr int QU = 4;  // row quads whose operands are loaded before their MFMAs run
     for (int m = 0; m < jb.nm; ++m) {
-      for (int64_t z = z0; z < z1; z += 4) {
-        const int64_t zr = z + lk;  // this lane's contraction slot is a row
-        const bool ok = zr < z1;
-        const T* __restrict__ xr = X + (ok ? zr : z0) * ldx + jb.x_off + int64_t(m) * jb.mu;
-        const T* __restrict__ gr = G + (ok ? zr : z0) * ldg + jb.g_off + int64_t(m) * jb.mv;
-        float a[2];
+      for (int64_t zq = z0; zq < z1; zq += 4 * QU) {
+        float a[QU][2], b[QU][8];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int u = ub + 16 * s + li;
-          a[s] = (ok && u < jb.mu) ? ld1(xr + u) : 0.f;
+        for (int q = 0; q < QU; ++q) {
+          const int64_t zr = zq + 4 * q + lk;  // this lane's contraction slot is a row
+          const bool ok = zr < z1;
+          const T* __restrict__ xr = X + (ok ? zr : z0) * ldx + jb.x_off + int64_t(m) * jb.mu;
+          const T* __restrict__ gr = G + (ok ? zr : z0) * ldg + jb.g_off + int64_t(m) * jb.mv;
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const int u = ub + 16 * s + li;
+            a[q][s] = (ok && u < jb.mu) ? ld1(xr + u) : 0.f;
+          }
+#pragma unroll
+          for (int tt = 0; tt < 8; ++tt) {
+            const int v = jb.v0 + 16 * tt + li;
+            b[q][tt] = (ok && v < jb.mv) ? ld1(gr + v) : 0.f;
+          }
         }
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-          const int v = jb.v0 + 16 * tt + li;
-          const float b = (ok && v < jb.mv) ? ld1(gr + v) : 0.f;
+        for (int q = 0; q < QU; ++q)
 #pragma unroll
-          for (int s = 0; s < 2; ++s) acc[s][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b, acc[s][tt], 0, 0, 0);
-        }
+          for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+              acc[s][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q][s], b[q][tt], acc[s][tt], 0, 0, 0);
       }
     }
   }
