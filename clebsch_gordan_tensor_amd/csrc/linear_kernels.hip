@@ -59,10 +59,10 @@ __device__ __forceinline__ float ld1(const T* p) {
   return to_acc<float>(*p);
 }
 
-// B (the weight matrix of a term) goes through LDS in chunks of 32
+// B (the weight matrix of a term) goes through LDS in chunks of 16
 // contraction rows x 128 columns, double-buffered: the next chunk's global
 // loads are in flight while the MFMAs run on the current one.
-constexpr int kKC = 32;          // contraction rows per B chunk
+constexpr int kKC = 16;          // contraction rows per B chunk
 constexpr int kBP = kLinCols + 4;  // padded LDS row (lanes of 4 k-slots land in different banks)
 
 template <typename T, bool AVEC>
@@ -112,39 +112,58 @@ __global__ __launch_bounds__(kLinThreads) void lin_rows_kernel(const T* __restri
         bs[buf][kk * kBP + n] = pre[q];
       }
     };
+    // this lane's A values of one chunk: [k16 half][row tile][4 consecutive k]
+    auto load_a = [&](int c, float (&a)[kKC / 16][2][4]) {
+#pragma unroll
+      for (int h = 0; h < kKC / 16; ++h) {
+        const int ka = c * kKC + 16 * h + 4 * lk;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const T* __restrict__ ar = A + (row_ok[s2] ? arow[s2] : int64_t(0)) * lda + tm.a_off;
+          if (AVEC && row_ok[s2] && ka + 3 < tm.K) {
+            VecIO<T, 4>::load(ar + ka, a[h][s2]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a[h][s2][j] = (row_ok[s2] && ka + j < tm.K) ? ld1(ar + ka + j) : 0.f;
+          }
+        }
+      }
+    };
     __syncthreads();  // the previous term's last chunk is consumed
+    float ac[kKC / 16][2][4], an[kKC / 16][2][4];
     fetch(0);
+    load_a(0, ac);
     stash(0);
     __syncthreads();
     for (int c = 0; c < nch; ++c) {
-      if (c + 1 < nch) fetch(c + 1);
+      if (c + 1 < nch) {  // next chunk's operands in flight during this chunk's MFMAs
+        fetch(c + 1);
+        load_a(c + 1, an);
+      }
       const float* __restrict__ bc = bs[c & 1];
 #pragma unroll
-      for (int k16 = 0; k16 < kKC; k16 += 16) {
-        const int ka = c * kKC + k16 + 4 * lk;
-        float a[2][4];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const T* __restrict__ ar = A + (row_ok[s] ? arow[s] : int64_t(0)) * lda + tm.a_off;
-          if (AVEC && row_ok[s] && ka + 3 < tm.K) {
-            VecIO<T, 4>::load(ar + ka, a[s]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) a[s][j] = (row_ok[s] && ka + j < tm.K) ? ld1(ar + ka + j) : 0.f;
-          }
-        }
+      for (int h = 0; h < kKC / 16; ++h) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float* __restrict__ br = bc + (k16 + 4 * lk + j) * kBP + li;
+          const float* __restrict__ br = bc + (16 * h + 4 * lk + j) * kBP + li;
 #pragma unroll
           for (int tt = 0; tt < 8; ++tt) {
             const float b = br[tt * 16];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) acc[s][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s][j], b, acc[s][tt], 0, 0, 0);
+            for (int s2 = 0; s2 < 2; ++s2)
+              acc[s2][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ac[h][s2][j], b, acc[s2][tt], 0, 0, 0);
           }
         }
       }
-      if (c + 1 < nch) stash((c + 1) & 1);
+      if (c + 1 < nch) {
+        stash((c + 1) & 1);
+#pragma unroll
+        for (int h = 0; h < kKC / 16; ++h)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ac[h][s2][j] = an[h][s2][j];
+      }
       __syncthreads();
     }
   }
