@@ -15,7 +15,8 @@ of x, y and w), with every input already resident in HBM. `value` is rows
 Besides the headline line's `roofline` (dominant kernel, algorithmic bytes per
 call over its mean HIP-event duration against 8 TB/s) and `cpu_baseline` (the
 fp64 oracle on a bounded sample, on the host cores), `extra` carries the
-per-kernel figures, the same workload in bf16 storage and, unless --no-conv,
+per-kernel figures, the same workload in bf16 storage, the equivariant linear
+map on the same rows (matrix cores) and, unless --no-conv,
 the fused convolution (forward and backward, fp32) on the 1000- and
 8000-molecule water boxes (the latter with the harmonics forward/backward of
 the force chain) and the 100,000-point uniform cloud.
@@ -34,7 +35,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "TP pairs/s + conv edges/s (fwd, fwd+bwd) as HBM GB/s and % of MI355X peak"
 PROFILES = os.path.join(ROOT, "profiles")
-WORKLOADS = ["tp_large", "tp_large_bf16", "conv_water1k", "conv_water8k", "conv_uniform100k"]
+WORKLOADS = ["tp_large", "tp_large_bf16", "conv_water1k", "conv_water8k", "conv_uniform100k", "linear_large",
+             "linear_large_bf16"]
+MFMA_FP32_PEAK_TFS = 157.3
 
 
 def parse():
@@ -208,7 +211,40 @@ class ConvWorkload:
         return 4 * (2 * p.w_numel + 2 * p.dim_y + 1) * self.E + 4 * (p.dim_out + 2 * p.dim_x + 1) * self.N
 
 
+class LinearWorkload:
+    """Equivariant linear map on the tensor-product rows: 2^20 rows of
+    128x(0e+1o+2e+3o) -> the same irreps (4 paths of 128 x 128 weights)."""
+
+    def __init__(self, torch, cgtp, synth, dtype):
+        irreps = synth.CONFIGS["tp_large"]["irreps_x"]
+        self.B = B = synth.CONFIGS["tp_large"]["B"]
+        self.lin = lin = cgtp.Linear(irreps, irreps, dtype=dtype)
+        td = torch.float32 if dtype == "f32" else torch.bfloat16
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(0)
+        self.x = torch.randn((B, lin.dim_in), generator=gen, device="cuda").to(td)
+        self.w = (torch.randn(lin.w_numel, generator=gen, device="cuda") / math.sqrt(128.0)).to(td)
+        self.g = torch.randn((B, lin.dim_out), generator=gen, device="cuda").to(td)
+        self.out = torch.empty((B, lin.dim_out), device="cuda", dtype=td)
+        self.dx, self.dw = torch.empty_like(self.x), torch.empty_like(self.w)
+        self.ws = torch.empty(lin.workspace_size(B), dtype=torch.uint8, device="cuda")
+        self.es = 4 if dtype == "f32" else 2
+        # 2 u v flops per (row, component) and path
+        self.flops = 2 * B * sum((2 * int(l) + 1) * int(mu) * int(mv) for _, _, l, mu, mv in lin.paths())
+
+    def fwd(self):
+        self.lin.forward(self.x, self.w, out=self.out)
+
+    def bwd_x(self):
+        self.lin.backward(self.x, self.w, self.g, need=(True, False), out=(self.dx, None))
+
+    def bwd_w(self):
+        self.lin.backward(self.x, self.w, self.g, need=(False, True), out=(None, self.dw), ws=self.ws)
+
+
 def make_workload(torch, cgtp, synth, name):
+    if name.startswith("linear"):
+        return LinearWorkload(torch, cgtp, synth, "bf16" if name.endswith("bf16") else "f32")
     if name == "tp_large":
         return TPWorkload(torch, cgtp, synth, "f32")
     if name == "tp_large_bf16":
@@ -219,14 +255,18 @@ def make_workload(torch, cgtp, synth, name):
 def profile(torch, cgtp, synth, name):
     """Three calls of every operation of one workload (the first one warms up)."""
     wl = make_workload(torch, cgtp, synth, name)
-    ops = [wl.sh, wl.fwd, wl.bwd] if name.startswith("tp") else [wl.sh_fwd, wl.fwd, wl.bwd, wl.sh_bwd]
+    if name.startswith("linear"):
+        ops = [wl.fwd, wl.bwd_x, wl.bwd_w]
+    else:
+        ops = [wl.sh, wl.fwd, wl.bwd] if name.startswith("tp") else [wl.sh_fwd, wl.fwd, wl.bwd, wl.sh_bwd]
     for _ in range(3):
         for op in ops:
             op()
     torch.cuda.synchronize()
-    units = wl.B if name.startswith("tp") else wl.E
+    rowwise = name.startswith("tp") or name.startswith("linear")
+    units = wl.B if rowwise else wl.E
     print(json.dumps({"profiled": name, "calls": 3, "units": units,
-                      "unit": "row" if name.startswith("tp") else "edge"}), flush=True)
+                      "unit": "row" if rowwise else "edge"}), flush=True)
 
 
 # ------------------------------------------------------------------ benches
@@ -345,6 +385,33 @@ def conv_bench(args, torch, cgtp, synth, name, steps, forces=False):
     return res
 
 
+def linear_bench(args, torch, cgtp, synth, dtype):
+    """Equivariant linear map (fp32 MFMA) on the tensor-product rows: call times,
+    TFLOP/s against the fp32 matrix-core peak, and algorithmic GB/s."""
+    wl = LinearWorkload(torch, cgtp, synth, dtype)
+    B = wl.B
+    tf, tx, tw = KernelTimer(torch), KernelTimer(torch), KernelTimer(torch)
+    wl.fwd()
+    wl.bwd_x()
+    wl.bwd_w()
+    for _ in range(3):
+        tf(wl.fwd)
+        tx(wl.bwd_x)
+        tw(wl.bwd_w)
+    torch.cuda.synchronize()
+    res = {"rows": B, "irreps": "128x0e+128x1o+128x2e+128x3o -> same", "flops_per_call": wl.flops}
+    dim = wl.lin.dim_in
+    for key, t, nbytes in (("fwd", tf, wl.es * B * 2 * dim), ("bwd_x", tx, wl.es * B * 2 * dim),
+                           ("bwd_w", tw, wl.es * B * 2 * dim)):
+        ms = t.mean_ms()
+        tfs = wl.flops / (ms * 1e-3) / 1e12
+        res[key] = dict(ms=round(ms, 3), TFLOPs=round(tfs, 1), frac_of_fp32_mfma_peak=round(tfs / MFMA_FP32_PEAK_TFS, 3),
+                        algorithmic_GBs=round(nbytes / (ms * 1e-3) / 1e9, 1))
+    del wl
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(args, synth):
     """The oracle as it stands, tp_large fwd+bwd on a bounded row sample."""
     from oracle import sh as osh
@@ -391,6 +458,8 @@ def main():
     extra = {"device": torch.cuda.get_device_name(0)}
     value, ms_step, roofline, plan = tp_large_bench(args, torch, cgtp, synth, extra)
     extra["tp_large_bf16"] = tp_large_bf16(args, torch, cgtp, synth)
+    extra["linear_large"] = linear_bench(args, torch, cgtp, synth, "f32")
+    extra["linear_large_bf16"] = linear_bench(args, torch, cgtp, synth, "bf16")
     if not args.no_conv:
         for name in ("conv_water1k", "conv_water8k", "conv_uniform100k"):
             extra[name] = conv_bench(args, torch, cgtp, synth, name, max(2, min(args.steps, 5)),

@@ -59,6 +59,35 @@ __device__ __forceinline__ float ld1(const T* p) {
   return to_acc<float>(*p);
 }
 
+// Guarded load as an unconditional load of an in-bounds element (the caller
+// clamps the index) followed by a select: a load under a branch would be
+// waited for before the next one is issued.
+template <typename T>
+__device__ __forceinline__ float ld_sel(const T* p, bool ok) {
+  const float v = ld1(p);
+  return ok ? v : 0.f;
+}
+
+// Four consecutive elements of one row, as stored; widened to fp32 at use.
+template <typename T>
+struct Quad;
+template <>
+struct Quad<float> {
+  typedef float V __attribute__((ext_vector_type(4)));
+  V v;
+  __device__ static __forceinline__ Quad load4(const float* p) { return Quad{*reinterpret_cast<const V*>(p)}; }
+  __device__ __forceinline__ void set(int j, const float* p) { v[j] = *p; }
+  __device__ __forceinline__ float get(int j) const { return v[j]; }
+};
+template <>
+struct Quad<bf16> {
+  typedef uint16_t V __attribute__((ext_vector_type(4)));
+  V v;
+  __device__ static __forceinline__ Quad load4(const bf16* p) { return Quad{*reinterpret_cast<const V*>(p)}; }
+  __device__ __forceinline__ void set(int j, const bf16* p) { v[j] = p->bits; }
+  __device__ __forceinline__ float get(int j) const { return bf16_to_f32(v[j]); }
+};
+
 // B (the weight matrix of a term) goes through LDS in chunks of 16
 // contraction rows x 128 columns, double-buffered: the next chunk's global
 // loads are in flight while the MFMAs run on the current one.
@@ -94,55 +123,74 @@ __global__ __launch_bounds__(kLinThreads) void lin_rows_kernel(const T* __restri
     const T* __restrict__ wb = W + tm.b_off + int64_t(jb.b_n0) * tm.b_sn;
     const bool kfast = tm.b_sk == 1;  // transposed weights: walk k fastest for contiguous reads
     const int nch = (tm.K + kKC - 1) / kKC;
-    float pre[PER];
+    // B chunk staging: fetch() requests the elements as stored (clamped
+    // in-bounds indexes, nothing depends on the loads yet), stash() widens,
+    // masks and writes them to LDS.
+    T pre[PER];
     auto fetch = [&](int c) {
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
         const int e = int(threadIdx.x) + q * kLinThreads;
         const int kk = kfast ? (e % kKC) : (e / kLinCols), n = kfast ? (e / kKC) : (e % kLinCols);
         const int k = c * kKC + kk;
-        pre[q] = (k < tm.K && n < jb.n_len) ? ld1(wb + int64_t(k) * tm.b_sk + int64_t(n) * tm.b_sn) : 0.f;
+        pre[q] = wb[int64_t(k < tm.K ? k : 0) * tm.b_sk + int64_t(n < jb.n_len ? n : 0) * tm.b_sn];
       }
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](int c, int buf) {
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
         const int e = int(threadIdx.x) + q * kLinThreads;
         const int kk = kfast ? (e % kKC) : (e / kLinCols), n = kfast ? (e / kKC) : (e % kLinCols);
-        bs[buf][kk * kBP + n] = pre[q];
+        const bool ok = c * kKC + kk < tm.K && n < jb.n_len;
+        bs[buf][kk * kBP + n] = ok ? ld1(&pre[q]) : 0.f;
       }
     };
-    // this lane's A values of one chunk: [k16 half][row tile][4 consecutive k]
-    auto load_a = [&](int c, float (&a)[kKC / 16][2][4]) {
+    // This lane's A elements of one chunk, [k16 half][row tile] x 4 consecutive
+    // k, kept as loaded (no dependent instruction, so the loads stay in flight
+    // during the previous chunk's MFMAs) and widened and masked at use. Rows
+    // past the end read row 0 (their results are not stored: row i of an MFMA
+    // product depends on row i of A only); k past K reads element 0 and is
+    // masked to zero at use.
+    auto load_a = [&](int c, Quad<T> (&a)[kKC / 16][2]) {
 #pragma unroll
       for (int h = 0; h < kKC / 16; ++h) {
         const int ka = c * kKC + 16 * h + 4 * lk;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const T* __restrict__ ar = A + (row_ok[s2] ? arow[s2] : int64_t(0)) * lda + tm.a_off;
-          if (AVEC && row_ok[s2] && ka + 3 < tm.K) {
-            VecIO<T, 4>::load(ar + ka, a[h][s2]);
+          if (AVEC) {
+            a[h][s2] = Quad<T>::load4(ar + (ka < tm.K ? ka : 0));
           } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) a[h][s2][j] = (row_ok[s2] && ka + j < tm.K) ? ld1(ar + ka + j) : 0.f;
+            for (int j = 0; j < 4; ++j) a[h][s2].set(j, ar + (ka + j < tm.K ? ka + j : 0));
           }
         }
       }
     };
     __syncthreads();  // the previous term's last chunk is consumed
-    float ac[kKC / 16][2][4], an[kKC / 16][2][4];
+    // Per chunk: the next chunk's operands are requested first, without a
+    // condition (past the last chunk the clamped requests read in-bounds
+    // elements that are masked to zero and never used; a conditional request
+    // could be moved behind the MFMAs by the compiler), the MFMAs run on the
+    // current chunk, then the next B chunk goes to the other LDS buffer.
+    Quad<T> ac[kKC / 16][2], an[kKC / 16][2];
     fetch(0);
     load_a(0, ac);
-    stash(0);
+    stash(0, 0);
     __syncthreads();
     for (int c = 0; c < nch; ++c) {
-      if (c + 1 < nch) {  // next chunk's operands in flight during this chunk's MFMAs
-        fetch(c + 1);
-        load_a(c + 1, an);
-      }
+      fetch(c + 1);
+      load_a(c + 1, an);
+      __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the MFMAs
       const float* __restrict__ bc = bs[c & 1];
 #pragma unroll
       for (int h = 0; h < kKC / 16; ++h) {
+        const int ka = c * kKC + 16 * h + 4 * lk;
+        float av[2][4];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) av[s2][j] = ka + j < tm.K ? ac[h][s2].get(j) : 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float* __restrict__ br = bc + (16 * h + 4 * lk + j) * kBP + li;
@@ -151,19 +199,16 @@ __global__ __launch_bounds__(kLinThreads) void lin_rows_kernel(const T* __restri
             const float b = br[tt * 16];
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
-              acc[s2][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ac[h][s2][j], b, acc[s2][tt], 0, 0, 0);
+              acc[s2][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s2][j], b, acc[s2][tt], 0, 0, 0);
           }
         }
       }
-      if (c + 1 < nch) {
-        stash((c + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);  // the requests complete behind the MFMAs
+      stash(c + 1, (c + 1) & 1);
 #pragma unroll
-        for (int h = 0; h < kKC / 16; ++h)
+      for (int h = 0; h < kKC / 16; ++h)
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ac[h][s2][j] = an[h][s2][j];
-      }
+        for (int s2 = 0; s2 < 2; ++s2) ac[h][s2] = an[h][s2];
       __syncthreads();
     }
   }
@@ -211,12 +256,12 @@ __global__ __launch_bounds__(kLinThreads) void lin_dw_kernel(const T* __restrict
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
             const int u = ub + 16 * s + li;
-            a[q][s] = (ok && u < jb.mu) ? ld1(xr + u) : 0.f;
+            a[q][s] = ld_sel(xr + (u < jb.mu ? u : 0), ok && u < jb.mu);
           }
 #pragma unroll
           for (int tt = 0; tt < 8; ++tt) {
             const int v = jb.v0 + 16 * tt + li;
-            b[q][tt] = (ok && v < jb.mv) ? ld1(gr + v) : 0.f;
+            b[q][tt] = ld_sel(gr + (v < jb.mv ? v : 0), ok && v < jb.mv);
           }
         }
 #pragma unroll
@@ -259,7 +304,7 @@ struct LinTables {
   LinTerm* xterms = nullptr;
   LinDW* wjobs = nullptr;
   int nf = 0, nx = 0, nw = 0;
-  bool avec_f = true, avec_x = true;  // 4-aligned A offsets (row strides checked per call)
+  bool avec_f = true, avec_x = true;  // 4-aligned A offsets and K (row strides checked per call)
 };
 
 std::mutex g_lin_mu;
@@ -294,7 +339,7 @@ const LinTables& lin_tables(const cgtp_linear_s* lin) {
           if (p.o == int(o)) {
             const int64_t a_off = lin->in_off[size_t(p.i)] + int64_t(m) * p.mu;
             ft.push_back(LinTerm{int32_t(a_off), p.mu, int32_t(p.w_off), p.mv, 1, 0, 0, 0});
-            t.avec_f = t.avec_f && a_off % 4 == 0;
+            t.avec_f = t.avec_f && a_off % 4 == 0 && p.mu % 4 == 0;
           }
         j.t1 = int32_t(ft.size());
         fj.push_back(j);
@@ -311,7 +356,7 @@ const LinTables& lin_tables(const cgtp_linear_s* lin) {
           if (p.i == int(i)) {
             const int64_t a_off = lin->out_off[size_t(p.o)] + int64_t(m) * p.mv;
             xt.push_back(LinTerm{int32_t(a_off), p.mv, int32_t(p.w_off), 1, p.mv, 0, 0, 0});
-            t.avec_x = t.avec_x && a_off % 4 == 0;
+            t.avec_x = t.avec_x && a_off % 4 == 0 && p.mv % 4 == 0;
           }
         j.t1 = int32_t(xt.size());
         xj.push_back(j);
