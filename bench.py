@@ -401,12 +401,15 @@ def linear_bench(args, torch, cgtp, synth, dtype):
     torch.cuda.synchronize()
     res = {"rows": B, "irreps": "128x0e+128x1o+128x2e+128x3o -> same", "flops_per_call": wl.flops}
     dim = wl.lin.dim_in
-    for key, t, nbytes in (("fwd", tf, wl.es * B * 2 * dim), ("bwd_x", tx, wl.es * B * 2 * dim),
-                           ("bwd_w", tw, wl.es * B * 2 * dim)):
+    wname = "linear_large" if dtype == "f32" else "linear_large_bf16"
+    for key, t, nbytes, kern in (("fwd", tf, wl.es * B * 2 * dim, "lin_rows_kernel"),
+                                 ("bwd_x", tx, wl.es * B * 2 * dim, "lin_rows_kernel"),
+                                 ("bwd_w", tw, wl.es * B * 2 * dim, "lin_dw_kernel")):
         ms = t.mean_ms()
         tfs = wl.flops / (ms * 1e-3) / 1e12
-        res[key] = dict(ms=round(ms, 3), TFLOPs=round(tfs, 1), frac_of_fp32_mfma_peak=round(tfs / MFMA_FP32_PEAK_TFS, 3),
-                        algorithmic_GBs=round(nbytes / (ms * 1e-3) / 1e9, 1))
+        res[key] = dict(kernel=kern, ms=round(ms, 3), TFLOPs=round(tfs, 1),
+                        frac_of_fp32_mfma_peak=round(tfs / MFMA_FP32_PEAK_TFS, 3),
+                        algorithmic_GBs=round(nbytes / (ms * 1e-3) / 1e9, 1), traffic=traffic_for(kern, wname, B))
     del wl
     torch.cuda.empty_cache()
     return res
