@@ -52,7 +52,10 @@ def dim(irreps):
     return sum(block_dims(irreps))
 
 
-def paths_uvu(irreps_x, irreps_y, irreps_out):
+SELECTIONS = ("all", "symmetric", "skew")
+
+
+def paths_uvu(irreps_x, irreps_y, irreps_out, select="all"):
     """Enumerate the uvu paths of the full tensor product.
 
     For every x block i1, every y block i2 and every l3 in |l1-l2| ... l1+l2
@@ -62,8 +65,15 @@ def paths_uvu(irreps_x, irreps_y, irreps_out):
     Order: i1, then i2, then l3 ascending. One output block per path, not
     collapsed (collapsing by degree is a separate comparison mode in [E3J] B.1).
 
+    ``select`` keeps a parity class of paths ([E3J] B.1: the Gaunt product
+    covers the symmetric paths, the vector signal product the skew-symmetric
+    ones, and e3j picks the matching paths by parity): "symmetric" keeps
+    l1 + l2 + l3 even, "skew" keeps it odd, "all" keeps every path.
+
     Returns a list of dicts with keys i1, i2, l1, l2, l3, p3, mul.
     """
+    if select not in SELECTIONS:
+        raise ValueError("select must be one of %s" % (SELECTIONS,))
     X, Y, O = parse_irreps(irreps_x), parse_irreps(irreps_y), parse_irreps(irreps_out)
     allowed = {(l, p) for _, l, p in O}
     for mul, _, _ in Y:
@@ -74,6 +84,8 @@ def paths_uvu(irreps_x, irreps_y, irreps_out):
         for i2, (_, l2, p2) in enumerate(Y):
             for l3 in range(abs(l1 - l2), l1 + l2 + 1):
                 p3 = p1 * p2
+                if select != "all" and ((l1 + l2 + l3) % 2 == 0) != (select == "symmetric"):
+                    continue
                 if (l3, p3) in allowed:
                     paths.append(dict(i1=i1, i2=i2, l1=l1, l2=l2, l3=l3, p3=p3, mul=u))
     return paths
@@ -85,24 +97,57 @@ class Layout:
     Within a block the layout is [2l+1][mul] (the ir_mul order of [COURSE] 12a:
     the channel index is the fast one). Output blocks follow path order; the
     weights of a row are [path][mul] concatenated.
+
+    With ``collapse`` the paths of one output type are summed into one block
+    ([E3J] B.1 and B.3: outputs collapsed by degree, summing the isomorphic
+    copies of each irreducible output space). Reading taken: one block per
+    (l3, p3) that some path reaches, blocks in the order of irreps_out (first
+    occurrence), multiplicity = that of the x blocks feeding it, which must
+    agree. ``groups`` lists the output blocks as dicts (l3, p3, mul, out_off).
     """
 
-    def __init__(self, irreps_x, irreps_y, irreps_out):
+    def __init__(self, irreps_x, irreps_y, irreps_out, select="all", collapse=False):
         self.X = parse_irreps(irreps_x)
         self.Y = parse_irreps(irreps_y)
-        self.paths = paths_uvu(irreps_x, irreps_y, irreps_out)
+        self.paths = paths_uvu(irreps_x, irreps_y, irreps_out, select)
+        self.select, self.collapse = select, collapse
         self.x_off = block_offsets(self.X)
         self.y_off = block_offsets(self.Y)
         self.dim_x = dim(self.X)
         self.dim_y = dim(self.Y)
-        o = w = 0
+        w = 0
         for p in self.paths:
-            p["out_off"] = o
             p["w_off"] = w
-            o += p["mul"] * (2 * p["l3"] + 1)
             w += p["mul"]
-        self.dim_out = o
         self.w_numel = w
+        self.groups = []
+        if not collapse:
+            o = 0
+            for p in self.paths:
+                p["out_off"] = o
+                self.groups.append(dict(l3=p["l3"], p3=p["p3"], mul=p["mul"], out_off=o))
+                o += p["mul"] * (2 * p["l3"] + 1)
+            self.dim_out = o
+            return
+        order = []
+        for _, l, par in parse_irreps(irreps_out):
+            if (l, par) not in order:
+                order.append((l, par))
+        o = 0
+        for l3, p3 in order:
+            feeding = [p for p in self.paths if (p["l3"], p["p3"]) == (l3, p3)]
+            if not feeding:
+                continue
+            muls = {p["mul"] for p in feeding}
+            if len(muls) != 1:
+                raise ValueError("collapsed output %d%s fed by different multiplicities %s"
+                                 % (l3, "e" if p3 > 0 else "o", sorted(muls)))
+            mul = muls.pop()
+            for p in feeding:
+                p["out_off"] = o
+            self.groups.append(dict(l3=l3, p3=p3, mul=mul, out_off=o))
+            o += mul * (2 * l3 + 1)
+        self.dim_out = o
 
     def x_block(self, x, i):
         """View of block i of x rows as [..., 2l+1, mul]."""

@@ -12,6 +12,9 @@ For every path p = (i1, i2, l3) with x block i1 of multiplicity u:
 ``w`` is either shared, shape [W], or one row per z, shape [B, W], where
 W = sum_p mul_p. Two forward routes are given: explicit loops over the nonzero
 CG entries (``forward``) and one dense einsum per path (``forward_dense``).
+With a collapsed layout several paths share an output block and their
+outputs are added there; in the backward each of them reads that block's
+cotangent.
 """
 
 import numpy as np
@@ -42,7 +45,7 @@ def forward(L, x, y, w):
         for m1, m2, m3 in zip(*np.nonzero(C)):
             ob[:, m3, :] += C[m1, m2, m3] * xb[:, m1, :] * yb[:, m2][:, None]
         ob *= _w_of(L, w, p, B)[:, None, :]
-        L.out_block(out, p)[...] = ob
+        L.out_block(out, p)[...] += ob
     return out
 
 
@@ -57,7 +60,7 @@ def forward_dense(L, x, y, w):
         C = cg_real(p["l1"], p["l2"], p["l3"])
         ob = np.einsum("abc,zau,zb,zu->zcu", C, L.x_block(x, p["i1"]),
                        L.y_block(y, p["i2"]), _w_of(L, w, p, B))
-        L.out_block(out, p)[...] = ob
+        L.out_block(out, p)[...] += ob
     return out
 
 
@@ -90,5 +93,5 @@ def backward(L, x, y, w, g):
     return dx, dy, dw
 
 
-def make_layout(irreps_x, irreps_y, irreps_out):
-    return Layout(irreps_x, irreps_y, irreps_out)
+def make_layout(irreps_x, irreps_y, irreps_out, select="all", collapse=False):
+    return Layout(irreps_x, irreps_y, irreps_out, select, collapse)
