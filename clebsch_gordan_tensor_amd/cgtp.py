@@ -37,6 +37,9 @@ _SIGS = {
     "cgtp_plan_destroy": ([_vp], ctypes.c_int),
     "cgtp_plan_query": ([_vp, _c_i64p, _c_i64p, _c_i64p, _c_i64p, _c_i64p], ctypes.c_int),
     "cgtp_plan_paths": ([_vp, _c_i32p], ctypes.c_int),
+    "cgtp_plan_create_ex": ([ctypes.c_char_p, ctypes.c_char_p, ctypes.c_char_p, ctypes.c_char_p,
+                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(_vp)], ctypes.c_int),
+    "cgtp_plan_outputs": ([_vp, ctypes.POINTER(ctypes.c_int64), _c_i32p], ctypes.c_int),
     "cgtp_plan_cg": ([_vp, ctypes.c_int32, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
     "cgtp_tp_forward": ([_vp, _c_i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "cgtp_tp_backward": ([_vp, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
@@ -116,17 +119,28 @@ def _need(t, shape, dtype, name):
     return t
 
 
-class Plan:
-    """A uvu tensor-product plan (cgtp_plan_create)."""
+_SEL = {"all": 0, "symmetric": 1, "skew": 2}
 
-    def __init__(self, irreps_x, irreps_y, irreps_out, mode="uvu", dtype="f32", wkind="per_row"):
+
+class Plan:
+    """A uvu tensor-product plan (cgtp_plan_create, or cgtp_plan_create_ex for a
+    path selection "symmetric" / "skew" or collapsed outputs)."""
+
+    def __init__(self, irreps_x, irreps_y, irreps_out, mode="uvu", dtype="f32", wkind="per_row",
+                 select="all", collapse=False):
         self.irreps_x, self.irreps_y, self.irreps_out = irreps_x, irreps_y, irreps_out
         self.dtype_code = _DT[dtype]
         self.wkind = _WK[wkind]
+        self.select, self.collapse = select, bool(collapse)
         h = _vp()
-        _check(_lib.cgtp_plan_create(irreps_x.encode(), irreps_y.encode(), irreps_out.encode(),
-                                     mode.encode(), self.dtype_code, self.wkind, ctypes.byref(h)),
-               "cgtp_plan_create")
+        if select == "all" and not collapse:
+            _check(_lib.cgtp_plan_create(irreps_x.encode(), irreps_y.encode(), irreps_out.encode(),
+                                         mode.encode(), self.dtype_code, self.wkind, ctypes.byref(h)),
+                   "cgtp_plan_create")
+        else:
+            _check(_lib.cgtp_plan_create_ex(irreps_x.encode(), irreps_y.encode(), irreps_out.encode(),
+                                            mode.encode(), self.dtype_code, self.wkind, _SEL[select],
+                                            int(bool(collapse)), ctypes.byref(h)), "cgtp_plan_create_ex")
         self._h = h
         v = [ctypes.c_int64() for _ in range(5)]
         _check(_lib.cgtp_plan_query(h, *[ctypes.byref(a) for a in v]), "cgtp_plan_query")
@@ -145,6 +159,14 @@ class Plan:
     def paths(self):
         t = np.zeros((self.num_paths, 6), np.int32)
         _check(_lib.cgtp_plan_paths(self._h, t.ctypes.data_as(_c_i32p)), "cgtp_plan_paths")
+        return t
+
+    def outputs(self):
+        """Output blocks as rows (l3, p3, mul, offset)."""
+        n = ctypes.c_int64()
+        _check(_lib.cgtp_plan_outputs(self._h, ctypes.byref(n), None), "cgtp_plan_outputs")
+        t = np.zeros((n.value, 4), np.int32)
+        _check(_lib.cgtp_plan_outputs(self._h, None, t.ctypes.data_as(_c_i32p)), "cgtp_plan_outputs")
         return t
 
     def cg(self, path):

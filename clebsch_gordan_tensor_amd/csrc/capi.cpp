@@ -75,6 +75,31 @@ cgtp_status cgtp_plan_create(const char* irreps_x, const char* irreps_y, const c
   });
 }
 
+cgtp_status cgtp_plan_create_ex(const char* irreps_x, const char* irreps_y, const char* irreps_out,
+                                const char* mode, cgtp_dtype dtype, cgtp_wkind wkind, cgtp_paths select,
+                                int collapse, cgtp_plan* out) {
+  return guarded([&] {
+    need(out != nullptr, "out handle is NULL");
+    *out = nullptr;
+    *out = build_plan(irreps_x, irreps_y, irreps_out, mode, dtype, wkind, select, collapse != 0);
+  });
+}
+
+cgtp_status cgtp_plan_outputs(cgtp_plan plan, int64_t* num_outputs, int32_t* host_table) {
+  return guarded([&] {
+    need(plan != nullptr, "NULL plan");
+    if (num_outputs) *num_outputs = int64_t(plan->outputs.size());
+    if (!host_table) return;
+    for (size_t k = 0; k < plan->outputs.size(); ++k) {
+      const OutBlock& o = plan->outputs[k];
+      host_table[4 * k + 0] = o.l3;
+      host_table[4 * k + 1] = o.p3;
+      host_table[4 * k + 2] = o.mul;
+      host_table[4 * k + 3] = o.out_off;
+    }
+  });
+}
+
 cgtp_status cgtp_plan_destroy(cgtp_plan plan) {
   return guarded([&] {
     if (!plan) return;
@@ -205,6 +230,7 @@ cgtp_status cgtp_conv_forward(cgtp_plan plan, cgtp_graph graph, const void* x, c
     need(plan != nullptr && graph != nullptr, "NULL plan or graph");
     if (plan->wkind != CGTP_W_PER_ROW)
       throw Error{CGTP_ERR_UNSUPPORTED, "the convolution needs per-edge weights (CGTP_W_PER_ROW)"};
+    if (plan->collapse) throw Error{CGTP_ERR_UNSUPPORTED, "the convolution does not take collapsed outputs"};
     if (graph->N == 0) return;
     need(out != nullptr, "out is NULL");
     need(graph->E == 0 || (x && sh && w), "NULL input tensor");
@@ -219,6 +245,7 @@ cgtp_status cgtp_conv_backward(cgtp_plan plan, cgtp_graph graph, const void* x, 
     need(plan != nullptr && graph != nullptr, "NULL plan or graph");
     if (plan->wkind != CGTP_W_PER_ROW)
       throw Error{CGTP_ERR_UNSUPPORTED, "the convolution needs per-edge weights (CGTP_W_PER_ROW)"};
+    if (plan->collapse) throw Error{CGTP_ERR_UNSUPPORTED, "the convolution does not take collapsed outputs"};
     need(graph->E == 0 || (x && sh && w && grad_out), "NULL input tensor");
     conv_backward_launch(plan, graph, x, sh, w, scale, grad_out, grad_x, grad_sh, grad_w, ws,
                          ws_bytes, as_stream(stream));

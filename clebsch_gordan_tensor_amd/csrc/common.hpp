@@ -46,11 +46,17 @@ struct BlockInfo {
   int l1, mul, x_off, path_begin, path_end;
 };
 
+// One output block: a path's own block, or with collapsed outputs the block
+// that every path of one (l3, p3) adds into.
+struct OutBlock {
+  int l3, p3, mul, out_off;
+};
+
 // Device copies (plain 32-bit fields).
 struct alignas(16) PathDev {
   int32_t l2, l3, y_off, out_off;
   int32_t w_off, coef_off, i2_end, mul;
-  int32_t l1, x_off, pad0, pad1;
+  int32_t l1, x_off, p3, pad1;
 };
 struct alignas(16) BlockDev {
   int32_t l1, mul, x_off, path_begin;
@@ -71,6 +77,12 @@ struct cgtp_plan_s {
   std::vector<cgtp::Irrep> X, Y, O;
   std::vector<cgtp::PathInfo> paths;
   std::vector<cgtp::BlockInfo> blocks;
+  std::vector<cgtp::OutBlock> outputs;
+  // x blocks that no path reads, as (offset, elements) within an x row: their
+  // gradient is zero and is written as such
+  std::vector<std::pair<int, int>> x_unread;
+  cgtp_paths select = CGTP_PATHS_ALL;
+  bool collapse = false;
   std::vector<std::vector<double>> cg_dense;  // per path, [2l1+1][2l2+1][2l3+1]
   std::vector<double> coef64;                 // packed in kernel pattern order
   std::vector<float> coef32;
@@ -98,7 +110,8 @@ namespace cgtp {
 // "MxLp + ..." -> blocks, order kept (CGTP_ERR_PARSE on malformed strings).
 std::vector<Irrep> irreps_from_string(const char* s);
 cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const char* mode,
-                        cgtp_dtype dtype, cgtp_wkind wkind);
+                        cgtp_dtype dtype, cgtp_wkind wkind, cgtp_paths select = CGTP_PATHS_ALL,
+                        bool collapse = false);
 // Real CG block by the ladder construction, [2l1+1][2l2+1][2l3+1], fp64.
 std::vector<double> real_cg_ladder(int l1, int l2, int l3);
 // Device tables of a plan on the current device (uploaded on first use).
@@ -137,5 +150,9 @@ struct TPBackwardRows {
   void* dw_ws = nullptr;
 };
 void tp_backward_rows(cgtp_plan_s* plan, const TPBackwardRows& r, hipStream_t stream);
+
+// Zero the x blocks no path reads in rows [rows][dim_x] of element size es
+// (the gradient of x there is zero).
+void zero_unread_x(const cgtp_plan_s* plan, void* p, int64_t rows, size_t es, hipStream_t stream);
 
 }  // namespace cgtp

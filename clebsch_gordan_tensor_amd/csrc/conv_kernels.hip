@@ -231,7 +231,10 @@ void conv_backward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* 
       throw Error{CGTP_ERR_WORKSPACE, "conv_backward needs " + std::to_string(need) + " workspace bytes"};
   }
   if (!grad_x && !grad_sh && !grad_w) return;
-  if (conv_backward_fused(plan, g, x, sh, w, scale, grad_out, grad_x, grad_sh, grad_w, ws, s)) return;
+  if (conv_backward_fused(plan, g, x, sh, w, scale, grad_out, grad_x, grad_sh, grad_w, ws, s)) {
+    zero_unread_x(plan, grad_x, g->N, dtype_size(plan->dtype), s);
+    return;
+  }
   TPBackwardRows r;
   r.rows = g->E;
   r.x = x;
@@ -252,6 +255,7 @@ void conv_backward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* 
       case CGTP_F64: dx_gather<double>(g, ws, grad_x, int(plan->dim_x), s); break;
       case CGTP_BF16: dx_gather<bf16>(g, ws, grad_x, int(plan->dim_x), s); break;
     }
+    zero_unread_x(plan, grad_x, g->N, dtype_size(plan->dtype), s);
   }
 }
 

@@ -232,7 +232,7 @@ void pack_path(int l1, int l2, int l3, const std::vector<double>& C, std::vector
 }  // namespace
 
 cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const char* mode,
-                        cgtp_dtype dtype, cgtp_wkind wkind) {
+                        cgtp_dtype dtype, cgtp_wkind wkind, cgtp_paths select, bool collapse) {
   if (!ix || !iy || !io || !mode) throw Error{CGTP_ERR_INVALID_ARG, "null irreps or mode"};
   if (std::strcmp(mode, "uvu") != 0)
     throw Error{CGTP_ERR_UNSUPPORTED, std::string("mode '") + mode + "' (only uvu)"};
@@ -240,7 +240,11 @@ cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const ch
     throw Error{CGTP_ERR_INVALID_ARG, "bad dtype"};
   if (wkind != CGTP_W_SHARED && wkind != CGTP_W_PER_ROW)
     throw Error{CGTP_ERR_INVALID_ARG, "bad weight kind"};
+  if (select != CGTP_PATHS_ALL && select != CGTP_PATHS_SYMMETRIC && select != CGTP_PATHS_SKEW)
+    throw Error{CGTP_ERR_INVALID_ARG, "bad path selection"};
   auto plan = std::make_unique<cgtp_plan_s>();
+  plan->select = select;
+  plan->collapse = collapse;
   plan->X = parse_irreps(ix);
   plan->Y = parse_irreps(iy);
   plan->O = parse_irreps(io);
@@ -280,6 +284,9 @@ cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const ch
       for (int l3 = std::abs(a.l - b.l); l3 <= a.l + b.l; ++l3) {
         const int p3 = a.p * b.p;
         if (!allowed.count({l3, p3})) continue;
+        // parity class of the path: symmetric when l1 + l2 + l3 is even
+        const bool sym = (a.l + b.l + l3) % 2 == 0;
+        if ((select == CGTP_PATHS_SYMMETRIC && !sym) || (select == CGTP_PATHS_SKEW && sym)) continue;
         PathInfo p{};
         p.i1 = i1; p.i2 = i2; p.l1 = a.l; p.l2 = b.l; p.l3 = l3; p.p3 = p3; p.mul = a.mul;
         p.x_off = xoff[i1];
@@ -297,9 +304,36 @@ cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const ch
       for (int k = run_begin; k < int(plan->paths.size()); ++k) plan->paths[k].i2_end = int(plan->paths.size());
     }
     blk.path_end = int(plan->paths.size());
-    if (blk.path_end > blk.path_begin) plan->blocks.push_back(blk);
+    if (blk.path_end > blk.path_begin)
+      plan->blocks.push_back(blk);
+    else
+      plan->x_unread.push_back({xoff[i1], a.mul * (2 * a.l + 1)});
   }
   if (plan->paths.empty()) throw Error{CGTP_ERR_UNSUPPORTED, "no path connects the irreps"};
+  if (!collapse) {
+    for (const PathInfo& p : plan->paths) plan->outputs.push_back(OutBlock{p.l3, p.p3, p.mul, p.out_off});
+  } else {
+    // one block per (l3, p3) that a path reaches, in irreps_out order (first
+    // occurrence); the paths feeding it must share their multiplicity
+    out_off = 0;
+    std::set<std::pair<int, int>> seen;
+    for (const Irrep& r : plan->O) {
+      if (!seen.insert({r.l, r.p}).second) continue;
+      int mul = -1;
+      for (const PathInfo& p : plan->paths)
+        if (p.l3 == r.l && p.p3 == r.p) {
+          if (mul >= 0 && p.mul != mul)
+            throw Error{CGTP_ERR_UNSUPPORTED, "collapsed output " + std::to_string(r.l) + (r.p > 0 ? "e" : "o") +
+                                                  " is fed by x blocks of different multiplicities"};
+          mul = p.mul;
+        }
+      if (mul < 0) continue;
+      for (PathInfo& p : plan->paths)
+        if (p.l3 == r.l && p.p3 == r.p) p.out_off = int(out_off);
+      plan->outputs.push_back(OutBlock{r.l, r.p, mul, int(out_off)});
+      out_off += int64_t(mul) * (2 * r.l + 1);
+    }
+  }
   if (out_off > INT32_MAX || w_off > INT32_MAX || plan->dim_x > INT32_MAX)
     throw Error{CGTP_ERR_UNSUPPORTED, "row too large for 32-bit offsets"};
   plan->dim_out = out_off;
@@ -352,7 +386,7 @@ const DevTables& plan_tables(cgtp_plan_s* plan) {
   std::vector<PathDev> pd;
   for (const PathInfo& p : plan->paths)
     pd.push_back(PathDev{p.l2, p.l3, p.y_off, p.out_off, p.w_off, p.coef_off, p.i2_end, p.mul,
-                         p.l1, p.x_off, 0, 0});
+                         p.l1, p.x_off, p.p3, 0});
   std::vector<BlockDev> bd;
   for (const BlockInfo& b : plan->blocks)
     bd.push_back(BlockDev{b.l1, b.mul, b.x_off, b.path_begin, b.path_end, 0, 0, 0});

@@ -78,6 +78,12 @@ struct TPArgs {
   int ngroups;   // channel groups per row = ceil(max_mul / VEC)
   int block;     // x block of a degree-specialised launch
   int dy_accum;  // add grad_y to what an earlier launch on the stream wrote
+  // collapsed outputs: the output parity this launch writes and, per parity
+  // (index 0: even, 1: odd) and degree l3, the block offset (-1 if absent)
+  // and multiplicity
+  int par;
+  int32_t goff[2][kLmax + 1];
+  int32_t gmul[2][kLmax + 1];
 };
 
 // LM: largest l2 and l3 compiled into a kernel (the plan's largest y or
@@ -171,6 +177,109 @@ __global__ __launch_bounds__(kBlock) CGTP_FWD_OCC void tp_fwd_kernel(TPArgs a) {
         });
       }
     }
+  }
+}
+
+// ------------------------------------------------------- collapsed forward
+// Outputs collapsed by (l3, p3): every path of one output type adds into one
+// block, so a lane accumulates all of them in registers (acc[l3^2 + m]) over
+// every x block of its row and writes each block once. A launch covers one
+// output parity (the parity of a path is fixed by its (i1, i2) run), which
+// halves the accumulators; x and y are read once per parity.
+template <typename T, typename A, int VEC, int LM>
+struct TPFwdCol {
+  static constexpr int NACC = (LM + 1) * (LM + 1);
+
+  template <int L1, int L2>
+  __device__ static __forceinline__ void run(const TPArgs& a, int p, int pend, const A (&xb)[2 * L1 + 1][VEC],
+                                             const T* yr, const T* wr, int c, A (&acc)[NACC][VEC]) {
+    A yb[2 * L2 + 1];
+    const int yoff = ldc(&a.paths[p].y_off);
+#pragma unroll
+    for (int m = 0; m < 2 * L2 + 1; ++m) yb[m] = to_acc<A>(yr[yoff + m]);
+    // the run's paths are in ascending l3: walk the possible degrees once
+    int q = p;
+    static_for<0, LM + 1>([&](auto L3c) {
+      constexpr int L3 = decltype(L3c)::value;
+      if constexpr (L3 >= (L1 > L2 ? L1 - L2 : L2 - L1) && L3 <= L1 + L2) {
+        if (q < pend && ldc(&a.paths[q].l3) == L3) {
+          const int coff = ldc(&a.paths[q].coef_off), woff = ldc(&a.paths[q].w_off);
+          ++q;
+          A o[2 * L3 + 1][VEC];
+          fwd_core<L1, L2, L3, VEC, A>(xb, yb, static_cast<const A*>(a.coef) + coff, o);
+          A wv[VEC];
+          VecIO<T, VEC>::load(wr + woff + c, wv);
+#pragma unroll
+          for (int m = 0; m < 2 * L3 + 1; ++m)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) acc[L3 * L3 + m][v] = fma(wv[v], o[m][v], acc[L3 * L3 + m][v]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    });
+  }
+
+  template <int L1>
+  __device__ static __forceinline__ void block(const TPArgs& a, const BlockDev& blk, const T* xr, const T* yr,
+                                               const T* wr, int c, A (&acc)[NACC][VEC]) {
+    A xb[2 * L1 + 1][VEC];
+#pragma unroll
+    for (int m = 0; m < 2 * L1 + 1; ++m) VecIO<T, VEC>::load(xr + blk.x_off + m * blk.mul + c, xb[m]);
+    int p = blk.path_begin;
+    while (p < blk.path_end) {
+      const int l2 = ldc(&a.paths[p].l2);
+      const int pend = ldc(&a.paths[p].i2_end);
+      if (ldc(&a.paths[p].p3) == a.par) {  // one parity per (i1, i2) run
+        static_for<0, LM + 1>([&](auto L2c) {
+          constexpr int L2 = decltype(L2c)::value;
+          if (l2 == L2) run<L1, L2>(a, p, pend, xb, yr, wr, c, acc);
+        });
+      }
+      p = pend;
+    }
+  }
+};
+
+template <typename T, typename A, int VEC, int LM>
+__global__ __launch_bounds__(kBlock) void tp_fwd_collapsed_kernel(TPArgs a) {
+  using F = TPFwdCol<T, A, VEC, LM>;
+  const int64_t gt = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+  const int64_t row = gt >> a.lpr_log2;
+  const int lpr = 1 << a.lpr_log2;
+  const int lr = int(gt & (lpr - 1));
+  if (row >= a.B) return;
+  const T* xr = static_cast<const T*>(a.x) + row * a.dim_x;
+  const T* yr = static_cast<const T*>(a.y) + row * a.dim_y;
+  const T* wr = static_cast<const T*>(a.w) + row * a.w_stride;
+  T* outr = static_cast<T*>(a.out) + row * a.dim_out;
+  const int pi = a.par > 0 ? 0 : 1;
+  for (int grp = lr; grp < a.ngroups; grp += lpr) {
+    const int c = grp * VEC;
+    A acc[F::NACC][VEC];
+#pragma unroll
+    for (int i = 0; i < F::NACC; ++i)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[i][v] = A(0);
+    for (int b = 0; b < a.nblocks; ++b) {
+      const BlockDev blk = ldc(a.blocks + b);
+      if (c >= blk.mul) continue;
+      static_for<0, kLmax + 1>([&](auto L1c) {
+        constexpr int D = decltype(L1c)::value;
+        if (blk.l1 == D) F::template block<D>(a, blk, xr, yr, wr, c, acc);
+      });
+    }
+    // addresses formed here, after the accumulation (kept out of the loop
+    // so they do not hold registers through it)
+    T* ob = outr + c;
+    asm volatile("" : "+v"(ob));
+    static_for<0, LM + 1>([&](auto L3c) {
+      constexpr int L3 = decltype(L3c)::value;
+      const int off = a.goff[pi][L3], mul = a.gmul[pi][L3];
+      if (off >= 0 && c < mul) {
+#pragma unroll
+        for (int m = 0; m < 2 * L3 + 1; ++m) VecIO<T, VEC>::store(ob + off + m * mul, acc[L3 * L3 + m]);
+      }
+    });
   }
 }
 
@@ -491,7 +600,18 @@ void tp_bwd_typed(const TPArgs& a, int l1, int lm, hipStream_t s) {
   }
 }
 
+template <typename T, int VEC>
+void tp_fwd_collapsed_typed(const TPArgs& a, int lm, hipStream_t s) {
+  using A = typename AccOf<T>::type;
+  const dim3 grid = grid_for(a.B, a.lpr_log2);
+  static_for<0, kLmax + 1>([&](auto J) {
+    constexpr int M = decltype(J)::value;
+    if (lm == M) hipLaunchKernelGGL((tp_fwd_collapsed_kernel<T, A, VEC, M>), grid, dim3(kBlock), 0, s, a);
+  });
+}
+
 #define CGTP_TP_EXTERN_FWD(T, V) extern template void tp_fwd_typed<T, V>(const TPArgs&, int, int, hipStream_t);
+#define CGTP_TP_EXTERN_FWDC(T, V) extern template void tp_fwd_collapsed_typed<T, V>(const TPArgs&, int, hipStream_t);
 #define CGTP_TP_EXTERN_BWD(T, V) extern template void tp_bwd_typed<T, V>(const TPArgs&, int, int, hipStream_t);
 
 }  // namespace cgtp

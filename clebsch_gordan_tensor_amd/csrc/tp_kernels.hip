@@ -9,6 +9,12 @@ CGTP_TP_EXTERN_FWD(bf16, 1)
 CGTP_TP_EXTERN_FWD(bf16, 4)
 CGTP_TP_EXTERN_FWD(double, 1)
 CGTP_TP_EXTERN_FWD(double, 2)
+CGTP_TP_EXTERN_FWDC(float, 1)
+CGTP_TP_EXTERN_FWDC(float, 4)
+CGTP_TP_EXTERN_FWDC(bf16, 1)
+CGTP_TP_EXTERN_FWDC(bf16, 4)
+CGTP_TP_EXTERN_FWDC(double, 1)
+CGTP_TP_EXTERN_FWDC(double, 2)
 CGTP_TP_EXTERN_BWD(float, 1)
 CGTP_TP_EXTERN_BWD(float, 2)
 CGTP_TP_EXTERN_BWD(float, 4)
@@ -81,6 +87,38 @@ void tp_forward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* 
   a.y = y;
   a.w = w;
   a.out = out;
+  if (plan->collapse) {
+    // one launch per output parity that has blocks, all x blocks in each
+    bool any[2] = {false, false};
+    for (int pi = 0; pi < 2; ++pi)
+      for (int l = 0; l <= kLmax; ++l) a.goff[pi][l] = -1, a.gmul[pi][l] = 0;
+    for (const OutBlock& o : plan->outputs) {
+      const int pi = o.p3 > 0 ? 0 : 1;
+      a.goff[pi][o.l3] = o.out_off;
+      a.gmul[pi][o.l3] = o.mul;
+      any[pi] = true;
+    }
+    for (int pi = 0; pi < 2; ++pi) {
+      if (!any[pi]) continue;
+      a.par = pi == 0 ? 1 : -1;
+      switch (plan->dtype) {
+        case CGTP_F32:
+          vec == 1 ? tp_fwd_collapsed_typed<float, 1>(a, plan->lm, stream)
+                   : tp_fwd_collapsed_typed<float, 4>(a, plan->lm, stream);
+          break;
+        case CGTP_BF16:
+          vec == 1 ? tp_fwd_collapsed_typed<bf16, 1>(a, plan->lm, stream)
+                   : tp_fwd_collapsed_typed<bf16, 4>(a, plan->lm, stream);
+          break;
+        case CGTP_F64:
+          vec == 1 ? tp_fwd_collapsed_typed<double, 1>(a, plan->lm, stream)
+                   : tp_fwd_collapsed_typed<double, 2>(a, plan->lm, stream);
+          break;
+      }
+      CGTP_CHECK_HIP(hipGetLastError());
+    }
+    return;
+  }
   // one launch per x block with the kernel specialised for its degree (the
   // general kernel in one launch when channels are not vectorised)
   const int nb = vec == 1 ? 1 : int(plan->blocks.size());
@@ -99,6 +137,36 @@ void tp_forward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* 
                  : tp_fwd_typed<double, 2>(a, l1, plan->lm, stream);
         break;
     }
+    CGTP_CHECK_HIP(hipGetLastError());
+  }
+}
+
+namespace {
+
+// p[r * ld + off + j] = 0 for j < n (one element per thread)
+template <typename E>
+__global__ __launch_bounds__(kBlock) void zero_cols_kernel(E* __restrict__ p, int64_t rows, int64_t ld, int off, int n) {
+  const int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+  if (i >= rows * n) return;
+  const int64_t r = i / n;
+  p[r * ld + off + (i - r * n)] = E(0);
+}
+
+}  // namespace
+
+void zero_unread_x(const cgtp_plan_s* plan, void* p, int64_t rows, size_t es, hipStream_t stream) {
+  if (!p || rows == 0) return;
+  for (const auto& blk : plan->x_unread) {
+    const dim3 grid(unsigned((rows * blk.second + kBlock - 1) / kBlock));
+    if (es == 2)
+      hipLaunchKernelGGL((zero_cols_kernel<uint16_t>), grid, dim3(kBlock), 0, stream, static_cast<uint16_t*>(p), rows,
+                         plan->dim_x, blk.first, blk.second);
+    else if (es == 4)
+      hipLaunchKernelGGL((zero_cols_kernel<uint32_t>), grid, dim3(kBlock), 0, stream, static_cast<uint32_t*>(p), rows,
+                         plan->dim_x, blk.first, blk.second);
+    else
+      hipLaunchKernelGGL((zero_cols_kernel<uint64_t>), grid, dim3(kBlock), 0, stream, static_cast<uint64_t*>(p), rows,
+                         plan->dim_x, blk.first, blk.second);
     CGTP_CHECK_HIP(hipGetLastError());
   }
 }
@@ -179,6 +247,7 @@ void tp_backward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void*
   r.dw = shared ? nullptr : dw;
   r.dw_ws = (shared && dw) ? ws : nullptr;
   tp_backward_rows(plan, r, stream);
+  zero_unread_x(plan, dx, B, dtype_size(plan->dtype), stream);
   if (shared && dw) {
     char* part = static_cast<char*>(ws) + size_t(B) * plan->w_numel * acc_size(plan->dtype);
     switch (plan->dtype) {

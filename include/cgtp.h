@@ -73,6 +73,11 @@ typedef enum { CGTP_F32 = 0, CGTP_F64 = 1, CGTP_BF16 = 2 } cgtp_dtype;
  * product (rows = B) and [edges][W] in CSR order for the convolution. */
 typedef enum { CGTP_W_SHARED = 0, CGTP_W_PER_ROW = 1 } cgtp_wkind;
 
+/* Path selections by parity class (E3J appendix B.1: the Gaunt product covers
+ * the symmetric paths, the vector signal product the skew-symmetric ones):
+ * SYMMETRIC keeps the paths with l1 + l2 + l3 even, SKEW those with it odd. */
+typedef enum { CGTP_PATHS_ALL = 0, CGTP_PATHS_SYMMETRIC = 1, CGTP_PATHS_SKEW = 2 } cgtp_paths;
+
 /* Operations for cgtp_workspace_size. */
 typedef enum { CGTP_OP_TP_BACKWARD = 1, CGTP_OP_CONV_BACKWARD = 2 } cgtp_op;
 
@@ -103,7 +108,26 @@ const char* cgtp_last_error(void);
  * != 1, any l > CGTP_LMAX, no path at all), INVALID_ARG (null pointers). */
 cgtp_status cgtp_plan_create(const char* irreps_x, const char* irreps_y, const char* irreps_out,
                              const char* mode, cgtp_dtype dtype, cgtp_wkind wkind, cgtp_plan* out);
+/* cgtp_plan_create with a path selection and, if collapse != 0, outputs
+ * collapsed by degree (E3J appendix B.1 and B.3: the isomorphic copies of each
+ * output irrep are summed). Collapsed layout: one output block [2l3+1][mul] per
+ * (l3, p3) that some path reaches, in the order of irreps_out (first
+ * occurrence), where every path of that (l3, p3) adds its output; mul is the
+ * multiplicity of the x blocks feeding it. The tensor product forward and
+ * backward accept collapsed plans; the convolution does not (UNSUPPORTED).
+ * Errors: as cgtp_plan_create; INVALID_ARG for a bad selection; UNSUPPORTED
+ * when the x blocks feeding one collapsed output differ in multiplicity or no
+ * path is selected. */
+cgtp_status cgtp_plan_create_ex(const char* irreps_x, const char* irreps_y, const char* irreps_out,
+                                const char* mode, cgtp_dtype dtype, cgtp_wkind wkind, cgtp_paths select,
+                                int collapse, cgtp_plan* out);
 cgtp_status cgtp_plan_destroy(cgtp_plan plan);
+
+/* Output blocks of a plan into a HOST table [num_outputs][4] of
+ * (l3, p3, mul, offset within the output row): one per path in path order, or
+ * one per collapsed (l3, p3). host_table may be NULL to query the count only;
+ * num_outputs may be NULL. */
+cgtp_status cgtp_plan_outputs(cgtp_plan plan, int64_t* num_outputs, int32_t* host_table);
 
 /* Sizes in elements per row: dim_x, dim_y, dim_out, the path count and W
  * (weights per row or per edge). Any output pointer may be NULL. */

@@ -49,7 +49,7 @@ def block_errors(gpu, ref, offsets_sizes):
 
 
 def out_blocks(L):
-    return [(p["out_off"], p["mul"] * (2 * p["l3"] + 1)) for p in L.paths]
+    return [(g["out_off"], g["mul"] * (2 * g["l3"] + 1)) for g in L.groups]
 
 
 def x_blocks(L):

@@ -3,7 +3,8 @@
 * the library loads and exports every function include/cgtp.h declares;
 * the planner's CG blocks (ladder construction) equal the oracle's (Racah);
 * path tables and row sizes equal the oracle's enumeration;
-* malformed or unsupported plans return the documented status codes.
+* malformed or unsupported plans return the documented status codes;
+* parity-selected and collapsed plans list the oracle's paths and output blocks.
 """
 
 import os
@@ -28,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 25
+    assert len(names) == 27
     for n in names:
         assert hasattr(cgtp._lib, n), n
     assert sorted(cgtp.EXPORTED) == names
@@ -132,3 +133,41 @@ def test_linear_errors():
     assert lin.workspace_size(0) == 0
     assert lin.workspace_size(1000) == 12 * 4          # one row chunk of partials
     assert lin.workspace_size(10 ** 6) > 0
+
+
+@pytest.mark.parametrize("select", ["all", "symmetric", "skew"])
+@pytest.mark.parametrize("collapse", [False, True])
+@pytest.mark.parametrize("ix,iy,io", [
+    ("2x0e+2x1o+2x2e+2x3o", "0e+1o+2e+3o", "0e+0o+1e+1o+2e+2o+3e+3o"),
+    ("64x0e+64x1o+64x2e+64x3o+64x4e", "0e+1o+2e+3o+4e", "0e+0o+1e+1o+2e+2o+3e+3o+4e+4o"),
+    ("4x0e+6x1e", "0e", "1e+0e"),                                  # groups in irreps_out order
+])
+def test_variant_plans_equal_oracle(ix, iy, io, select, collapse):
+    L = Layout(ix, iy, io, select, collapse)
+    if not L.paths:
+        with pytest.raises(cgtp.CgtpError):
+            cgtp.Plan(ix, iy, io, select=select, collapse=collapse)
+        return
+    plan = cgtp.Plan(ix, iy, io, select=select, collapse=collapse)
+    assert (plan.dim_out, plan.num_paths, plan.w_numel) == (L.dim_out, len(L.paths), L.w_numel)
+    want = [(p["i1"], p["i2"], p["l1"], p["l2"], p["l3"], p["p3"]) for p in L.paths]
+    assert [tuple(r) for r in plan.paths()] == want
+    assert [tuple(r) for r in plan.outputs()] == [(g["l3"], g["p3"], g["mul"], g["out_off"]) for g in L.groups]
+
+
+def test_variant_plan_errors():
+    bad = ctypes_plan_ex("2x0e+3x1o", "0e+1o", "0e+1o", 0, 1)      # 0e fed by 2x and 3x blocks
+    assert bad == 3
+    assert ctypes_plan_ex("2x0e", "0e", "0e", 7, 0) == 1              # no such selection
+    assert ctypes_plan_ex("2x1o", "1o", "1e", 1, 0) == 3              # the only path is skew
+    assert ctypes_plan_ex("2x1o", "1o", "1e", 2, 1) == 0
+
+
+def ctypes_plan_ex(ix, iy, io, select, collapse):
+    import ctypes
+    h = ctypes.c_void_p()
+    st = cgtp._lib.cgtp_plan_create_ex(ix.encode(), iy.encode(), io.encode(), b"uvu", 0, 1, select, collapse,
+                                       ctypes.byref(h))
+    if st == 0:
+        cgtp._lib.cgtp_plan_destroy(h)
+    return st
