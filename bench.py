@@ -15,8 +15,9 @@ of x, y and w), with every input already resident in HBM. `value` is rows
 Besides the headline line's `roofline` (dominant kernel, algorithmic bytes per
 call over its mean HIP-event duration against 8 TB/s) and `cpu_baseline` (the
 fp64 oracle on a bounded sample, on the host cores), `extra` carries the
-per-kernel figures, the same workload in bf16 storage, the equivariant linear
-map on the same rows (matrix cores) and, unless --no-conv,
+per-kernel figures, the same workload in bf16 storage and with outputs
+collapsed by (l3, p3) (all, symmetric and skew path sets), the equivariant
+linear map on the same rows (matrix cores) and, unless --no-conv,
 the fused convolution (forward and backward, fp32) on the 1000- and
 8000-molecule water boxes (the latter with the harmonics forward/backward of
 the force chain) and the 100,000-point uniform cloud.
@@ -36,7 +37,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "TP pairs/s + conv edges/s (fwd, fwd+bwd) as HBM GB/s and % of MI355X peak"
 PROFILES = os.path.join(ROOT, "profiles")
 WORKLOADS = ["tp_large", "tp_large_bf16", "conv_water1k", "conv_water8k", "conv_uniform100k", "linear_large",
-             "linear_large_bf16"]
+             "linear_large_bf16", "tp_large_collapsed"]
 MFMA_FP32_PEAK_TFS = 157.3
 
 
@@ -108,10 +109,11 @@ class TPWorkload:
     """tp_large: 2^20 rows, per-row weights; fp32 (with the harmonics of the row
     directions computed in the step) or bf16 storage (harmonics drawn directly)."""
 
-    def __init__(self, torch, cgtp, synth, dtype):
+    def __init__(self, torch, cgtp, synth, dtype, select="all", collapse=False):
         c = synth.CONFIGS["tp_large"]
         self.torch, self.cgtp, self.dtype = torch, cgtp, dtype
-        self.plan = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"], dtype=dtype, wkind="per_row")
+        self.plan = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"], dtype=dtype, wkind="per_row",
+                              select=select, collapse=collapse)
         self.irreps_x = c["irreps_x"]
         self.B = B = c["B"]
         p = self.plan
@@ -249,6 +251,8 @@ def make_workload(torch, cgtp, synth, name):
         return TPWorkload(torch, cgtp, synth, "f32")
     if name == "tp_large_bf16":
         return TPWorkload(torch, cgtp, synth, "bf16")
+    if name == "tp_large_collapsed":
+        return TPWorkload(torch, cgtp, synth, "f32", collapse=True)
     return ConvWorkload(torch, cgtp, synth, name)
 
 
@@ -385,6 +389,37 @@ def conv_bench(args, torch, cgtp, synth, name, steps, forces=False):
     return res
 
 
+def tp_variants_bench(args, torch, cgtp, synth):
+    """tp_large fp32 with outputs collapsed by (l3, p3), all / symmetric / skew
+    paths: forward and backward call times and algorithmic GB/s."""
+    res = {}
+    for sel in ("all", "symmetric", "skew"):
+        wl = TPWorkload(torch, cgtp, synth, "f32", select=sel, collapse=True)
+        B = wl.B
+        tf, tb = KernelTimer(torch), KernelTimer(torch)
+        wl.fwd()
+        wl.bwd()
+        for _ in range(3):
+            tf(wl.fwd)
+            tb(wl.bwd)
+        torch.cuda.synchronize()
+        f, b = tf.mean_ms(), tb.mean_ms()
+        res[sel] = dict(paths=wl.plan.num_paths, dim_out=wl.plan.dim_out, fwd_ms=round(f, 3),
+                        fwd_algorithmic_GBs=round(wl.bytes_fwd() * B / (f * 1e-3) / 1e9, 1),
+                        bwd_ms=round(b, 3), bwd_algorithmic_GBs=round(wl.bytes_bwd() * B / (b * 1e-3) / 1e9, 1),
+                        fwd_bwd_pairs_per_s=B / ((f + b) * 1e-3))
+        if sel == "all":
+            # the collapsed forward is one dispatch per output parity (the counter
+            # summary holds one dispatch); the backward one per x block
+            npar = len({int(r[1]) for r in wl.plan.outputs()})
+            t = traffic_for("tp_fwd_collapsed_kernel", "tp_large_collapsed", B)
+            res[sel]["fwd_traffic"] = t * npar if t is not None else None
+            res[sel]["bwd_traffic"] = traffic_for("tp_bwd_kernel", "tp_large_collapsed", B)
+        del wl
+        torch.cuda.empty_cache()
+    return res
+
+
 def linear_bench(args, torch, cgtp, synth, dtype):
     """Equivariant linear map (fp32 MFMA) on the tensor-product rows: call times,
     TFLOP/s against the fp32 matrix-core peak, and algorithmic GB/s."""
@@ -461,6 +496,7 @@ def main():
     extra = {"device": torch.cuda.get_device_name(0)}
     value, ms_step, roofline, plan = tp_large_bench(args, torch, cgtp, synth, extra)
     extra["tp_large_bf16"] = tp_large_bf16(args, torch, cgtp, synth)
+    extra["tp_large_collapsed"] = tp_variants_bench(args, torch, cgtp, synth)
     extra["linear_large"] = linear_bench(args, torch, cgtp, synth, "f32")
     extra["linear_large_bf16"] = linear_bench(args, torch, cgtp, synth, "bf16")
     if not args.no_conv:

@@ -10,8 +10,10 @@ CGTP_TP_EXTERN_FWD(bf16, 4)
 CGTP_TP_EXTERN_FWD(double, 1)
 CGTP_TP_EXTERN_FWD(double, 2)
 CGTP_TP_EXTERN_FWDC(float, 1)
+CGTP_TP_EXTERN_FWDC(float, 2)
 CGTP_TP_EXTERN_FWDC(float, 4)
 CGTP_TP_EXTERN_FWDC(bf16, 1)
+CGTP_TP_EXTERN_FWDC(bf16, 2)
 CGTP_TP_EXTERN_FWDC(bf16, 4)
 CGTP_TP_EXTERN_FWDC(double, 1)
 CGTP_TP_EXTERN_FWDC(double, 2)
@@ -31,6 +33,13 @@ CGTP_TP_EXTERN_BWD(double, 2)
 #endif
 #ifndef CGTP_TP_BWD_VEC_BF16
 #define CGTP_TP_BWD_VEC_BF16 4
+#endif
+// Channels per lane of the collapsed-output forward with 4- and 2-byte
+// storage: its accumulators for every output degree stay in registers, and
+// 2 channels keep the kernel at 3-4 waves per SIMD where 4 channels drop
+// it to 1-2.
+#ifndef CGTP_TP_FWDC_VEC
+#define CGTP_TP_FWDC_VEC 2
 #endif
 
 // ----------------------------------------------------------------- launchers
@@ -89,6 +98,14 @@ void tp_forward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* 
   a.out = out;
   if (plan->collapse) {
     // one launch per output parity that has blocks, all x blocks in each
+    if (plan->dtype != CGTP_F64 && vec > CGTP_TP_FWDC_VEC) {
+      vec = CGTP_TP_FWDC_VEC;
+      a = make_args(plan, t, B, vec);
+      a.x = x;
+      a.y = y;
+      a.w = w;
+      a.out = out;
+    }
     bool any[2] = {false, false};
     for (int pi = 0; pi < 2; ++pi)
       for (int l = 0; l <= kLmax; ++l) a.goff[pi][l] = -1, a.gmul[pi][l] = 0;
@@ -103,12 +120,14 @@ void tp_forward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* 
       a.par = pi == 0 ? 1 : -1;
       switch (plan->dtype) {
         case CGTP_F32:
-          vec == 1 ? tp_fwd_collapsed_typed<float, 1>(a, plan->lm, stream)
-                   : tp_fwd_collapsed_typed<float, 4>(a, plan->lm, stream);
+          vec == 1   ? tp_fwd_collapsed_typed<float, 1>(a, plan->lm, stream)
+          : vec == 2 ? tp_fwd_collapsed_typed<float, 2>(a, plan->lm, stream)
+                     : tp_fwd_collapsed_typed<float, 4>(a, plan->lm, stream);
           break;
         case CGTP_BF16:
-          vec == 1 ? tp_fwd_collapsed_typed<bf16, 1>(a, plan->lm, stream)
-                   : tp_fwd_collapsed_typed<bf16, 4>(a, plan->lm, stream);
+          vec == 1   ? tp_fwd_collapsed_typed<bf16, 1>(a, plan->lm, stream)
+          : vec == 2 ? tp_fwd_collapsed_typed<bf16, 2>(a, plan->lm, stream)
+                     : tp_fwd_collapsed_typed<bf16, 4>(a, plan->lm, stream);
           break;
         case CGTP_F64:
           vec == 1 ? tp_fwd_collapsed_typed<double, 1>(a, plan->lm, stream)
