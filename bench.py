@@ -20,7 +20,9 @@ collapsed by (l3, p3) (all, symmetric and skew path sets), the equivariant
 linear map on the same rows (matrix cores) and, unless --no-conv,
 the fused convolution (forward and backward, fp32) on the 1000- and
 8000-molecule water boxes (the latter with the harmonics forward/backward of
-the force chain) and the 100,000-point uniform cloud.
+the force chain), the 100,000-point uniform cloud, and 2048 points with 45
+neighbours and 128 channels per degree with outputs collapsed by (l3, p3)
+(L = 3 and 4).
 """
 
 import argparse
@@ -37,7 +39,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "TP pairs/s + conv edges/s (fwd, fwd+bwd) as HBM GB/s and % of MI355X peak"
 PROFILES = os.path.join(ROOT, "profiles")
 WORKLOADS = ["tp_large", "tp_large_bf16", "conv_water1k", "conv_water8k", "conv_uniform100k", "linear_large",
-             "linear_large_bf16", "tp_large_collapsed"]
+             "linear_large_bf16", "tp_large_collapsed", "conv_collapsed_l3", "conv_collapsed_l4"]
 MFMA_FP32_PEAK_TFS = 157.3
 
 
@@ -164,7 +166,8 @@ class ConvWorkload:
         c = synth.CONFIGS[name]
         self.torch, self.cgtp, self.c = torch, cgtp, c
         dev = torch.device("cuda:0")
-        self.plan = p = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"], dtype="f32", wkind="per_row")
+        self.plan = p = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"], dtype="f32", wkind="per_row",
+                                  collapse=c.get("collapse", False))
         pos = synth.positions_for(c, 0)
         src, dst, vec = synth.radius_graph(pos, c["box"], c["r_cut"])
         self.N, self.E = N, E = pos.shape[0], src.shape[0]
@@ -500,7 +503,7 @@ def main():
     extra["linear_large"] = linear_bench(args, torch, cgtp, synth, "f32")
     extra["linear_large_bf16"] = linear_bench(args, torch, cgtp, synth, "bf16")
     if not args.no_conv:
-        for name in ("conv_water1k", "conv_water8k", "conv_uniform100k"):
+        for name in ("conv_water1k", "conv_water8k", "conv_uniform100k", "conv_collapsed_l3", "conv_collapsed_l4"):
             extra[name] = conv_bench(args, torch, cgtp, synth, name, max(2, min(args.steps, 5)),
                                      forces=name == "conv_water8k")
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, synth)

@@ -230,7 +230,6 @@ cgtp_status cgtp_conv_forward(cgtp_plan plan, cgtp_graph graph, const void* x, c
     need(plan != nullptr && graph != nullptr, "NULL plan or graph");
     if (plan->wkind != CGTP_W_PER_ROW)
       throw Error{CGTP_ERR_UNSUPPORTED, "the convolution needs per-edge weights (CGTP_W_PER_ROW)"};
-    if (plan->collapse) throw Error{CGTP_ERR_UNSUPPORTED, "the convolution does not take collapsed outputs"};
     if (graph->N == 0) return;
     need(out != nullptr, "out is NULL");
     need(graph->E == 0 || (x && sh && w), "NULL input tensor");
@@ -245,7 +244,6 @@ cgtp_status cgtp_conv_backward(cgtp_plan plan, cgtp_graph graph, const void* x, 
     need(plan != nullptr && graph != nullptr, "NULL plan or graph");
     if (plan->wkind != CGTP_W_PER_ROW)
       throw Error{CGTP_ERR_UNSUPPORTED, "the convolution needs per-edge weights (CGTP_W_PER_ROW)"};
-    if (plan->collapse) throw Error{CGTP_ERR_UNSUPPORTED, "the convolution does not take collapsed outputs"};
     need(graph->E == 0 || (x && sh && w && grad_out), "NULL input tensor");
     conv_backward_launch(plan, graph, x, sh, w, scale, grad_out, grad_x, grad_sh, grad_w, ws,
                          ws_bytes, as_stream(stream));

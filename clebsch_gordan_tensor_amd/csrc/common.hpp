@@ -154,5 +154,7 @@ void tp_backward_rows(cgtp_plan_s* plan, const TPBackwardRows& r, hipStream_t st
 // Zero the x blocks no path reads in rows [rows][dim_x] of element size es
 // (the gradient of x there is zero).
 void zero_unread_x(const cgtp_plan_s* plan, void* p, int64_t rows, size_t es, hipStream_t stream);
+// Zero n elements of size es (a fill kernel, so the call may sit in a captured graph).
+void zero_rows(void* p, int64_t n, size_t es, hipStream_t stream);
 
 }  // namespace cgtp

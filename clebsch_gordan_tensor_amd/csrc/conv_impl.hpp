@@ -96,6 +96,7 @@ struct ConvArgs {
   int nblocks, nchunks, npaths, L;
   int block;    // x block of a degree-specialised launch
   int lg_log2;  // lanes per edge group (fused forward)
+  int collapse; // outputs collapsed by (l3, p3): add into the (zeroed) output instead of storing
   int yoff[kLmax + 1];
   double scale;
 };
@@ -255,6 +256,12 @@ __device__ __forceinline__ void fwd_fused_chunk(const ConvArgs& a, int64_t n, co
         A o[VEC];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) o[v] = sc * acc[st.acc - acc0 + m][v];
+        if (a.collapse) {  // several slots share the block: add in launch, chunk and slot order
+          A prev[VEC];
+          VecIO<T, VEC>::load(outn + pd.out_off + m * pd.mul + c, prev);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) o[v] += prev[v];
+        }
         VecIO<T, VEC>::store(outn + pd.out_off + m * pd.mul + c, o);
       }
     }
@@ -266,14 +273,17 @@ __device__ __forceinline__ void fwd_fused_chunk(const ConvArgs& a, int64_t n, co
 template <typename T, typename A, int VEC, int L1, int L>
 __global__ __launch_bounds__(kBlock) void conv_fwd_fused_kernel(ConvArgs a) {
   using CK = Chunks<L1, L, conv_budget<A, VEC>()>;
+  // with collapsed outputs one wave runs every slot chunk of its receiver in
+  // turn, so the additions into a shared block never overlap
+  const int nch = a.collapse ? 1 : CK::NCH;
   const int64_t item = xcd_block() * kWaves + conv_wave_id();
-  const int64_t per_node = int64_t(CK::NCH) * a.nchunks;
+  const int64_t per_node = int64_t(nch) * a.nchunks;
   const int64_t pos = item / per_node;
   if (pos >= a.N) return;
   const int rem = int(item - pos * per_node);
   const int64_t n = a.order[pos];
-  const int cc = rem / CK::NCH;
-  const int ch = rem - cc * CK::NCH;
+  const int cc = rem / nch;
+  const int ch = rem - cc * nch;
   const BlockDev blk = ldc(a.blocks + a.block);
   const int lane = int(threadIdx.x & 63);
   const int LG = 1 << a.lg_log2;
@@ -283,7 +293,7 @@ __global__ __launch_bounds__(kBlock) void conv_fwd_fused_kernel(ConvArgs a) {
   const bool valid = c < blk.mul;
   static_for<0, CK::NCH>([&](auto C) {
     constexpr int CH = decltype(C)::value;
-    if (ch == CH) fwd_fused_chunk<T, A, VEC, L1, L, CH>(a, n, blk, c, valid, g, G);
+    if (a.collapse || ch == CH) fwd_fused_chunk<T, A, VEC, L1, L, CH>(a, n, blk, c, valid, g, G);
   });
 }
 
@@ -314,38 +324,47 @@ __device__ __forceinline__ void fwd_general_path(const ConvArgs& a, int64_t n, c
   T* __restrict__ outn = static_cast<T*>(a.out) + n * a.dim_out;
   const A sc = A(a.scale);
 #pragma unroll
-  for (int m = 0; m < 2 * L3 + 1; ++m) from_acc(outn[pd.out_off + m * pd.mul + c], sc * acc[m]);
+  for (int m = 0; m < 2 * L3 + 1; ++m) {
+    A o = sc * acc[m];
+    if (a.collapse) o += to_acc<A>(outn[pd.out_off + m * pd.mul + c]);
+    from_acc(outn[pd.out_off + m * pd.mul + c], o);
+  }
 }
 
 template <typename T, typename A>
 __global__ __launch_bounds__(kBlock) void conv_fwd_general_kernel(ConvArgs a) {
   const int64_t item = xcd_block() * kWaves + conv_wave_id();
-  const int64_t per_node = int64_t(a.npaths) * a.nchunks;
+  // collapsed outputs: one wave takes every path of its receiver in turn
+  const int np = a.collapse ? 1 : a.npaths;
+  const int64_t per_node = int64_t(np) * a.nchunks;
   const int64_t pos = item / per_node;
   if (pos >= a.N) return;
   const int rem = int(item - pos * per_node);
   const int64_t n = a.order[pos];
-  const int p = rem / a.nchunks;
-  const int chunk = rem - p * a.nchunks;
-  const PathDev pd = ldc(a.paths + p);
-  const int c = chunk * 64 + int(threadIdx.x & 63);
-  if (c >= pd.mul) return;
-  static_for<0, kLmax + 1>([&](auto A1) {
-    constexpr int L1 = decltype(A1)::value;
-    if (pd.l1 == L1) {
-      static_for<0, kLmax + 1>([&](auto A2) {
-        constexpr int L2 = decltype(A2)::value;
-        if (pd.l2 == L2) {
-          static_for<0, kLmax + 1>([&](auto A3) {
-            constexpr int L3 = decltype(A3)::value;
-            if constexpr (L3 >= idiff(L1, L2) && L3 <= L1 + L2) {
-              if (pd.l3 == L3) fwd_general_path<T, A, L1, L2, L3>(a, n, pd, c);
-            }
-          });
-        }
-      });
-    }
-  });
+  const int p0 = rem / a.nchunks;
+  const int chunk = rem - p0 * a.nchunks;
+  const int p1 = a.collapse ? a.npaths : p0 + 1;
+  for (int p = p0; p < p1; ++p) {
+    const PathDev pd = ldc(a.paths + p);
+    const int c = chunk * 64 + int(threadIdx.x & 63);
+    if (c >= pd.mul) continue;
+    static_for<0, kLmax + 1>([&](auto A1) {
+      constexpr int L1 = decltype(A1)::value;
+      if (pd.l1 == L1) {
+        static_for<0, kLmax + 1>([&](auto A2) {
+          constexpr int L2 = decltype(A2)::value;
+          if (pd.l2 == L2) {
+            static_for<0, kLmax + 1>([&](auto A3) {
+              constexpr int L3 = decltype(A3)::value;
+              if constexpr (L3 >= idiff(L1, L2) && L3 <= L1 + L2) {
+                if (pd.l3 == L3) fwd_general_path<T, A, L1, L2, L3>(a, n, pd, c);
+              }
+            });
+          }
+        });
+      }
+    });
+  }
 }
 
 // ------------------------------------------------------------ fused backward

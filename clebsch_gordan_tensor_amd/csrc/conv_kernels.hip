@@ -80,8 +80,12 @@ void fwd_typed(cgtp_plan_s* plan, ConvArgs a, hipStream_t s) {
   const size_t vb = size_t(conv_vec(plan->dtype)) * dtype_size(plan->dtype);
   const bool fused = plan->conv_fused && plan->vec == conv_vec(plan->dtype) && aligned_to(a.x, vb) &&
                      aligned_to(a.w, vb) && aligned_to(a.out, vb);
+  if (plan->collapse) {  // the kernels add into the output
+    zero_rows(a.out, a.N * int64_t(a.dim_out), dtype_size(plan->dtype), s);
+    a.collapse = 1;
+  }
   if (!fused) {
-    const int64_t items = a.N * int64_t(a.npaths) * a.nchunks;
+    const int64_t items = a.N * int64_t(a.collapse ? 1 : a.npaths) * a.nchunks;
     conv_fwd_general_typed<T>(a, dim3(unsigned((items + kWaves - 1) / kWaves)), s);
     CGTP_CHECK_HIP(hipGetLastError());
     return;
@@ -96,7 +100,7 @@ void fwd_typed(cgtp_plan_s* plan, ConvArgs a, hipStream_t s) {
     a.block = int(b);
     a.lg_log2 = lg;
     a.nchunks = (lanes + (1 << lg) - 1) >> lg;
-    const int nch = conv_fused_chunks<T>(blk.l1, plan->conv_L);
+    const int nch = a.collapse ? 1 : conv_fused_chunks<T>(blk.l1, plan->conv_L);
     const int64_t items = a.N * int64_t(nch) * a.nchunks;
     conv_fwd_fused_typed<T>(a, blk.l1, plan->conv_L, dim3(unsigned((items + kWaves - 1) / kWaves)), s);
     CGTP_CHECK_HIP(hipGetLastError());

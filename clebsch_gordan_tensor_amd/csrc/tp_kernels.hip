@@ -173,6 +173,21 @@ __global__ __launch_bounds__(kBlock) void zero_cols_kernel(E* __restrict__ p, in
 
 }  // namespace
 
+void zero_rows(void* p, int64_t n, size_t es, hipStream_t stream) {
+  if (!p || n == 0) return;
+  const dim3 grid(unsigned((n + kBlock - 1) / kBlock));
+  if (es == 2)
+    hipLaunchKernelGGL((zero_cols_kernel<uint16_t>), grid, dim3(kBlock), 0, stream, static_cast<uint16_t*>(p), n,
+                       int64_t(1), 0, 1);
+  else if (es == 4)
+    hipLaunchKernelGGL((zero_cols_kernel<uint32_t>), grid, dim3(kBlock), 0, stream, static_cast<uint32_t*>(p), n,
+                       int64_t(1), 0, 1);
+  else
+    hipLaunchKernelGGL((zero_cols_kernel<uint64_t>), grid, dim3(kBlock), 0, stream, static_cast<uint64_t*>(p), n,
+                       int64_t(1), 0, 1);
+  CGTP_CHECK_HIP(hipGetLastError());
+}
+
 void zero_unread_x(const cgtp_plan_s* plan, void* p, int64_t rows, size_t es, hipStream_t stream) {
   if (!p || rows == 0) return;
   for (const auto& blk : plan->x_unread) {

@@ -246,6 +246,13 @@ CONFIGS = {
                          n_mol=8000, box=62.1, r_cut=6.0),
     "conv_uniform100k": dict(kind="conv", irreps_x="64x0e+64x1o+64x2e+64x3o+64x4e", L=4,
                              system="uniform", n=100000, box=100.0, r_cut=5.0),
+    # The collapsed-output comparison setting of [E3J] B.3: 2048 nodes, 45 edges per
+    # node, 128 channels per degree; uniform points in a periodic cube with the
+    # cutoff giving 45 neighbours on average (4/3 pi r^3 * 2047 / 20^3 = 45).
+    "conv_collapsed_l3": dict(kind="conv", irreps_x="128x0e+128x1o+128x2e+128x3o", L=3, system="uniform",
+                              n=2048, box=20.0, r_cut=3.475, collapse=True),
+    "conv_collapsed_l4": dict(kind="conv", irreps_x="128x0e+128x1o+128x2e+128x3o+128x4e", L=4,
+                              system="uniform", n=2048, box=20.0, r_cut=3.475, collapse=True),
 }
 for _c in CONFIGS.values():
     _c["irreps_y"] = _sh_irreps(_c["L"])

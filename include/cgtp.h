@@ -113,8 +113,10 @@ cgtp_status cgtp_plan_create(const char* irreps_x, const char* irreps_y, const c
  * output irrep are summed). Collapsed layout: one output block [2l3+1][mul] per
  * (l3, p3) that some path reaches, in the order of irreps_out (first
  * occurrence), where every path of that (l3, p3) adds its output; mul is the
- * multiplicity of the x blocks feeding it. The tensor product forward and
- * backward accept collapsed plans; the convolution does not (UNSUPPORTED).
+ * multiplicity of the x blocks feeding it. The tensor product and the
+ * convolution accept collapsed plans (the collapsed convolution forward adds
+ * the paths into the output in a fixed order: x block, slot chunk, path; with
+ * bf16 storage each addition rounds to bf16).
  * Errors: as cgtp_plan_create; INVALID_ARG for a bad selection; UNSUPPORTED
  * when the x blocks feeding one collapsed output differ in multiplicity or no
  * path is selected. */

@@ -5,7 +5,7 @@ backward, fp32 / bf16 / fp64, per-row and shared weights, at ragged batches; the
 L = 4 irreps of the 100k-point workload; the unaligned (one channel per lane)
 route; groups of different multiplicities; the full-size tp_large batch on
 sampled rows; x blocks no path reads (zero gradient); and the convolution with
-symmetric-only and skew-only plans (its collapsed form is rejected).
+every path selection and collapsed outputs (fused and general kernels).
 """
 
 import numpy as np
@@ -149,31 +149,46 @@ def small_graph(seed=0):
     return 60, row_ptr, src_s, vec[perm]
 
 
-@pytest.mark.parametrize("select", ["symmetric", "skew"])
-def test_conv_selected_plan_and_collapsed_rejected(select):
-    # skew: the 0e block reaches no output (0 + l2 + l2 is even), so its grad_x is zero
-    ix, iy, io = "16x0e+16x1o+16x2e", "0e+1o+2e", "0e+0o+1e+1o+2e+2o"
+CONV_PLANS = [
+    ("16x0e+16x1o+16x2e", "0e+1o+2e", "0e+0o+1e+1o+2e+2o", 2),          # fused kernels
+    ("8x0e+8x1o", "0e+1o+2e+3o", "0e+0o+1e+1o+2e+2o+3e+3o", 3),        # fused, L > l1
+    ("68x0e+68x2e", "0e+1o+2e", "0e+1o+2e+3o+4e", 2),                   # two channel chunks
+    ("3x1o+3x0e", "1o+1e", "0e+1o+1e+2e", -1),                          # general kernel (repeated degree)
+]
+
+
+@pytest.mark.parametrize("select", ["all", "symmetric", "skew"])
+@pytest.mark.parametrize("collapse", [False, True])
+@pytest.mark.parametrize("ix,iy,io,lmax", CONV_PLANS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f64"])
+def test_conv_variants(ix, iy, io, lmax, select, collapse, dtype):
+    """Convolution with selected paths and collapsed outputs (skew: the 0e block
+    reaches no output, 0 + l2 + l2 being even, so its grad_x is zero)."""
+    try:
+        L = Layout(ix, iy, io, select, collapse)
+    except ValueError:
+        pytest.skip("collapsed outputs fed by different multiplicities")
+    if not L.paths:
+        pytest.skip("no path in this selection")
     N, row_ptr, src, vec = small_graph(3)
     E = len(src)
-    L = Layout(ix, iy, io, select, False)
-    plan = cgtp.Plan(ix, iy, io, select=select)
+    plan = cgtp.Plan(ix, iy, io, dtype=dtype, select=select, collapse=collapse)
     graph = cgtp.Graph(N, torch.from_numpy(row_ptr.astype(np.int32)).cuda(),
                        torch.from_numpy(src.astype(np.int32)).cuda())
     x = synth.gaussian((N, L.dim_x), 7, synth.S_X)
-    Y = osh.real_sh(2, vec)
+    Y = osh.real_sh(lmax, vec) if lmax >= 0 else synth.gaussian((E, L.dim_y), 7, synth.S_Y)
     w = synth.gaussian((E, L.w_numel), 7, synth.S_W)
     g = synth.gaussian((N, L.dim_out), 7, synth.S_G)
-    dx_, dY_, dw_, dg_ = (dev(a, "f32") for a in (x, Y, w, g))
+    dx_, dY_, dw_, dg_ = (dev(a, dtype) for a in (x, Y, w, g))
     hx, hY, hw, hg = (host(t) for t in (dx_, dY_, dw_, dg_))
     scale = 0.37
+    tag = "%s %s collapse=%s %s" % (ix, select, collapse, dtype)
     out = plan.conv_forward(graph, dx_, dY_, dw_, scale)
     gx, gY, gw = plan.conv_backward(graph, dx_, dY_, dw_, scale, dg_)
     torch.cuda.synchronize()
-    assert_close(host(out), oconv.forward(L, row_ptr, src, hx, hY, hw, scale), out_blocks(L), "f32", "sym conv")
+    assert_close(host(out), oconv.forward(L, row_ptr, src, hx, hY, hw, scale), out_blocks(L), dtype,
+                 "conv " + tag)
     rdx, rdY, rdw = oconv.backward(L, row_ptr, src, hx, hY, hw, scale, hg)
-    assert_close(host(gx), rdx, x_blocks(L), "f32", "sym conv grad_x")
-    assert_close(host(gY), rdY, y_blocks(L), "f32", "sym conv grad_Y")
-    assert_close(host(gw), rdw, w_blocks(L), "f32", "sym conv grad_w")
-    cplan = cgtp.Plan(ix, iy, io, select=select, collapse=True)
-    with pytest.raises(cgtp.CgtpError):
-        cplan.conv_forward(graph, dx_, dY_, dw_, scale)
+    assert_close(host(gx), rdx, x_blocks(L), dtype, "conv grad_x " + tag)
+    assert_close(host(gY), rdY, y_blocks(L), dtype, "conv grad_Y " + tag)
+    assert_close(host(gw), rdw, w_blocks(L), dtype, "conv grad_w " + tag)
