@@ -40,6 +40,7 @@ namespace cgtp {
 // ------------------------------------------------- compile-time slot layout
 struct SlotT {
   int l2, l3, acc;  // acc: first accumulator register of the slot
+  int src;          // index of the slot in the plan's (l2, l3) slot table
 };
 
 constexpr int imin(int a, int b) { return a < b ? a : b; }
@@ -70,8 +71,53 @@ struct Slots {
     int k = 0, acc = 0;
     for (int l2 = 0; l2 <= L; ++l2)
       for (int l3 = idiff(L1, l2); l3 <= imin(L1 + l2, L); ++l3) {
-        a.p[k++] = SlotT{l2, l3, acc};
+        a.p[k] = SlotT{l2, l3, acc, k};
+        ++k;
         acc += 2 * l3 + 1;
+      }
+    return a;
+  }
+  static constexpr Arr arr = build();
+};
+
+// Slots of a plan with outputs collapsed by (l3, p3). Within one x block the
+// output parity of a slot is fixed by the parity of l2 (harmonics of degree
+// l2 have parity (-1)^l2), so the slots of one output type are those with
+// equal (l2 mod 2, l3): they are listed together and share one accumulator.
+constexpr int slot_regs_collapsed(int L1, int L) {
+  int n = 0;
+  for (int par = 0; par < 2; ++par)
+    for (int l3 = 0; l3 <= L; ++l3) {
+      bool any = false;
+      for (int l2 = par; l2 <= L; l2 += 2) any = any || (l3 >= idiff(L1, l2) && l3 <= imin(L1 + l2, L));
+      if (any) n += 2 * l3 + 1;
+    }
+  return n;
+}
+
+template <int L1, int L>
+struct SlotsC {
+  static constexpr int NS = slot_count(L1, L);
+  static constexpr int NACC = slot_regs_collapsed(L1, L);
+  struct Arr {
+    SlotT p[NS > 0 ? NS : 1];
+  };
+  static constexpr Arr build() {
+    Arr a{};
+    int k = 0, acc = 0;
+    for (int par = 0; par < 2; ++par)
+      for (int l3 = 0; l3 <= L; ++l3) {
+        bool any = false;
+        for (int l2 = par; l2 <= L; l2 += 2)
+          if (l3 >= idiff(L1, l2) && l3 <= imin(L1 + l2, L)) {
+            // index of (l2, l3) in the (l2, l3)-ordered table
+            int src = 0;
+            for (int q2 = 0; q2 < l2; ++q2) src += imin(L1 + q2, L) - idiff(L1, q2) + 1;
+            src += l3 - idiff(L1, l2);
+            a.p[k++] = SlotT{l2, l3, acc, src};
+            any = true;
+          }
+        if (any) acc += 2 * l3 + 1;
       }
     return a;
   }
@@ -97,6 +143,7 @@ struct ConvArgs {
   int block;    // x block of a degree-specialised launch
   int lg_log2;  // lanes per edge group (fused forward)
   int collapse; // outputs collapsed by (l3, p3): add into the (zeroed) output instead of storing
+  int coef_zero;  // offset of a run of zero coefficients (one whole pattern) in the table
   int yoff[kLmax + 1];
   double scale;
 };
@@ -120,12 +167,14 @@ __device__ __forceinline__ int64_t xcd_block() {
 // Slot chunks: consecutive slots whose accumulators fit a register budget of
 // `budget` entries per channel; the chunks of one block run as separate waves
 // of the same workgroup (they share the gathered rows through the caches).
-template <int L1, int L, int budget>
+// Slots that share an accumulator (collapsed outputs) stay in one chunk.
+template <typename S, int budget>
 struct Chunks {
-  using S = Slots<L1, L>;
+  static constexpr bool opens(int i) { return i == 0 || S::arr.p[i].acc != S::arr.p[i - 1].acc; }
   static constexpr int count() {
     int n = 0, acc = budget;
     for (int i = 0; i < S::NS; ++i) {
+      if (!opens(i)) continue;
       const int sz = 2 * S::arr.p[i].l3 + 1;
       if (acc + sz > budget) {
         ++n;
@@ -143,6 +192,7 @@ struct Chunks {
     Arr a{};
     int n = 0, acc = budget;
     for (int i = 0; i < S::NS; ++i) {
+      if (!opens(i)) continue;
       const int sz = 2 * S::arr.p[i].l3 + 1;
       if (acc + sz > budget) {
         a.begin[n++] = i;
@@ -155,6 +205,9 @@ struct Chunks {
   }
   static constexpr Arr arr = build();
 };
+
+template <int L1, int L, bool COL>
+using SlotsOf = typename std::conditional<COL, SlotsC<L1, L>, Slots<L1, L>>::type;
 
 #ifndef CGTP_CONV_ACC_REGS
 #define CGTP_CONV_ACC_REGS 64
@@ -177,11 +230,11 @@ constexpr int conv_budget() {
 // all loads of an edge are independent once its source index is known, and
 // the source indices of up to 64 edges are fetched with one load and handed
 // out with lane shuffles.
-template <typename T, typename A, int VEC, int L1, int L, int CH>
+template <typename T, typename A, int VEC, int L1, int L, bool COL, int CH>
 __device__ __forceinline__ void fwd_fused_chunk(const ConvArgs& a, int64_t n, const BlockDev& blk,
                                                 int c, bool valid, int g, int G) {
-  using S = Slots<L1, L>;
-  using CK = Chunks<L1, L, conv_budget<A, VEC>()>;
+  using S = SlotsOf<L1, L, COL>;
+  using CK = Chunks<S, conv_budget<A, VEC>()>;
   constexpr int s0 = CK::arr.begin[CH], s1 = CK::arr.begin[CH + 1];
   constexpr int acc0 = S::arr.p[s0].acc;
   constexpr int NACC = (s1 < S::NS ? S::arr.p[s1].acc : S::NACC) - acc0;
@@ -194,9 +247,11 @@ __device__ __forceinline__ void fwd_fused_chunk(const ConvArgs& a, int64_t n, co
   const int so = ldc(a.slot_off + a.block);
 #pragma unroll
   for (int s = 0; s < s1 - s0; ++s) {
-    pid[s] = ldc(a.slot_paths + so + s0 + s);
+    pid[s] = ldc(a.slot_paths + so + S::arr.p[s0 + s].src);
     woff[s] = pid[s] >= 0 ? ldc(&a.paths[pid[s]].w_off) : 0;
-    coff[s] = pid[s] >= 0 ? ldc(&a.paths[pid[s]].coef_off) : 0;
+    // an absent slot runs on zero coefficients when its accumulator is
+    // shared (collapsed outputs); otherwise on any in-bounds ones (discarded)
+    coff[s] = pid[s] >= 0 ? ldc(&a.paths[pid[s]].coef_off) : (COL ? a.coef_zero : 0);
   }
   const A* __restrict__ cf = static_cast<const A*>(a.coef);
   const T* __restrict__ X = static_cast<const T*>(a.x);
@@ -215,12 +270,31 @@ __device__ __forceinline__ void fwd_fused_chunk(const ConvArgs& a, int64_t n, co
       for (int m = 0; m < 2 * L1 + 1; ++m) VecIO<T, VEC>::load(X + j * a.dim_x + blk.x_off + m * blk.mul + c, xb[m]);
       const T* __restrict__ Ye = static_cast<const T*>(a.sh) + e * a.dim_y;
       const T* __restrict__ we = static_cast<const T*>(a.w) + e * a.W;
+      // harmonics of the edge: per l2 run of slots, or (collapsed order, where
+      // l2 alternates) every degree the chunk uses, once per edge
       A ycur[2 * L + 1];
+      A yall[COL ? (L + 1) * (L + 1) : 1];
+      if constexpr (COL) {
+        static_for<0, L + 1>([&](auto D2) {
+          constexpr int l2 = decltype(D2)::value;
+          constexpr bool used = [] {
+            for (int i = s0; i < s1; ++i)
+              if (S::arr.p[i].l2 == l2) return true;
+            return false;
+          }();
+          if constexpr (used) {
+            const int yo = a.yoff[l2];
+            const T* __restrict__ yp = yo >= 0 ? Ye + yo : static_cast<const T*>(a.coef);
+#pragma unroll
+            for (int m = 0; m < 2 * l2 + 1; ++m) yall[l2 * l2 + m] = to_acc<A>(yp[m]);
+          }
+        });
+      }
       static_for<s0, s1>([&](auto I) {
         constexpr int i = decltype(I)::value;
         constexpr SlotT st = S::arr.p[i];
         constexpr bool first_of_l2 = (i == s0) || (S::arr.p[i > 0 ? i - 1 : 0].l2 != st.l2);
-        if constexpr (first_of_l2) {
+        if constexpr (!COL && first_of_l2) {
           const int yo = a.yoff[st.l2];
           const T* __restrict__ yp = yo >= 0 ? Ye + yo : static_cast<const T*>(a.coef);
 #pragma unroll
@@ -230,9 +304,11 @@ __device__ __forceinline__ void fwd_fused_chunk(const ConvArgs& a, int64_t n, co
         VecIO<T, VEC>::load(we + woff[i - s0] + c, wv);
         A yb[2 * st.l2 + 1];
 #pragma unroll
-        for (int m = 0; m < 2 * st.l2 + 1; ++m) yb[m] = ycur[m];
+        for (int m = 0; m < 2 * st.l2 + 1; ++m) yb[m] = COL ? yall[st.l2 * st.l2 + m] : ycur[m];
         A t[2 * st.l3 + 1][VEC];
         fwd_core<L1, st.l2, st.l3, VEC, A>(xb, yb, cf + coff[i - s0], t);
+        // an absent slot (zero coefficients) adds zero to a shared accumulator
+        // for finite inputs
 #pragma unroll
         for (int m = 0; m < 2 * st.l3 + 1; ++m)
 #pragma unroll
@@ -249,41 +325,57 @@ __device__ __forceinline__ void fwd_fused_chunk(const ConvArgs& a, int64_t n, co
   static_for<s0, s1>([&](auto I) {
     constexpr int i = decltype(I)::value;
     constexpr SlotT st = S::arr.p[i];
-    if (pid[i - s0] >= 0) {
-      const PathDev pd = ldc(a.paths + pid[i - s0]);
+    if constexpr (!COL) {
+      if (pid[i - s0] >= 0) {
+        const PathDev pd = ldc(a.paths + pid[i - s0]);
 #pragma unroll
-      for (int m = 0; m < 2 * st.l3 + 1; ++m) {
-        A o[VEC];
+        for (int m = 0; m < 2 * st.l3 + 1; ++m) {
+          A o[VEC];
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) o[v] = sc * acc[st.acc - acc0 + m][v];
-        if (a.collapse) {  // several slots share the block: add in launch, chunk and slot order
-          A prev[VEC];
+          for (int v = 0; v < VEC; ++v) o[v] = sc * acc[st.acc - acc0 + m][v];
+          VecIO<T, VEC>::store(outn + pd.out_off + m * pd.mul + c, o);
+        }
+      }
+    } else if constexpr (i == s0 || S::arr.p[i > 0 ? i - 1 : 0].acc != st.acc) {
+      // first slot of an output type: the block of any of its present slots;
+      // x blocks of one output type add into it in launch order
+      int path = -1;
+      static_for<i, s1>([&](auto J) {
+        constexpr int jj = decltype(J)::value;
+        if constexpr (S::arr.p[jj].acc == st.acc) {
+          if (path < 0) path = pid[jj - s0];
+        }
+      });
+      if (path >= 0) {
+        const PathDev pd = ldc(a.paths + path);
+#pragma unroll
+        for (int m = 0; m < 2 * st.l3 + 1; ++m) {
+          A o[VEC], prev[VEC];
           VecIO<T, VEC>::load(outn + pd.out_off + m * pd.mul + c, prev);
 #pragma unroll
-          for (int v = 0; v < VEC; ++v) o[v] += prev[v];
+          for (int v = 0; v < VEC; ++v) o[v] = prev[v] + sc * acc[st.acc - acc0 + m][v];
+          VecIO<T, VEC>::store(outn + pd.out_off + m * pd.mul + c, o);
         }
-        VecIO<T, VEC>::store(outn + pd.out_off + m * pd.mul + c, o);
       }
     }
   });
 }
 
 // Work items: (receiver, slot chunk, channel chunk), slot chunks innermost so
-// one workgroup's waves read the same rows.
-template <typename T, typename A, int VEC, int L1, int L>
+// one workgroup's waves read the same rows. With collapsed outputs (COL) the
+// chunks hold whole output types, so no two waves of a launch add into the
+// same block.
+template <typename T, typename A, int VEC, int L1, int L, bool COL>
 __global__ __launch_bounds__(kBlock) void conv_fwd_fused_kernel(ConvArgs a) {
-  using CK = Chunks<L1, L, conv_budget<A, VEC>()>;
-  // with collapsed outputs one wave runs every slot chunk of its receiver in
-  // turn, so the additions into a shared block never overlap
-  const int nch = a.collapse ? 1 : CK::NCH;
+  using CK = Chunks<SlotsOf<L1, L, COL>, conv_budget<A, VEC>()>;
   const int64_t item = xcd_block() * kWaves + conv_wave_id();
-  const int64_t per_node = int64_t(nch) * a.nchunks;
+  const int64_t per_node = int64_t(CK::NCH) * a.nchunks;
   const int64_t pos = item / per_node;
   if (pos >= a.N) return;
   const int rem = int(item - pos * per_node);
   const int64_t n = a.order[pos];
-  const int cc = rem / nch;
-  const int ch = rem - cc * nch;
+  const int cc = rem / CK::NCH;
+  const int ch = rem - cc * CK::NCH;
   const BlockDev blk = ldc(a.blocks + a.block);
   const int lane = int(threadIdx.x & 63);
   const int LG = 1 << a.lg_log2;
@@ -293,7 +385,7 @@ __global__ __launch_bounds__(kBlock) void conv_fwd_fused_kernel(ConvArgs a) {
   const bool valid = c < blk.mul;
   static_for<0, CK::NCH>([&](auto C) {
     constexpr int CH = decltype(C)::value;
-    if (a.collapse || ch == CH) fwd_fused_chunk<T, A, VEC, L1, L, CH>(a, n, blk, c, valid, g, G);
+    if (ch == CH) fwd_fused_chunk<T, A, VEC, L1, L, COL, CH>(a, n, blk, c, valid, g, G);
   });
 }
 
@@ -608,7 +700,7 @@ constexpr int conv_vec(cgtp_dtype d) { return d == CGTP_F64 ? 2 : 4; }
 
 // Waves per receiver for the fused forward of x degree l1 and largest degree L.
 template <typename T>
-int conv_fused_chunks(int l1, int L) {
+int conv_fused_chunks(int l1, int L, bool col) {
   using A = typename AccOf<T>::type;
   constexpr int VEC = std::is_same<T, double>::value ? 2 : 4;
   int n = 0;
@@ -616,7 +708,8 @@ int conv_fused_chunks(int l1, int L) {
     static_for<0, kLmax + 1>([&](auto J) {
       constexpr int D = decltype(I)::value, M = decltype(J)::value;
       if constexpr (Slots<D, M>::NS > 0) {
-        if (l1 == D && L == M) n = Chunks<D, M, conv_budget<A, VEC>()>::NCH;
+        if (l1 == D && L == M)
+          n = col ? Chunks<SlotsC<D, M>, conv_budget<A, VEC>()>::NCH : Chunks<Slots<D, M>, conv_budget<A, VEC>()>::NCH;
       }
     });
   });
@@ -631,8 +724,12 @@ void conv_fwd_fused_typed(const ConvArgs& a, int l1, int L, dim3 grid, hipStream
     static_for<0, kLmax + 1>([&](auto J) {
       constexpr int D = decltype(I)::value, M = decltype(J)::value;
       if constexpr (Slots<D, M>::NS > 0) {
-        if (l1 == D && L == M)
-          hipLaunchKernelGGL((conv_fwd_fused_kernel<T, A, VEC, D, M>), grid, dim3(kBlock), 0, s, a);
+        if (l1 == D && L == M) {
+          if (a.collapse)
+            hipLaunchKernelGGL((conv_fwd_fused_kernel<T, A, VEC, D, M, true>), grid, dim3(kBlock), 0, s, a);
+          else
+            hipLaunchKernelGGL((conv_fwd_fused_kernel<T, A, VEC, D, M, false>), grid, dim3(kBlock), 0, s, a);
+        }
       }
     });
   });
@@ -646,7 +743,7 @@ void conv_fwd_general_typed(const ConvArgs& a, dim3 grid, hipStream_t s) {
 #define CGTP_CONV_EXTERN(T)                                                                   \
   extern template void conv_fwd_fused_typed<T>(const ConvArgs&, int, int, dim3, hipStream_t); \
   extern template void conv_fwd_general_typed<T>(const ConvArgs&, dim3, hipStream_t);         \
-  extern template int conv_fused_chunks<T>(int, int);                                        \
+  extern template int conv_fused_chunks<T>(int, int, bool);                                  \
   extern template void conv_bwd_fused_typed<T>(const ConvArgs&, const ConvBwdArgs&, int, int, dim3, size_t, \
                                                hipStream_t);                                   \
   extern template size_t conv_bwd_fused_lds<T>(int, int, int);

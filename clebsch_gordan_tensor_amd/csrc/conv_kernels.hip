@@ -69,6 +69,7 @@ ConvArgs make_conv_args(cgtp_plan_s* plan, const DevTables& t, const cgtp_graph_
   a.npaths = int(plan->paths.size());
   a.nchunks = (plan->max_mul + 63) / 64;
   a.L = plan->conv_L;
+  a.coef_zero = int(plan->coef64.size());
   for (int l = 0; l <= kLmax; ++l) a.yoff[l] = plan->yoff_by_l[l];
   return a;
 }
@@ -100,7 +101,7 @@ void fwd_typed(cgtp_plan_s* plan, ConvArgs a, hipStream_t s) {
     a.block = int(b);
     a.lg_log2 = lg;
     a.nchunks = (lanes + (1 << lg) - 1) >> lg;
-    const int nch = a.collapse ? 1 : conv_fused_chunks<T>(blk.l1, plan->conv_L);
+    const int nch = conv_fused_chunks<T>(blk.l1, plan->conv_L, a.collapse != 0);
     const int64_t items = a.N * int64_t(nch) * a.nchunks;
     conv_fwd_fused_typed<T>(a, blk.l1, plan->conv_L, dim3(unsigned((items + kWaves - 1) / kWaves)), s);
     CGTP_CHECK_HIP(hipGetLastError());

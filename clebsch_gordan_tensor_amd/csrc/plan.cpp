@@ -392,10 +392,11 @@ const DevTables& plan_tables(cgtp_plan_s* plan) {
     bd.push_back(BlockDev{b.l1, b.mul, b.x_off, b.path_begin, b.path_end, 0, 0, 0});
   DevTables t;
   const bool f64 = plan->dtype == CGTP_F64;
-  // The device table is zero-padded to at least one whole pattern of the
-  // largest degrees, so a kernel may run a pattern from offset 0 for a slot
-  // the plan does not have (its results are discarded).
-  const size_t ncoef = std::max<size_t>(plan->coef64.size(), size_t(max_pattern_coefs(kLmax)));
+  // The device table is followed by one whole pattern of the largest degrees
+  // in zeros: a kernel may run a pattern from offset 0 for a slot the plan
+  // does not have (its results discarded) or from that zero run (its results
+  // added as zeros).
+  const size_t ncoef = plan->coef64.size() + size_t(max_pattern_coefs(kLmax));
   std::vector<double> c64(plan->coef64);
   std::vector<float> c32(plan->coef32);
   c64.resize(ncoef, 0.0);
