@@ -54,6 +54,29 @@ def backward(L, row_ptr, src, x, Y, w, scale, g):
     return dx, dY, dw
 
 
+def double_backward(L, row_ptr, src, x, Y, w, scale, g, gx=None, gY=None, gw=None):
+    """Reverse mode of ``backward`` (twice-differentiable convolution, e.g. for
+    training on forces): cotangents of (x, Y, w, g) for cotangents (gx, gY, gw)
+    of (dx, dY, dw); a missing one counts as zero.
+
+    The backward is the tensor-product backward on the gathered rows
+    (x[src], Y, w, scale * g[dst]) followed by a scatter-add of dx over src, so
+    its reverse mode gathers gx over src, runs the tensor-product double
+    backward per edge, and scatters: ddx over src, ddg (times scale) over dst.
+    """
+    x = np.asarray(x, np.float64)
+    dst = dst_of_csr(row_ptr)
+    src = np.asarray(src)
+    ge = scale * np.asarray(g, np.float64)[dst]
+    gxe = None if gx is None else np.asarray(gx, np.float64)[src]
+    ddxe, ddY, ddw, ddge = tp.double_backward(L, x[src], Y, w, ge, gxe, gY, gw)
+    ddx = np.zeros_like(x)
+    np.add.at(ddx, src, ddxe)
+    ddg = np.zeros((len(row_ptr) - 1, L.dim_out))
+    np.add.at(ddg, dst, scale * ddge)
+    return ddx, ddY, ddw, ddg
+
+
 def avg_neighbors_scale(N, E):
     """1 / sqrt(E / N): the sqrt(num_neighbors) normalisation of [V2106] with the
     average degree of the built graph."""

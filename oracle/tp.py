@@ -93,5 +93,44 @@ def backward(L, x, y, w, g):
     return dx, dy, dw
 
 
+def double_backward(L, x, y, w, g, gx=None, gy=None, gw=None):
+    """Reverse mode of ``backward``: cotangents of (x, y, w, g) for cotangents
+    (gx, gy, gw) of its outputs (dx, dy, dw); a missing one counts as zero.
+
+    The backward's outputs are the transposed maps of [E3J] E.1, each linear in
+    the other three tensors; differentiating
+      S = <gx, dx> + <gy, dy> + <gw, dw>
+    entry by entry gives, per path (C the CG block, u the channel):
+      ddx[m1, u] = sum C (gy[m2] g[m3, u] w[u] + y[m2] g[m3, u] gw[u])
+      ddy[m2]    = sum C (gx[m1, u] g[m3, u] w[u] + x[m1, u] g[m3, u] gw[u])
+      ddw[u]     = sum C (gx[m1, u] y[m2] + x[m1, u] gy[m2]) g[m3, u]
+      ddg[m3, u] = sum C (gx[m1, u] y[m2] w[u] + x[m1, u] gy[m2] w[u] + x[m1, u] y[m2] gw[u])
+    (sums over the indices not on the left; a shared w gets ddw summed over rows).
+    """
+    x, y, w, g = (np.asarray(t, np.float64) for t in (x, y, w, g))
+    B = x.shape[0]
+    z = lambda t, like: np.zeros_like(like) if t is None else np.asarray(t, np.float64)
+    gx, gy, gw = z(gx, x), z(gy, y), z(gw, w)
+    ddx, ddy, ddg = np.zeros_like(x), np.zeros_like(y), np.zeros((B, L.dim_out))
+    ddw_rows = np.zeros((B, L.w_numel))
+    for p in L.paths:
+        C = cg_real(p["l1"], p["l2"], p["l3"])
+        xb, ax = L.x_block(x, p["i1"]), L.x_block(gx, p["i1"])
+        yb, by = L.y_block(y, p["i2"]), L.y_block(gy, p["i2"])
+        gb = L.out_block(g, p)
+        wb, cw = _w_of(L, w, p, B), _w_of(L, gw, p, B)
+        L.x_block(ddx, p["i1"])[...] += (np.einsum("abc,zb,zcu,zu->zau", C, by, gb, wb)
+                                         + np.einsum("abc,zb,zcu,zu->zau", C, yb, gb, cw))
+        L.y_block(ddy, p["i2"])[...] += (np.einsum("abc,zau,zcu,zu->zb", C, ax, gb, wb)
+                                         + np.einsum("abc,zau,zcu,zu->zb", C, xb, gb, cw))
+        ddw_rows[:, p["w_off"]:p["w_off"] + p["mul"]] = (np.einsum("abc,zau,zb,zcu->zu", C, ax, yb, gb)
+                                                         + np.einsum("abc,zau,zb,zcu->zu", C, xb, by, gb))
+        L.out_block(ddg, p)[...] += (np.einsum("abc,zau,zb,zu->zcu", C, ax, yb, wb)
+                                     + np.einsum("abc,zau,zb,zu->zcu", C, xb, by, wb)
+                                     + np.einsum("abc,zau,zb,zu->zcu", C, xb, yb, cw))
+    ddw = ddw_rows if w.ndim == 2 else ddw_rows.sum(axis=0)
+    return ddx, ddy, ddw, ddg
+
+
 def make_layout(irreps_x, irreps_y, irreps_out, select="all", collapse=False):
     return Layout(irreps_x, irreps_y, irreps_out, select, collapse)
