@@ -20,7 +20,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 F32, F64, BF16 = 0, 1, 2
 W_SHARED, W_PER_ROW = 0, 1
-OP_TP_BACKWARD, OP_CONV_BACKWARD = 1, 2
+OP_TP_BACKWARD, OP_CONV_BACKWARD, OP_TP_DOUBLE_BACKWARD, OP_CONV_DOUBLE_BACKWARD = 1, 2, 3, 4
 LMAX = 4
 
 _c_i64 = ctypes.c_int64
@@ -49,6 +49,9 @@ _SIGS = {
     "cgtp_graph_destroy": ([_vp], ctypes.c_int),
     "cgtp_graph_transpose": ([_vp, _vp, _vp, _vp], ctypes.c_int),
     "cgtp_conv_forward": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_double, _vp, _vp], ctypes.c_int),
+    "cgtp_tp_double_backward": ([_vp, _c_i64] + [_vp] * 12 + [ctypes.c_size_t, _vp], ctypes.c_int),
+    "cgtp_conv_double_backward": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_double] + [_vp] * 9 + [ctypes.c_size_t, _vp],
+                                  ctypes.c_int),
     "cgtp_conv_backward": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_double, _vp, _vp, _vp, _vp, _vp,
                             ctypes.c_size_t, _vp], ctypes.c_int),
     "cgtp_workspace_size": ([_vp, _vp, _c_i64, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
@@ -238,6 +241,60 @@ class Plan:
         _check(_lib.cgtp_conv_forward(self._h, graph._h, _ptr(x), _ptr(sh), _ptr(w), float(scale),
                                       _ptr(out), _stream(x)), "cgtp_conv_forward")
         return out
+
+    def _double_outputs(self, shapes, need, out, dt, device):
+        torch = _torch()
+        res = []
+        for k in range(4):
+            if not need[k]:
+                res.append(None)
+                continue
+            t = out[k] if out[k] is not None else torch.empty(shapes[k], dtype=dt, device=device)
+            res.append(_need(t, shapes[k], dt, "double-backward output"))
+        return res
+
+    def tp_double_backward(self, x, y, w, grad_out, gg=(None, None, None), need=(True, True, True, True),
+                           out=(None, None, None, None), ws=None):
+        """Cotangents of (x, y, w, grad_out) for cotangents gg of the backward's
+        (grad_x, grad_y, grad_w) (cgtp_tp_double_backward); None counts as zero."""
+        torch = _torch()
+        B = x.shape[0]
+        dt = self.torch_dtype
+        shapes = [(B, self.dim_x), (B, self.dim_y), self._w_shape(B), (B, self.dim_out)]
+        for t, shp, nm in zip((x, y, w, grad_out), shapes, ("x", "y", "w", "grad_out")):
+            _need(t, shp, dt, nm)
+        for t, shp in zip(gg, shapes[:3]):
+            if t is not None:
+                _need(t, shp, dt, "cotangent")
+        res = self._double_outputs(shapes, need, out, dt, x.device)
+        nws = self.workspace_size(OP_TP_DOUBLE_BACKWARD, B)
+        if ws is None:
+            ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device)
+        _check(_lib.cgtp_tp_double_backward(self._h, B, _ptr(x), _ptr(y), _ptr(w), _ptr(grad_out),
+                                            *[_ptr(t) for t in gg], *[_ptr(t) for t in res], _ptr(ws), ws.numel(),
+                                            _stream(x)), "cgtp_tp_double_backward")
+        return tuple(res)
+
+    def conv_double_backward(self, graph, x, sh, w, scale, grad_out, gg=(None, None, None),
+                             need=(True, True, True, True), out=(None, None, None, None), ws=None):
+        """Cotangents of (x, sh, w, grad_out) for cotangents gg of the
+        convolution backward's (grad_x, grad_sh, grad_w) (cgtp_conv_double_backward)."""
+        torch = _torch()
+        dt = self.torch_dtype
+        shapes = [(graph.N, self.dim_x), (graph.E, self.dim_y), (graph.E, self.w_numel), (graph.N, self.dim_out)]
+        for t, shp, nm in zip((x, sh, w, grad_out), shapes, ("x", "sh", "w", "grad_out")):
+            _need(t, shp, dt, nm)
+        for t, shp in zip(gg, shapes[:3]):
+            if t is not None:
+                _need(t, shp, dt, "cotangent")
+        res = self._double_outputs(shapes, need, out, dt, x.device)
+        nws = self.workspace_size(OP_CONV_DOUBLE_BACKWARD, graph=graph)
+        if ws is None:
+            ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device)
+        _check(_lib.cgtp_conv_double_backward(self._h, graph._h, _ptr(x), _ptr(sh), _ptr(w), float(scale),
+                                              _ptr(grad_out), *[_ptr(t) for t in gg], *[_ptr(t) for t in res],
+                                              _ptr(ws), ws.numel(), _stream(x)), "cgtp_conv_double_backward")
+        return tuple(res)
 
     def conv_backward(self, graph, x, sh, w, scale, grad_out, need=(True, True, True),
                       out=(None, None, None), ws=None):

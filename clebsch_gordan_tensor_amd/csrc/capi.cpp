@@ -171,6 +171,35 @@ cgtp_status cgtp_tp_backward(cgtp_plan plan, int64_t B, const void* x, const voi
   });
 }
 
+cgtp_status cgtp_tp_double_backward(cgtp_plan plan, int64_t B, const void* x, const void* y, const void* w,
+                                    const void* grad_out, const void* gg_x, const void* gg_y, const void* gg_w,
+                                    void* out_x, void* out_y, void* out_w, void* out_grad_out, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  return guarded([&] {
+    need(plan != nullptr, "NULL plan");
+    need(B >= 0, "B < 0");
+    if (B == 0) return;
+    need(x && y && w && grad_out, "NULL input tensor");
+    tp_double_backward_launch(plan, B, x, y, w, grad_out, gg_x, gg_y, gg_w, out_x, out_y, out_w, out_grad_out, ws,
+                              ws_bytes, as_stream(stream));
+  });
+}
+
+cgtp_status cgtp_conv_double_backward(cgtp_plan plan, cgtp_graph graph, const void* x, const void* sh,
+                                      const void* w, double scale, const void* grad_out, const void* gg_x,
+                                      const void* gg_sh, const void* gg_w, void* out_x, void* out_sh, void* out_w,
+                                      void* out_grad_out, void* ws, size_t ws_bytes, void* stream) {
+  return guarded([&] {
+    need(plan != nullptr && graph != nullptr, "NULL plan or graph");
+    if (plan->wkind != CGTP_W_PER_ROW)
+      throw Error{CGTP_ERR_UNSUPPORTED, "the convolution needs per-edge weights (CGTP_W_PER_ROW)"};
+    if (graph->N == 0) return;
+    need(x && grad_out && (graph->E == 0 || (sh && w)), "NULL input tensor");
+    conv_double_backward_launch(plan, graph, x, sh, w, scale, grad_out, gg_x, gg_sh, gg_w, out_x, out_sh, out_w,
+                                out_grad_out, ws, ws_bytes, as_stream(stream));
+  });
+}
+
 cgtp_status cgtp_workspace_size(cgtp_plan plan, cgtp_graph graph, int64_t B, int op, size_t* bytes) {
   return guarded([&] {
     need(plan != nullptr && bytes != nullptr, "NULL argument");
@@ -180,6 +209,12 @@ cgtp_status cgtp_workspace_size(cgtp_plan plan, cgtp_graph graph, int64_t B, int
     } else if (op == CGTP_OP_CONV_BACKWARD) {
       need(graph != nullptr, "graph is NULL");
       *bytes = conv_backward_ws_bytes(plan, graph);
+    } else if (op == CGTP_OP_TP_DOUBLE_BACKWARD) {
+      need(B >= 0, "B < 0");
+      *bytes = tp_double_backward_ws_bytes(plan, B);
+    } else if (op == CGTP_OP_CONV_DOUBLE_BACKWARD) {
+      need(graph != nullptr, "graph is NULL");
+      *bytes = conv_double_backward_ws_bytes(plan, graph);
     } else {
       throw Error{CGTP_ERR_INVALID_ARG, "unknown op"};
     }

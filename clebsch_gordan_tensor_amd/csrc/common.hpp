@@ -128,6 +128,11 @@ void tp_backward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void*
                         const void* w, const void* g, void* dx, void* dy, void* dw, void* ws,
                         size_t ws_bytes, hipStream_t stream);
 size_t tp_backward_ws_bytes(const cgtp_plan_s* plan, int64_t B);
+// Double backward (double_backward.hip).
+size_t tp_double_backward_ws_bytes(const cgtp_plan_s* plan, int64_t B);
+void tp_double_backward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* y, const void* w,
+                               const void* g, const void* gx, const void* gy, const void* gw, void* ddx,
+                               void* ddy, void* ddw, void* ddg, void* ws, size_t ws_bytes, hipStream_t s);
 
 // Backward over generic rows: row r reads x row x_idx[r] (or r), grad_out row
 // g_idx[r] (or r) times g_scale, y/w row r; writes grad_x row r either in the

@@ -29,6 +29,11 @@ void conv_backward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* 
                           const void* w, double scale, const void* grad_out, void* grad_x,
                           void* grad_sh, void* grad_w, void* ws, size_t ws_bytes, hipStream_t s);
 size_t conv_backward_ws_bytes(const cgtp_plan_s* plan, const cgtp_graph_s* g);
+size_t conv_double_backward_ws_bytes(const cgtp_plan_s* plan, const cgtp_graph_s* g);
+void conv_double_backward_launch(cgtp_plan_s* plan, const cgtp_graph_s* gr, const void* x, const void* sh,
+                                 const void* w, double scale, const void* g, const void* gx, const void* gsh,
+                                 const void* gw, void* ddx, void* ddsh, void* ddw, void* ddg, void* ws,
+                                 size_t ws_bytes, hipStream_t s);
 
 void sh_forward_launch(int lmax, cgtp_dtype dtype, int64_t n, const void* vec, void* sh, hipStream_t s);
 void sh_backward_launch(int lmax, cgtp_dtype dtype, int64_t n, const void* vec, const void* grad_sh,

@@ -79,7 +79,12 @@ typedef enum { CGTP_W_SHARED = 0, CGTP_W_PER_ROW = 1 } cgtp_wkind;
 typedef enum { CGTP_PATHS_ALL = 0, CGTP_PATHS_SYMMETRIC = 1, CGTP_PATHS_SKEW = 2 } cgtp_paths;
 
 /* Operations for cgtp_workspace_size. */
-typedef enum { CGTP_OP_TP_BACKWARD = 1, CGTP_OP_CONV_BACKWARD = 2 } cgtp_op;
+typedef enum {
+  CGTP_OP_TP_BACKWARD = 1,
+  CGTP_OP_CONV_BACKWARD = 2,
+  CGTP_OP_TP_DOUBLE_BACKWARD = 3,
+  CGTP_OP_CONV_DOUBLE_BACKWARD = 4
+} cgtp_op;
 
 typedef struct cgtp_plan_s* cgtp_plan;
 typedef struct cgtp_graph_s* cgtp_graph;
@@ -162,6 +167,26 @@ cgtp_status cgtp_tp_backward(cgtp_plan plan, int64_t B, const void* x, const voi
                              const void* grad_out, void* grad_x, void* grad_y, void* grad_w,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* Double backward: the reverse mode of cgtp_tp_backward (needed to train on
+ * quantities that are themselves gradients, such as forces). For cotangents
+ * (gg_x, gg_y, gg_w) of (grad_x, grad_y, grad_w) it writes the cotangents of
+ * (x, y, w, grad_out). The backward's outputs are each linear in the other
+ * three tensors (E3J appendix E.1), so with S = <gg_x, grad_x> + <gg_y,
+ * grad_y> + <gg_w, grad_w>:
+ *   out_grad_out = TP(gg_x, y, w) + TP(x, gg_y, w) + TP(x, y, gg_w)
+ *   out_x = back(x, gg_y, w, g).grad_x + back(x, y, gg_w, g).grad_x
+ *   out_y = back(gg_x, y, w, g).grad_y + back(x, y, gg_w, g).grad_y
+ *   out_w = back(gg_x, y, w, g).grad_w + back(x, gg_y, w, g).grad_w
+ * summed in that order. Shapes are those of x, y, w, grad_out (gg_w and out_w
+ * are [W] for SHARED plans). A NULL cotangent counts as zero; a NULL output is
+ * not computed; outputs no cotangent reaches are written as zeros. Needs
+ * cgtp_workspace_size(plan, NULL, B, CGTP_OP_TP_DOUBLE_BACKWARD) bytes of
+ * workspace (partial results). Errors: WORKSPACE, INVALID_ARG (null inputs). */
+cgtp_status cgtp_tp_double_backward(cgtp_plan plan, int64_t B, const void* x, const void* y, const void* w,
+                                    const void* grad_out, const void* gg_x, const void* gg_y, const void* gg_w,
+                                    void* out_x, void* out_y, void* out_w, void* out_grad_out, void* ws,
+                                    size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------ graphs */
 
 /* COO -> CSR by destination. Sort key (dst, src), ties in input order (so
@@ -212,6 +237,19 @@ cgtp_status cgtp_conv_forward(cgtp_plan plan, cgtp_graph graph, const void* x, c
 cgtp_status cgtp_conv_backward(cgtp_plan plan, cgtp_graph graph, const void* x, const void* sh,
                                const void* w, double scale, const void* grad_out, void* grad_x,
                                void* grad_sh, void* grad_w, void* ws, size_t ws_bytes, void* stream);
+
+/* Double backward of the convolution, the reverse mode of
+ * cgtp_conv_backward: the same sums as cgtp_tp_double_backward with the
+ * convolution's forward and backward (scale included), for cotangents gg_x
+ * [N][dim_x], gg_sh [E][dim_y], gg_w [E][W] (CSR order) of (grad_x, grad_sh,
+ * grad_w); outputs out_x [N][dim_x], out_sh [E][dim_y], out_w [E][W],
+ * out_grad_out [N][dim_out]. NULL cotangents count as zero, NULL outputs are
+ * skipped. Workspace: cgtp_workspace_size(plan, graph, 0,
+ * CGTP_OP_CONV_DOUBLE_BACKWARD) bytes. */
+cgtp_status cgtp_conv_double_backward(cgtp_plan plan, cgtp_graph graph, const void* x, const void* sh,
+                                      const void* w, double scale, const void* grad_out, const void* gg_x,
+                                      const void* gg_sh, const void* gg_w, void* out_x, void* out_sh, void* out_w,
+                                      void* out_grad_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes for op (graph may be NULL for the tensor product, B is
  * ignored for the convolution). */
