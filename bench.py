@@ -22,7 +22,7 @@ the fused convolution (forward and backward, fp32) on the 1000- and
 8000-molecule water boxes (the latter with the harmonics forward/backward of
 the force chain), the 100,000-point uniform cloud, and 2048 points with 45
 neighbours and 128 channels per degree with outputs collapsed by (l3, p3)
-(L = 3 and 4).
+(L = 3 and 4), and the water8k double backward in the force-training shape.
 """
 
 import argparse
@@ -392,6 +392,40 @@ def conv_bench(args, torch, cgtp, synth, name, steps, forces=False):
     return res
 
 
+def double_backward_bench(args, torch, cgtp, synth, name="conv_water8k"):
+    """Convolution double backward in the force-training shape (cotangents on
+    grad_sh and grad_w, all four outputs) on one full-size workload, next to its
+    forward and backward."""
+    wl = ConvWorkload(torch, cgtp, synth, name)
+    p, E = wl.plan, wl.E
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    gY = torch.randn(wl.Y.shape, generator=gen, device="cuda")
+    gw = torch.randn(wl.w.shape, generator=gen, device="cuda")
+    outs = (torch.empty_like(wl.x), torch.empty_like(wl.Y), torch.empty_like(wl.w), torch.empty_like(wl.gout))
+    ws = torch.empty(p.workspace_size(cgtp.OP_CONV_DOUBLE_BACKWARD, graph=wl.graph), dtype=torch.uint8,
+                     device="cuda")
+
+    def dd():
+        p.conv_double_backward(wl.graph, wl.x, wl.Y, wl.w, wl.scale, wl.gout, gg=(None, gY, gw), out=outs, ws=ws)
+
+    tf, tb, td = KernelTimer(torch), KernelTimer(torch), KernelTimer(torch)
+    wl.fwd()
+    wl.bwd()
+    dd()
+    for _ in range(3):
+        tf(wl.fwd)
+        tb(wl.bwd)
+        td(dd)
+    torch.cuda.synchronize()
+    res = dict(workload=name, E=E, cotangents="grad_sh, grad_w", fwd_ms=round(tf.mean_ms(), 3),
+               bwd_ms=round(tb.mean_ms(), 3), double_bwd_ms=round(td.mean_ms(), 3),
+               calls="2 forwards + 2 backwards + 3 adds", workspace_GB=round(ws.numel() / 1e9, 2))
+    del wl, outs, ws, gY, gw
+    torch.cuda.empty_cache()
+    return res
+
+
 def tp_variants_bench(args, torch, cgtp, synth):
     """tp_large fp32 with outputs collapsed by (l3, p3), all / symmetric / skew
     paths: forward and backward call times and algorithmic GB/s."""
@@ -506,6 +540,7 @@ def main():
         for name in ("conv_water1k", "conv_water8k", "conv_uniform100k", "conv_collapsed_l3", "conv_collapsed_l4"):
             extra[name] = conv_bench(args, torch, cgtp, synth, name, max(2, min(args.steps, 5)),
                                      forces=name == "conv_water8k")
+        extra["conv_water8k_double_backward"] = double_backward_bench(args, torch, cgtp, synth)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, synth)
     line = {
         "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
