@@ -52,6 +52,7 @@ _SIGS = {
     "cgtp_tp_double_backward": ([_vp, _c_i64] + [_vp] * 12 + [ctypes.c_size_t, _vp], ctypes.c_int),
     "cgtp_conv_double_backward": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_double] + [_vp] * 9 + [ctypes.c_size_t, _vp],
                                   ctypes.c_int),
+    "cgtp_graph_create_ex": ([_c_i64, _c_i64, _vp, _vp, ctypes.c_int32, _vp, ctypes.POINTER(_vp)], ctypes.c_int),
     "cgtp_conv_backward": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_double, _vp, _vp, _vp, _vp, _vp,
                             ctypes.c_size_t, _vp], ctypes.c_int),
     "cgtp_workspace_size": ([_vp, _vp, _c_i64, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
@@ -396,16 +397,21 @@ class Graph:
     """A CSR-by-destination graph handle (cgtp_graph_create). Keeps the CSR
     tensors alive for as long as the handle exists."""
 
-    def __init__(self, N, row_ptr, src):
+    def __init__(self, N, row_ptr, src, pad_node=None):
         torch = _torch()
         _need(row_ptr, (N + 1,), torch.int32, "row_ptr")
         E = src.shape[0]
         _need(src, (E,), torch.int32, "src")
         self.N, self.E = int(N), int(E)
         self.row_ptr, self.src = row_ptr, src
+        self.pad_node = pad_node
         h = _vp()
-        _check(_lib.cgtp_graph_create(self.N, self.E, _ptr(row_ptr), _ptr(src), _stream(row_ptr),
-                                      ctypes.byref(h)), "cgtp_graph_create")
+        if pad_node is None:
+            _check(_lib.cgtp_graph_create(self.N, self.E, _ptr(row_ptr), _ptr(src), _stream(row_ptr),
+                                          ctypes.byref(h)), "cgtp_graph_create")
+        else:
+            _check(_lib.cgtp_graph_create_ex(self.N, self.E, _ptr(row_ptr), _ptr(src), int(pad_node),
+                                             _stream(row_ptr), ctypes.byref(h)), "cgtp_graph_create_ex")
         self._h = h
 
     def __del__(self):
@@ -417,10 +423,10 @@ class Graph:
     def transpose(self):
         torch = _torch()
         col_ptr = torch.empty(self.N + 1, dtype=torch.int32, device=self.row_ptr.device)
-        eid = torch.empty(self.E, dtype=torch.int32, device=self.row_ptr.device)
+        eid = torch.empty(max(self.E, 1), dtype=torch.int32, device=self.row_ptr.device)
         _check(_lib.cgtp_graph_transpose(self._h, _ptr(col_ptr), _ptr(eid), _stream(col_ptr)),
                "cgtp_graph_transpose")
-        return col_ptr, eid
+        return col_ptr, eid[:int(col_ptr[-1].item()) if self.N > 0 else 0]
 
 
 def csr_from_coo(N, src, dst):

@@ -245,6 +245,19 @@ cgtp_status cgtp_graph_create(int64_t N, int64_t E, const int32_t* row_ptr, cons
   });
 }
 
+cgtp_status cgtp_graph_create_ex(int64_t N, int64_t E, const int32_t* row_ptr, const int32_t* src,
+                                 int32_t pad_node, void* stream, cgtp_graph* out) {
+  return guarded([&] {
+    need(out != nullptr, "out handle is NULL");
+    *out = nullptr;
+    need(N >= 0 && E >= 0, "negative size");
+    need(N < INT32_MAX && E < INT32_MAX, "graph too large for int32 indices");
+    need(row_ptr != nullptr, "row_ptr is NULL");
+    need(E == 0 || src != nullptr, "src is NULL");
+    *out = graph_create(N, E, row_ptr, src, as_stream(stream), pad_node);
+  });
+}
+
 cgtp_status cgtp_graph_destroy(cgtp_graph graph) {
   return guarded([&] {
     if (graph) graph_destroy(graph);

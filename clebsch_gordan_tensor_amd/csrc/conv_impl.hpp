@@ -144,6 +144,7 @@ struct ConvArgs {
   int lg_log2;  // lanes per edge group (fused forward)
   int collapse; // outputs collapsed by (l3, p3): add into the (zeroed) output instead of storing
   int coef_zero;  // offset of a run of zero coefficients (one whole pattern) in the table
+  int pad;        // padding node (its incoming edges are skipped) or -1
   int yoff[kLmax + 1];
   double scale;
 };
@@ -256,7 +257,7 @@ __device__ __forceinline__ void fwd_fused_chunk(const ConvArgs& a, int64_t n, co
   const A* __restrict__ cf = static_cast<const A*>(a.coef);
   const T* __restrict__ X = static_cast<const T*>(a.x);
   const int lane = int(threadIdx.x & 63);
-  const int32_t e0 = a.row_ptr[n], e1 = a.row_ptr[n + 1];
+  const int32_t e0 = a.row_ptr[n], e1 = n == a.pad ? e0 : a.row_ptr[n + 1];  // padding edges skipped
   for (int32_t base = e0; base < e1; base += 64) {
     const int nb = e1 - base < 64 ? e1 - base : 64;  // uniform over the wave
     const int32_t srcv = lane < nb ? a.src[base + lane] : 0;
@@ -397,7 +398,7 @@ __device__ __forceinline__ void fwd_general_path(const ConvArgs& a, int64_t n, c
   for (int m = 0; m < 2 * L3 + 1; ++m) acc[m] = A(0);
   const A* __restrict__ cf = static_cast<const A*>(a.coef) + pd.coef_off;
   const T* __restrict__ X = static_cast<const T*>(a.x);
-  const int32_t e0 = a.row_ptr[n], e1 = a.row_ptr[n + 1];
+  const int32_t e0 = a.row_ptr[n], e1 = n == a.pad ? e0 : a.row_ptr[n + 1];  // padding edges skipped
   for (int32_t e = e0; e < e1; ++e) {
     const int64_t j = a.src[e];
     A xb[2 * L1 + 1][1];
@@ -526,7 +527,7 @@ __global__ __launch_bounds__(kBlock) void conv_bwd_fused_kernel(ConvArgs a, Conv
   const bool valid = c < U;
   const A* __restrict__ cf = static_cast<const A*>(a.coef);
   const T* __restrict__ X = static_cast<const T*>(a.x);
-  const int32_t e0 = a.row_ptr[n], e1 = a.row_ptr[n + 1];
+  const int32_t e0 = a.row_ptr[n], e1 = n == a.pad ? e0 : a.row_ptr[n + 1];  // padding edges skipped
   const int lane = int(threadIdx.x & 63);
   const int cl = valid ? c : 0;  // lanes past the channels load channel 0 and use zeros
   // Source indices of up to 64 edges come with one load and are handed out by

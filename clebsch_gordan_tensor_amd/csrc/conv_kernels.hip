@@ -70,6 +70,7 @@ ConvArgs make_conv_args(cgtp_plan_s* plan, const DevTables& t, const cgtp_graph_
   a.nchunks = (plan->max_mul + 63) / 64;
   a.L = plan->conv_L;
   a.coef_zero = int(plan->coef64.size());
+  a.pad = g->pad;
   for (int l = 0; l <= kLmax; ++l) a.yoff[l] = plan->yoff_by_l[l];
   return a;
 }
@@ -236,24 +237,44 @@ void conv_backward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* 
       throw Error{CGTP_ERR_WORKSPACE, "conv_backward needs " + std::to_string(need) + " workspace bytes"};
   }
   if (!grad_x && !grad_sh && !grad_w) return;
+  const size_t es = dtype_size(plan->dtype), as = acc_size(plan->dtype);
+  // padding edges: their gradients are zero (their partials of grad_x are
+  // not in the transpose, so dx_gather never reads them)
+  auto zero_padding = [&] {
+    const int64_t np = g->pad_e1 - g->pad_e0;
+    if (np == 0) return;
+    if (grad_sh) zero_rows(static_cast<char*>(grad_sh) + g->pad_e0 * plan->dim_y * es, np * plan->dim_y, es, s);
+    if (grad_w) zero_rows(static_cast<char*>(grad_w) + g->pad_e0 * plan->w_numel * es, np * plan->w_numel, es, s);
+  };
   if (conv_backward_fused(plan, g, x, sh, w, scale, grad_out, grad_x, grad_sh, grad_w, ws, s)) {
-    zero_unread_x(plan, grad_x, g->N, dtype_size(plan->dtype), s);
+    zero_unread_x(plan, grad_x, g->N, es, s);
+    zero_padding();
     return;
   }
-  TPBackwardRows r;
-  r.rows = g->E;
-  r.x = x;
-  r.x_idx = g->src;
-  r.y = sh;
-  r.w = w;
-  r.w_stride = plan->w_numel;
-  r.g = grad_out;
-  r.g_idx = g->dst;
-  r.g_scale = scale;
-  r.dx_ws = grad_x ? ws : nullptr;
-  r.dy = grad_sh;
-  r.dw = grad_w;
-  tp_backward_rows(plan, r, s);
+  // general kernel over edge rows, the padding range left out
+  auto rows = [&](int64_t e0, int64_t e1) {
+    if (e1 <= e0) return;
+    auto off = [&](const void* p, int64_t per, size_t sz) -> const void* {
+      return p ? static_cast<const char*>(p) + e0 * per * int64_t(sz) : nullptr;
+    };
+    TPBackwardRows r;
+    r.rows = e1 - e0;
+    r.x = x;
+    r.x_idx = g->src + e0;
+    r.y = off(sh, plan->dim_y, es);
+    r.w = off(w, plan->w_numel, es);
+    r.w_stride = plan->w_numel;
+    r.g = grad_out;
+    r.g_idx = g->dst + e0;
+    r.g_scale = scale;
+    r.dx_ws = grad_x ? const_cast<void*>(off(ws, plan->dim_x, as)) : nullptr;
+    r.dy = const_cast<void*>(off(grad_sh, plan->dim_y, es));
+    r.dw = const_cast<void*>(off(grad_w, plan->w_numel, es));
+    tp_backward_rows(plan, r, s);
+  };
+  rows(0, g->pad_e0 < g->pad_e1 ? g->pad_e0 : g->E);
+  if (g->pad_e0 < g->pad_e1) rows(g->pad_e1, g->E);
+  zero_padding();
   if (grad_x) {
     switch (plan->dtype) {
       case CGTP_F32: dx_gather<float>(g, ws, grad_x, int(plan->dim_x), s); break;

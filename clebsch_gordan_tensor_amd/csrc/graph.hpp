@@ -12,6 +12,11 @@ struct cgtp_graph_s {
   int32_t* dst = nullptr;      // owned: destination of each CSR edge
   int32_t* order = nullptr;    // owned: receiver schedule, a permutation of [0, N)
   int device = 0;
+  // padding: edges whose destination is the padding node (the CSR range
+  // [pad_e0, pad_e1)) contribute nothing and are left out of the transpose
+  int32_t pad = -1;
+  int64_t pad_e0 = 0, pad_e1 = 0;
+  int64_t E_t() const { return E - (pad_e1 - pad_e0); }  // edges in the transpose
 };
 
 namespace cgtp {
@@ -19,7 +24,7 @@ namespace cgtp {
 void csr_from_coo_launch(int64_t N, int64_t E, const int32_t* src, const int32_t* dst,
                          int32_t* row_ptr, int32_t* src_sorted, int32_t* perm, hipStream_t s);
 cgtp_graph_s* graph_create(int64_t N, int64_t E, const int32_t* row_ptr, const int32_t* src,
-                           hipStream_t s);
+                           hipStream_t s, int32_t pad = -1);
 void graph_destroy(cgtp_graph_s* g);
 void graph_transpose_copy(const cgtp_graph_s* g, int32_t* col_ptr, int32_t* eid, hipStream_t s);
 

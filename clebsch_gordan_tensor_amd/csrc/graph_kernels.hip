@@ -169,16 +169,18 @@ __global__ void validate_csr(const int32_t* __restrict__ row_ptr, const int32_t*
   }
 }
 
-__global__ void src_count(const int32_t* __restrict__ src, int32_t* __restrict__ counts, int64_t E) {
+// Edges in [pe0, pe1) (the padding node's segment) are left out of the transpose.
+__global__ void src_count(const int32_t* __restrict__ src, int32_t* __restrict__ counts, int64_t E, int64_t pe0,
+                          int64_t pe1) {
   const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (e < E) atomicAdd(&counts[src[e]], 1);
+  if (e < E && (e < pe0 || e >= pe1)) atomicAdd(&counts[src[e]], 1);
 }
 
 __global__ void src_scatter(const int32_t* __restrict__ src, const int32_t* __restrict__ col_ptr,
                             int32_t* __restrict__ fill, int32_t* __restrict__ t_src,
-                            int32_t* __restrict__ t_pos, int64_t E) {
+                            int32_t* __restrict__ t_pos, int64_t E, int64_t pe0, int64_t pe1) {
   const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (e >= E) return;
+  if (e >= E || (e >= pe0 && e < pe1)) return;
   const int32_t s = src[e];
   const int32_t pos = col_ptr[s] + atomicAdd(&fill[s], 1);
   t_src[pos] = s;
@@ -259,12 +261,14 @@ void csr_from_coo_launch(int64_t N, int64_t E, const int32_t* src, const int32_t
 }
 
 cgtp_graph_s* graph_create(int64_t N, int64_t E, const int32_t* row_ptr, const int32_t* src,
-                           hipStream_t s) {
+                           hipStream_t s, int32_t pad) {
+  if (pad < -1 || (pad >= 0 && pad >= N)) throw Error{CGTP_ERR_INDEX, "graph_create: padding node outside [-1, N)"};
   auto g = std::make_unique<cgtp_graph_s>();
   g->N = N;
   g->E = E;
   g->row_ptr = row_ptr;
   g->src = src;
+  g->pad = pad;
   CGTP_CHECK_HIP(hipGetDevice(&g->device));
   {
     DevBuf flag(4);
@@ -286,6 +290,10 @@ cgtp_graph_s* graph_create(int64_t N, int64_t E, const int32_t* row_ptr, const i
     if (E > 0) CGTP_CHECK_HIP(hipMemcpyAsync(hsrc.data(), src, size_t(E) * 4, hipMemcpyDeviceToHost, s));
     CGTP_CHECK_HIP(hipStreamSynchronize(s));
     order = receiver_schedule(N, hrp, hsrc);
+    if (pad >= 0) {
+      g->pad_e0 = hrp[size_t(pad)];
+      g->pad_e1 = hrp[size_t(pad) + 1];
+    }
   }
   CGTP_CHECK_HIP(hipMalloc(&g->col_ptr, size_t(N + 1) * 4));
   if (hipMalloc(&g->order, size_t(N) * 4 + 4) != hipSuccess) {
@@ -304,7 +312,8 @@ cgtp_graph_s* graph_create(int64_t N, int64_t E, const int32_t* row_ptr, const i
     DevBuf counts(size_t(N + 1) * 4);
     CGTP_CHECK_HIP(hipMemsetAsync(counts.p, 0, size_t(N + 1) * 4, s));
     if (E > 0) {
-      hipLaunchKernelGGL(src_count, dim3(blocks_for(E, 256)), dim3(256), 0, s, src, counts.as<int32_t>(), E);
+      hipLaunchKernelGGL(src_count, dim3(blocks_for(E, 256)), dim3(256), 0, s, src, counts.as<int32_t>(), E,
+                         g->pad_e0, g->pad_e1);
       CGTP_CHECK_HIP(hipGetLastError());
     }
     if (N > 0)
@@ -314,10 +323,12 @@ cgtp_graph_s* graph_create(int64_t N, int64_t E, const int32_t* row_ptr, const i
       DevBuf fill(size_t(N) * 4 + 4), ts(size_t(E) * 4), tp(size_t(E) * 4);
       CGTP_CHECK_HIP(hipMemsetAsync(fill.p, 0, size_t(N) * 4 + 4, s));
       hipLaunchKernelGGL(src_scatter, dim3(blocks_for(E, 256)), dim3(256), 0, s, src, g->col_ptr,
-                         fill.as<int32_t>(), ts.as<int32_t>(), tp.as<int32_t>(), E);
+                         fill.as<int32_t>(), ts.as<int32_t>(), tp.as<int32_t>(), E, g->pad_e0, g->pad_e1);
       CGTP_CHECK_HIP(hipGetLastError());
-      hipLaunchKernelGGL(transpose_rank, dim3(blocks_for(E, 256)), dim3(256), 0, s, g->col_ptr,
-                         ts.as<int32_t>(), tp.as<int32_t>(), g->eid, E);
+      const int64_t Et = g->E_t();
+      if (Et > 0)
+        hipLaunchKernelGGL(transpose_rank, dim3(blocks_for(Et, 256)), dim3(256), 0, s, g->col_ptr,
+                           ts.as<int32_t>(), tp.as<int32_t>(), g->eid, Et);
       CGTP_CHECK_HIP(hipGetLastError());
       hipLaunchKernelGGL(fill_dst, dim3(blocks_for(N, 256)), dim3(256), 0, s, row_ptr, g->dst, N);
       CGTP_CHECK_HIP(hipGetLastError());
@@ -348,8 +359,8 @@ void graph_destroy(cgtp_graph_s* g) {
 
 void graph_transpose_copy(const cgtp_graph_s* g, int32_t* col_ptr, int32_t* eid, hipStream_t s) {
   CGTP_CHECK_HIP(hipMemcpyAsync(col_ptr, g->col_ptr, size_t(g->N + 1) * 4, hipMemcpyDeviceToDevice, s));
-  if (g->E > 0)
-    CGTP_CHECK_HIP(hipMemcpyAsync(eid, g->eid, size_t(g->E) * 4, hipMemcpyDeviceToDevice, s));
+  if (g->E_t() > 0)
+    CGTP_CHECK_HIP(hipMemcpyAsync(eid, g->eid, size_t(g->E_t()) * 4, hipMemcpyDeviceToDevice, s));
 }
 
 }  // namespace cgtp

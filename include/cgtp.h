@@ -210,10 +210,21 @@ cgtp_status cgtp_csr_from_coo(int64_t N, int64_t E, const int32_t* src, const in
  * Errors: INDEX on invalid arrays, ALLOC if device memory runs out. */
 cgtp_status cgtp_graph_create(int64_t N, int64_t E, const int32_t* row_ptr, const int32_t* src,
                               void* stream, cgtp_graph* out);
+/* cgtp_graph_create with a padding node (E3J 3.1.2 and 3.2: fixed-shape
+ * callers pad the edge list with edges into a shared padding node, whose one
+ * CSR segment then holds all of them). pad_node in [0, N), or -1 for none.
+ * The edges whose destination is pad_node are padding edges: they are
+ * skipped, so out[pad_node] = 0, their grad_sh and grad_w rows are zero, and
+ * they add nothing to grad_x; they are left out of the transpose. Other edges
+ * (also those whose source is pad_node) are ordinary.
+ * Errors: as cgtp_graph_create; INDEX for pad_node outside [-1, N). */
+cgtp_status cgtp_graph_create_ex(int64_t N, int64_t E, const int32_t* row_ptr, const int32_t* src,
+                                 int32_t pad_node, void* stream, cgtp_graph* out);
 cgtp_status cgtp_graph_destroy(cgtp_graph graph);
 
-/* Copy the handle's transpose into caller device buffers col_ptr[N+1], eid[E]
- * (eid[k] = CSR position of the k-th source-ordered edge). */
+/* Copy the handle's transpose into caller device buffers col_ptr[N+1] and
+ * eid[col_ptr[N]] (eid[k] = CSR position of the k-th source-ordered edge;
+ * col_ptr[N] = E minus the padding edges). */
 cgtp_status cgtp_graph_transpose(cgtp_graph graph, int32_t* col_ptr, int32_t* eid, void* stream);
 
 /* ------------------------------------------------------------- convolution */

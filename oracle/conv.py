@@ -19,6 +19,17 @@ from . import tp
 from .graph import dst_of_csr
 
 
+def padding_mask(row_ptr, pad_node):
+    """Edges whose destination is the padding node ([E3J] 3.1.2 and 3.2: a
+    fixed-shape caller pads the edge list with edges into one shared padding
+    node); they contribute nothing. None: no padding."""
+    E = int(row_ptr[-1])
+    m = np.zeros(E, bool)
+    if pad_node is not None:
+        m[row_ptr[pad_node]:row_ptr[pad_node + 1]] = True
+    return m
+
+
 def forward_loops(L, row_ptr, src, x, Y, w, scale):
     """Explicit per-node, per-edge loops (for tiny graphs)."""
     N = len(row_ptr) - 1
@@ -31,30 +42,34 @@ def forward_loops(L, row_ptr, src, x, Y, w, scale):
     return out
 
 
-def forward(L, row_ptr, src, x, Y, w, scale):
-    """Materialised-message route: TP on gathered rows, then a scatter-add."""
+def forward(L, row_ptr, src, x, Y, w, scale, pad_node=None):
+    """Materialised-message route: TP on gathered rows, then a scatter-add.
+    Padding edges (into pad_node) carry no message."""
     x = np.asarray(x, np.float64)
     N = len(row_ptr) - 1
     dst = dst_of_csr(row_ptr)
     msg = tp.forward(L, x[np.asarray(src)], Y, w)
+    msg[padding_mask(row_ptr, pad_node)] = 0.0
     out = np.zeros((N, L.dim_out))
     np.add.at(out, dst, msg)
     return scale * out
 
 
-def backward(L, row_ptr, src, x, Y, w, scale, g):
-    """Cotangents (dx [N, dim_x], dY [E, dim_y], dw [E, W]) for out cotangent g [N, dim_out]."""
+def backward(L, row_ptr, src, x, Y, w, scale, g, pad_node=None):
+    """Cotangents (dx [N, dim_x], dY [E, dim_y], dw [E, W]) for out cotangent g [N, dim_out].
+    Padding edges (into pad_node) get zero gradients and add nothing to dx."""
     x = np.asarray(x, np.float64)
     dst = dst_of_csr(row_ptr)
     src = np.asarray(src)
     ge = scale * np.asarray(g, np.float64)[dst]
+    ge[padding_mask(row_ptr, pad_node)] = 0.0
     dxe, dY, dw = tp.backward(L, x[src], Y, w, ge)
     dx = np.zeros_like(x)
     np.add.at(dx, src, dxe)
     return dx, dY, dw
 
 
-def double_backward(L, row_ptr, src, x, Y, w, scale, g, gx=None, gY=None, gw=None):
+def double_backward(L, row_ptr, src, x, Y, w, scale, g, gx=None, gY=None, gw=None, pad_node=None):
     """Reverse mode of ``backward`` (twice-differentiable convolution, e.g. for
     training on forces): cotangents of (x, Y, w, g) for cotangents (gx, gY, gw)
     of (dx, dY, dw); a missing one counts as zero.
@@ -68,8 +83,11 @@ def double_backward(L, row_ptr, src, x, Y, w, scale, g, gx=None, gY=None, gw=Non
     dst = dst_of_csr(row_ptr)
     src = np.asarray(src)
     ge = scale * np.asarray(g, np.float64)[dst]
+    pm = padding_mask(row_ptr, pad_node)
+    ge[pm] = 0.0
     gxe = None if gx is None else np.asarray(gx, np.float64)[src]
     ddxe, ddY, ddw, ddge = tp.double_backward(L, x[src], Y, w, ge, gxe, gY, gw)
+    ddge[pm] = 0.0
     ddx = np.zeros_like(x)
     np.add.at(ddx, src, ddxe)
     ddg = np.zeros((len(row_ptr) - 1, L.dim_out))

@@ -225,3 +225,43 @@ def test_force_chain_matches_fd():
         vm[e, k] -= h
         fd = (f(vp) - f(vm)) / (2 * h)
         assert gv[e, k] == pytest.approx(fd, rel=1e-6, abs=1e-7)
+
+
+def test_padding_edges_equal_the_graph_without_them():
+    """Edges into a padding node add nothing ([E3J] 3.1.2, 3.2): forward, backward
+    and double backward equal those of the graph with the padding edges removed
+    (built again from the remaining edge list), with zero rows for the padding."""
+    from oracle import graph as og
+    L = Layout("2x0e+2x1o+2x2e", "0e+1o+2e", "0e+0o+1e+1o+2e+2o")
+    rng = np.random.default_rng(41)
+    N, pad = 12, 11
+    src = rng.integers(0, N - 1, 40)
+    dst = rng.integers(0, N - 1, 40)
+    src = np.concatenate([src, np.full(15, pad), rng.integers(0, N - 1, 3)])   # padding edges, and 3 more into pad
+    dst = np.concatenate([dst, np.full(15, pad), np.full(3, pad)])
+    row_ptr, s, perm = og.csr_from_coo(N, src, dst)
+    E = len(s)
+    x = synth.gaussian((N, L.dim_x), 42, synth.S_X)
+    Y = synth.gaussian((E, L.dim_y), 42, synth.S_Y)
+    w = synth.gaussian((E, L.w_numel), 42, synth.S_W)
+    g = synth.gaussian((N, L.dim_out), 42, synth.S_G)
+    keep = np.ones(E, bool)
+    keep[row_ptr[pad]:row_ptr[pad + 1]] = False
+    d = og.dst_of_csr(row_ptr)
+    rp2, s2, perm2 = og.csr_from_coo(N, s[keep], d[keep])
+    Yk, wk = Y[keep][perm2], w[keep][perm2]
+    out = conv.forward(L, row_ptr, s, x, Y, w, 0.6, pad_node=pad)
+    ref = conv.forward(L, rp2, s2, x, Yk, wk, 0.6)
+    assert np.abs(out - ref).max() < 1e-13 and np.all(out[pad] == 0)
+    dx, dY, dw = conv.backward(L, row_ptr, s, x, Y, w, 0.6, g, pad_node=pad)
+    rdx, rdY, rdw = conv.backward(L, rp2, s2, x, Yk, wk, 0.6, g)
+    assert np.abs(dx - rdx).max() < 1e-13
+    kept_pos = np.nonzero(keep)[0][perm2]          # CSR position (full graph) of each edge of the reduced graph
+    assert np.abs(dY[kept_pos] - rdY).max() < 1e-13 and np.abs(dw[kept_pos] - rdw).max() < 1e-13
+    assert np.all(dY[~keep] == 0) and np.all(dw[~keep] == 0)
+    gY = synth.gaussian((E, L.dim_y), 43, synth.S_Y)
+    gw = synth.gaussian((E, L.w_numel), 43, synth.S_W)
+    dd = conv.double_backward(L, row_ptr, s, x, Y, w, 0.6, g, None, gY, gw, pad_node=pad)
+    rd = conv.double_backward(L, rp2, s2, x, Yk, wk, 0.6, g, None, gY[keep][perm2], gw[keep][perm2])
+    assert np.abs(dd[0] - rd[0]).max() < 1e-12 and np.abs(dd[3] - rd[3]).max() < 1e-12
+    assert np.abs(dd[1][kept_pos] - rd[1]).max() < 1e-12 and np.all(dd[2][~keep] == 0)
