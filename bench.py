@@ -22,7 +22,8 @@ the fused convolution (forward and backward, fp32) on the 1000- and
 8000-molecule water boxes (the latter with the harmonics forward/backward of
 the force chain), the 100,000-point uniform cloud, and 2048 points with 45
 neighbours and 128 channels per degree with outputs collapsed by (l3, p3)
-(L = 3 and 4), and the water8k double backward in the force-training shape.
+(L = 3 and 4), the water8k double backward in the force-training shape, and
+water1k with 25 % padding edges with and without padding-edge skipping.
 """
 
 import argparse
@@ -392,6 +393,58 @@ def conv_bench(args, torch, cgtp, synth, name, steps, forces=False):
     return res
 
 
+def padding_bench(args, torch, cgtp, synth, name="conv_water1k"):
+    """Padding edges ([E3J] 3.1.2, 3.2): the workload's graph plus one padding
+    node and padding edges into it making up 25 % of all edges (what a
+    fixed-shape caller produces), convolution forward + backward with the
+    padding edges skipped (graph created with the padding node) and without."""
+    import numpy as np
+    c = synth.CONFIGS[name]
+    p = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"])
+    pos = synth.positions_for(c, 0)
+    src, dst, vec = synth.radius_graph(pos, c["box"], c["r_cut"])
+    N0, E0 = pos.shape[0], src.shape[0]
+    npad = E0 // 3
+    pad = N0
+    rng = np.random.default_rng(0)
+    src = np.concatenate([src, np.full(npad, pad)]).astype(np.int32)
+    dst = np.concatenate([dst, np.full(npad, pad)]).astype(np.int32)
+    vec = np.concatenate([vec, rng.standard_normal((npad, 3)) + 1.0])
+    N, E = N0 + 1, src.shape[0]
+    row_ptr, s, perm = cgtp.csr_from_coo(N, torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda())
+    v = torch.from_numpy(vec).cuda()[perm.long()].float().contiguous()
+    Y = cgtp.sh_forward(c["L"], v)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1)
+    w = torch.randn((E, p.w_numel), generator=gen, device="cuda")
+    x = torch.randn((N, p.dim_x), generator=gen, device="cuda")
+    g = torch.randn((N, p.dim_out), generator=gen, device="cuda")
+    sc = 1.0 / math.sqrt(E0 / N0)
+    res = dict(workload=name, E=E, padding_edges=npad, padding_fraction=round(npad / E, 3))
+    for key, pn in (("skipped", pad), ("not_skipped", None)):
+        t0 = time.perf_counter()
+        graph = cgtp.Graph(N, row_ptr, s, pad_node=pn)
+        torch.cuda.synchronize()
+        t_graph = time.perf_counter() - t0
+        ws = torch.empty(p.workspace_size(cgtp.OP_CONV_BACKWARD, graph=graph), dtype=torch.uint8, device="cuda")
+        out = torch.empty((N, p.dim_out), device="cuda")
+        dx, dY, dw = torch.empty_like(x), torch.empty_like(Y), torch.empty_like(w)
+        fwd = lambda: p.conv_forward(graph, x, Y, w, sc, out=out)
+        bwd = lambda: p.conv_backward(graph, x, Y, w, sc, g, out=(dx, dY, dw), ws=ws)
+        tf, tb = KernelTimer(torch), KernelTimer(torch)
+        fwd()
+        bwd()
+        for _ in range(3):
+            tf(fwd)
+            tb(bwd)
+        torch.cuda.synchronize()
+        res[key] = dict(fwd_ms=round(tf.mean_ms(), 3), bwd_ms=round(tb.mean_ms(), 3),
+                        graph_create_s=round(t_graph, 3))
+        del graph, ws, out, dx, dY, dw
+    torch.cuda.empty_cache()
+    return res
+
+
 def double_backward_bench(args, torch, cgtp, synth, name="conv_water8k"):
     """Convolution double backward in the force-training shape (cotangents on
     grad_sh and grad_w, all four outputs) on one full-size workload, next to its
@@ -541,6 +594,7 @@ def main():
             extra[name] = conv_bench(args, torch, cgtp, synth, name, max(2, min(args.steps, 5)),
                                      forces=name == "conv_water8k")
         extra["conv_water8k_double_backward"] = double_backward_bench(args, torch, cgtp, synth)
+        extra["conv_water1k_padded"] = padding_bench(args, torch, cgtp, synth)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, synth)
     line = {
         "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
