@@ -449,7 +449,7 @@ struct TPBwd {
 template <typename T, int L1, int LM>
 struct BwdWaves {
   static constexpr int value =
-      (L1 >= 0 && LM <= 3 && sizeof(T) <= 4 && CGTP_TP_BWD_WAVES > 1) ? CGTP_TP_BWD_WAVES : 1;
+      ((L1 >= 0 || L1 == -2) && LM <= 3 && sizeof(T) <= 4 && CGTP_TP_BWD_WAVES > 1) ? CGTP_TP_BWD_WAVES : 1;
 };
 
 template <typename T, typename A, int VEC, int L1, int LM>
@@ -482,13 +482,17 @@ void tp_bwd_kernel(TPArgs a) {
           TPBwd<T, A, VEC, LM>::template block<L1, CGTP_TP_BWD_DX_LDS != 0>(a, blk, xr, yr, gr, wr, dxr, dxa,
                                                                            dwr, dwa, c, lds);
       } else {
+        // every x block in one launch (L1 = -1: grad_x rows in registers;
+        // L1 = -2: in LDS, for collapsed outputs, whose x blocks share their
+        // cotangent blocks and so read them while they are still in cache)
         for (int b = 0; b < a.nblocks; ++b) {
           const BlockDev blk = ldc(a.blocks + b);
           if (c >= blk.mul) continue;
           static_for<0, kLmax + 1>([&](auto L1c) {
             constexpr int D = decltype(L1c)::value;
             if (blk.l1 == D)
-              TPBwd<T, A, VEC, LM>::template block<D, false>(a, blk, xr, yr, gr, wr, dxr, dxa, dwr, dwa, c, lds);
+              TPBwd<T, A, VEC, LM>::template block<D, L1 == -2 && CGTP_TP_BWD_DX_LDS != 0>(
+                  a, blk, xr, yr, gr, wr, dxr, dxa, dwr, dwa, c, lds);
           });
         }
       }
@@ -579,15 +583,22 @@ template <typename T, int VEC>
 void tp_bwd_typed(const TPArgs& a, int l1, int lm, hipStream_t s) {
   using A = typename AccOf<T>::type;
   const dim3 grid = grid_for(a.B, a.lpr_log2);
-  const size_t lds = size_t(a.dim_y) * kBlock * sizeof(A) +
-                     (CGTP_TP_BWD_DX_LDS && VEC > 1 && l1 >= 0 ? size_t(2 * l1 + 1) * kBlock * VEC * sizeof(A) : 0);
+  const size_t dx_rows = !CGTP_TP_BWD_DX_LDS || VEC == 1 ? 0 : (l1 >= 0 ? 2 * l1 + 1 : l1 == -2 ? 2 * kLmax + 1 : 0);
+  const size_t lds = size_t(a.dim_y) * kBlock * sizeof(A) + dx_rows * kBlock * VEC * sizeof(A);
   if constexpr (VEC == 1) {
     (void)l1;
     (void)lm;
     hipLaunchKernelGGL((tp_bwd_kernel<T, A, VEC, -1, kLmax>), grid, dim3(kBlock), lds, s, a);
   } else {
-    if (l1 < 0) {
+    if (l1 == -1) {
       hipLaunchKernelGGL((tp_bwd_kernel<T, A, VEC, -1, kLmax>), grid, dim3(kBlock), lds, s, a);
+      return;
+    }
+    if (l1 == -2) {
+      static_for<0, kLmax + 1>([&](auto J) {
+        constexpr int M = decltype(J)::value;
+        if (lm == M) hipLaunchKernelGGL((tp_bwd_kernel<T, A, VEC, -2, M>), grid, dim3(kBlock), lds, s, a);
+      });
       return;
     }
     static_for<0, kLmax + 1>([&](auto I) {

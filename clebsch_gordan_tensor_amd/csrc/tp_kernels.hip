@@ -38,6 +38,9 @@ CGTP_TP_EXTERN_BWD(double, 2)
 // storage: its accumulators for every output degree stay in registers, and
 // 2 channels keep the kernel at 3-4 waves per SIMD where 4 channels drop
 // it to 1-2.
+#ifndef CGTP_TP_BWDC_ALL_BLOCKS
+#define CGTP_TP_BWDC_ALL_BLOCKS 1
+#endif
 #ifndef CGTP_TP_FWDC_VEC
 #define CGTP_TP_FWDC_VEC 2
 #endif
@@ -236,13 +239,16 @@ void tp_backward_rows(cgtp_plan_s* plan, const TPBackwardRows& r, hipStream_t st
   a.g_idx = r.g_idx;
   a.g_scale = r.g_scale;
   // one launch per x block (degree-specialised); grad_y accumulates across
-  // the launches in stream order, so its summation order is fixed
-  const int nb = vec == 1 ? 1 : int(plan->blocks.size());
+  // the launches in stream order, so its summation order is fixed. With
+  // collapsed outputs one launch takes every x block (they share cotangent
+  // blocks, which are then read once from memory).
+  const bool all_blocks = vec > 1 && plan->collapse && CGTP_TP_BWDC_ALL_BLOCKS;
+  const int nb = vec == 1 || all_blocks ? 1 : int(plan->blocks.size());
   const int lm = plan->lm;
   for (int b = 0; b < nb; ++b) {
     a.block = b;
     a.dy_accum = b > 0 ? 1 : 0;
-    const int l1 = vec == 1 ? -1 : plan->blocks[size_t(b)].l1;
+    const int l1 = vec == 1 ? -1 : all_blocks ? -2 : plan->blocks[size_t(b)].l1;
     switch (plan->dtype) {
       case CGTP_F32:
         vec == 1 ? tp_bwd_typed<float, 1>(a, l1, lm, stream)
