@@ -316,11 +316,12 @@ def tp_large_bench(args, torch, cgtp, synth, extra):
     dom = max(("tp_fwd_kernel", "tp_bwd_kernel"), key=lambda k: kern[k]["ms"])
     d = kern[dom]
     nblk = len([t for t in wl.irreps_x.split("+") if t])
+    how = ("1 launch of tp_bwd_kernel over all %d x blocks" % nblk if dom == "tp_bwd_kernel"
+           else "%d launches of tp_fwd_kernel (one per x block, degree-specialised), timed as one" % nblk)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": d["algorithmic_GBs"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": d["frac_of_hbm_peak"], "traffic": d["traffic"],
                 "algorithmic_bytes_per_launch": d["bytes_per_row"] * B, "mean_launch_ms": d["ms"],
-                "launch": "one call = %d launches of %s (one per x block, degree-specialised), timed as one"
-                          % (nblk, dom)}
+                "launch": "one call = " + how}
     extra["tp_large_kernels"] = kern
     extra["tp_large_fwd_pairs_per_s"] = kern["tp_fwd_kernel"]["rows_per_s"]
     extra["tp_large_fwd_bwd_pairs_per_s"] = B / ((kern["tp_fwd_kernel"]["ms"] + kern["tp_bwd_kernel"]["ms"]) * 1e-3)

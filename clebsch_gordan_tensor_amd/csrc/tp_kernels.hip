@@ -41,6 +41,9 @@ CGTP_TP_EXTERN_BWD(double, 2)
 #ifndef CGTP_TP_BWDC_ALL_BLOCKS
 #define CGTP_TP_BWDC_ALL_BLOCKS 1
 #endif
+#ifndef CGTP_TP_BWD_ALL_BLOCKS
+#define CGTP_TP_BWD_ALL_BLOCKS 1
+#endif
 #ifndef CGTP_TP_FWDC_VEC
 #define CGTP_TP_FWDC_VEC 2
 #endif
@@ -238,11 +241,14 @@ void tp_backward_rows(cgtp_plan_s* plan, const TPBackwardRows& r, hipStream_t st
   a.x_idx = r.x_idx;
   a.g_idx = r.g_idx;
   a.g_scale = r.g_scale;
-  // one launch per x block (degree-specialised); grad_y accumulates across
-  // the launches in stream order, so its summation order is fixed. With
-  // collapsed outputs one launch takes every x block (they share cotangent
-  // blocks, which are then read once from memory).
-  const bool all_blocks = vec > 1 && plan->collapse && CGTP_TP_BWDC_ALL_BLOCKS;
+  // One launch over every x block (grad_x rows in LDS, the block's degree
+  // dispatched per block), or one launch per x block (degree-specialised;
+  // grad_y then accumulates across the launches in stream order). Either way
+  // the summation order is fixed. With collapsed outputs the x blocks share
+  // cotangent blocks, which one launch reads once from memory; without, the
+  // single launch saves the per-launch tails and grad_y round trips
+  // (tp_large fp32: 26.4 -> 25.0 ms).
+  const bool all_blocks = vec > 1 && (plan->collapse ? CGTP_TP_BWDC_ALL_BLOCKS : CGTP_TP_BWD_ALL_BLOCKS);
   const int nb = vec == 1 || all_blocks ? 1 : int(plan->blocks.size());
   const int lm = plan->lm;
   for (int b = 0; b < nb; ++b) {
