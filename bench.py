@@ -1,7 +1,7 @@
 """Benchmark of the hot path on one MI355X; prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload tp_large]
-                    [--no-conv] [--no-cpu-baseline]
+                    [--no-conv] [--no-extra] [--no-cpu-baseline]
     python bench.py --profile WORKLOAD      (a few calls of every operation, for rocprofv3)
     python bench.py --calibrate-copy        (a plain copy of known size, for the byte counters)
 
@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="tp_large", choices=["tp_large"])
     ap.add_argument("--no-conv", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="only the headline step (for a kernel trace of exactly its launches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -586,11 +588,12 @@ def main():
         return
     extra = {"device": torch.cuda.get_device_name(0)}
     value, ms_step, roofline, plan = tp_large_bench(args, torch, cgtp, synth, extra)
-    extra["tp_large_bf16"] = tp_large_bf16(args, torch, cgtp, synth)
-    extra["tp_large_collapsed"] = tp_variants_bench(args, torch, cgtp, synth)
-    extra["linear_large"] = linear_bench(args, torch, cgtp, synth, "f32")
-    extra["linear_large_bf16"] = linear_bench(args, torch, cgtp, synth, "bf16")
-    if not args.no_conv:
+    if not args.no_extra:
+        extra["tp_large_bf16"] = tp_large_bf16(args, torch, cgtp, synth)
+        extra["tp_large_collapsed"] = tp_variants_bench(args, torch, cgtp, synth)
+        extra["linear_large"] = linear_bench(args, torch, cgtp, synth, "f32")
+        extra["linear_large_bf16"] = linear_bench(args, torch, cgtp, synth, "bf16")
+    if not args.no_conv and not args.no_extra:
         for name in ("conv_water1k", "conv_water8k", "conv_uniform100k", "conv_collapsed_l3", "conv_collapsed_l4"):
             extra[name] = conv_bench(args, torch, cgtp, synth, name, max(2, min(args.steps, 5)),
                                      forces=name == "conv_water8k")
