@@ -28,6 +28,7 @@
 #include <map>
 #include <memory>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "device_util.hpp"
@@ -48,6 +49,10 @@ struct LinJob {  // output columns c_off .. c_off + n_len of every row; terms t0
 struct LinDW {  // weight tile [u0, u0 + 128) x [v0, v0 + 128) of one path
   int32_t x_off, mu, g_off, mv, nm, w_off, u0, v0;
 };
+
+#ifndef CGTP_LINEAR_BF16_MFMA
+#define CGTP_LINEAR_BF16_MFMA 1
+#endif
 
 constexpr int kLinThreads = 256;
 constexpr int kLinRows = 128;  // rows per workgroup of the row kernel (4 waves x 32)
@@ -225,6 +230,138 @@ __global__ __launch_bounds__(kLinThreads) void lin_rows_kernel(const T* __restri
     }
 }
 
+// bf16 storage with every offset, width and row stride a multiple of 8: the
+// products run on v_mfma_f32_16x16x32_bf16 (bf16 x bf16 products are exact in
+// fp32 and accumulate in fp32, so the result matches widening to fp32 first
+// up to summation order). Lane l supplies A[l % 16][8 (l / 16) + j] and
+// B[8 (l / 16) + j][l % 16], j < 8 (checked on the device), so each lane
+// loads 8 consecutive k of its row in one 16-byte load, and the B chunk sits
+// in LDS n-major ([n][k]) so each lane reads its 8 k values in one access.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+constexpr int kKB = 32;         // contraction rows per B chunk (the MFMA's K)
+constexpr int kBTP = kKB + 8;   // padded n-major LDS row of a B chunk, in elements
+
+__global__ __launch_bounds__(kLinThreads) void lin_rows_bf16_kernel(const bf16* __restrict__ A, int64_t lda,
+                                                                  const bf16* __restrict__ W, bf16* __restrict__ C,
+                                                                  int64_t ldcr, int64_t rows,
+                                                                  const LinJob* __restrict__ jobs,
+                                                                  const LinTerm* __restrict__ terms) {
+  __shared__ __attribute__((aligned(16))) uint16_t bt[2][kLinCols * kBTP];
+  const LinJob jb = ldc(jobs + blockIdx.y);
+  const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
+  const int li = lane & 15, lk = lane >> 4;
+  const int64_t r0 = int64_t(blockIdx.x) * kLinRows + wave * 32;  // two 16-row tiles per wave
+  int64_t arow[2];
+  bool row_ok[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    arow[s] = r0 + 16 * s + li;
+    row_ok[s] = arow[s] < rows;
+  }
+  v4f acc[2][8];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[s][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  const u16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int t = jb.t0; t < jb.t1; ++t) {
+    const LinTerm tm = ldc(terms + t);
+    const uint16_t* __restrict__ wb =
+        reinterpret_cast<const uint16_t*>(W) + tm.b_off + int64_t(jb.b_n0) * tm.b_sn;
+    const bool kfast = tm.b_sk == 1;  // transposed weights: runs of 8 along k
+    const int nch = (tm.K + kKB - 1) / kKB;
+    // B chunk: 32 x 128 as 512 runs of 8 elements, two per thread, requested
+    // unconditionally from clamped addresses and masked when stashed
+    u16x8 pre[2];
+    auto unit = [&](int q, int c, int& n, int& k) {
+      const int u = int(threadIdx.x) + q * kLinThreads;
+      if (kfast) {
+        n = u >> 2;
+        k = c * kKB + (u & 3) * 8;
+      } else {
+        k = c * kKB + (u >> 4);
+        n = (u & 15) * 8;
+      }
+    };
+    auto fetch = [&](int c) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        int n, k;
+        unit(q, c, n, k);
+        const bool ok = k < tm.K && n < jb.n_len;
+        pre[q] = *reinterpret_cast<const u16x8*>(wb + int64_t(ok ? k : 0) * tm.b_sk + int64_t(ok ? n : 0) * tm.b_sn);
+      }
+    };
+    auto stash = [&](int c, int buf) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        int n, k;
+        unit(q, c, n, k);
+        const u16x8 v = (k < tm.K && n < jb.n_len) ? pre[q] : zero8;
+        const int kk = k - c * kKB;
+        if (kfast) {
+          *reinterpret_cast<u16x8*>(&bt[buf][n * kBTP + kk]) = v;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) bt[buf][(n + j) * kBTP + kk] = v[j];
+        }
+      }
+    };
+    // this lane's 8 consecutive k of each of its two rows (K is a multiple of
+    // 8, so a run is wholly inside or past K; rows past the end read row 0,
+    // whose results are not stored)
+    auto load_a = [&](int c, u16x8 (&a)[2]) {
+      const int ka = c * kKB + 8 * lk;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const uint16_t* __restrict__ ar =
+            reinterpret_cast<const uint16_t*>(A) + (row_ok[s2] ? arow[s2] : int64_t(0)) * lda + tm.a_off;
+        a[s2] = *reinterpret_cast<const u16x8*>(ar + (ka < tm.K ? ka : 0));
+      }
+    };
+    __syncthreads();  // the previous term's last chunk is consumed
+    u16x8 ac[2], an[2];
+    fetch(0);
+    load_a(0, ac);
+    stash(0, 0);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+      fetch(c + 1);
+      load_a(c + 1, an);
+      __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the MFMAs
+      const uint16_t* __restrict__ bc = bt[c & 1];
+      const bool kin = c * kKB + 8 * lk < tm.K;
+      bf16x8 av[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) av[s2] = __builtin_bit_cast(bf16x8, kin ? ac[s2] : zero8);
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(bc + (tt * 16 + li) * kBTP + 8 * lk));
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+          acc[s2][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s2], bv, acc[s2][tt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // the requests complete behind the MFMAs
+      stash(c + 1, (c + 1) & 1);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) ac[s2] = an[s2];
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      const int n = tt * 16 + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = r0 + 16 * s + 4 * lk + r;
+        if (row < rows && n < jb.n_len) from_acc(C[row * ldcr + jb.c_off + n], acc[s][tt][r]);
+      }
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kLinThreads) void lin_dw_kernel(const T* __restrict__ X, int64_t ldx,
                                                            const T* __restrict__ G, int64_t ldg,
@@ -305,6 +442,7 @@ struct LinTables {
   LinDW* wjobs = nullptr;
   int nf = 0, nx = 0, nw = 0;
   bool avec_f = true, avec_x = true;  // 4-aligned A offsets and K (row strides checked per call)
+  bool v8_f = true, v8_x = true;      // every offset and width a multiple of 8 (bf16 matrix-core kernel)
 };
 
 std::mutex g_lin_mu;
@@ -340,6 +478,7 @@ const LinTables& lin_tables(const cgtp_linear_s* lin) {
             const int64_t a_off = lin->in_off[size_t(p.i)] + int64_t(m) * p.mu;
             ft.push_back(LinTerm{int32_t(a_off), p.mu, int32_t(p.w_off), p.mv, 1, 0, 0, 0});
             t.avec_f = t.avec_f && a_off % 4 == 0 && p.mu % 4 == 0;
+            t.v8_f = t.v8_f && a_off % 8 == 0 && p.mu % 8 == 0 && p.mv % 8 == 0 && p.w_off % 8 == 0;
           }
         j.t1 = int32_t(ft.size());
         fj.push_back(j);
@@ -357,6 +496,7 @@ const LinTables& lin_tables(const cgtp_linear_s* lin) {
             const int64_t a_off = lin->out_off[size_t(p.o)] + int64_t(m) * p.mv;
             xt.push_back(LinTerm{int32_t(a_off), p.mv, int32_t(p.w_off), 1, p.mv, 0, 0, 0});
             t.avec_x = t.avec_x && a_off % 4 == 0 && p.mv % 4 == 0;
+            t.v8_x = t.v8_x && a_off % 8 == 0 && p.mu % 8 == 0 && p.mv % 8 == 0 && p.w_off % 8 == 0;
           }
         j.t1 = int32_t(xt.size());
         xj.push_back(j);
@@ -401,9 +541,25 @@ void rows_launch(const T* A, int64_t lda, const T* W, T* C, int64_t ldc, int64_t
   CGTP_CHECK_HIP(hipGetLastError());
 }
 
+// bf16 with 8-aligned offsets, widths and row strides: the bf16 matrix-core kernel
+bool rows_bf16_mfma(const void* A, int64_t lda, const void* W, void* C, int64_t ldc, int64_t rows,
+                    const LinJob* jobs, const LinTerm* terms, int njobs, bool v8, hipStream_t s) {
+  if (!v8 || lda % 8 != 0 || !aligned16(A, 16) || !aligned16(W, 16) || CGTP_LINEAR_BF16_MFMA == 0) return false;
+  if (rows == 0 || njobs == 0) return true;
+  const dim3 grid(unsigned((rows + kLinRows - 1) / kLinRows), unsigned(njobs));
+  hipLaunchKernelGGL(lin_rows_bf16_kernel, grid, dim3(kLinThreads), 0, s, static_cast<const bf16*>(A), lda,
+                     static_cast<const bf16*>(W), static_cast<bf16*>(C), ldc, rows, jobs, terms);
+  CGTP_CHECK_HIP(hipGetLastError());
+  (void)ldc;
+  return true;
+}
+
 template <typename T>
 void forward_typed(const cgtp_linear_s* lin, int64_t B, const void* x, const void* w, void* out, hipStream_t s) {
   const LinTables& t = lin_tables(lin);
+  if (std::is_same<T, bf16>::value &&
+      rows_bf16_mfma(x, lin->dim_in, w, out, lin->dim_out, B, t.fjobs, t.fterms, t.nf, t.v8_f, s))
+    return;
   const bool avec = t.avec_f && lin->dim_in % 4 == 0 && aligned16(x, 4 * sizeof(T));
   rows_launch<T>(static_cast<const T*>(x), lin->dim_in, static_cast<const T*>(w), static_cast<T*>(out), lin->dim_out,
                  B, t.fjobs, t.fterms, t.nf, avec, s);
@@ -413,6 +569,9 @@ template <typename T>
 void backward_typed(const cgtp_linear_s* lin, int64_t B, const void* x, const void* w, const void* g, void* dx,
                     void* dw, void* ws, hipStream_t s) {
   const LinTables& t = lin_tables(lin);
+  if (dx && std::is_same<T, bf16>::value &&
+      rows_bf16_mfma(g, lin->dim_out, w, dx, lin->dim_in, B, t.xjobs, t.xterms, t.nx, t.v8_x, s))
+    dx = nullptr;  // done
   if (dx) {
     const bool avec = t.avec_x && lin->dim_out % 4 == 0 && aligned16(g, 4 * sizeof(T));
     rows_launch<T>(static_cast<const T*>(g), lin->dim_out, static_cast<const T*>(w), static_cast<T*>(dx),
