@@ -423,6 +423,113 @@ __global__ __launch_bounds__(kLinThreads) void lin_dw_kernel(const T* __restrict
       }
 }
 
+// grad_W partials with bf16 storage on v_mfma_f32_16x16x32_bf16: the
+// contraction runs over rows, which are strided in memory, so each 32-row
+// step stages x and g transposed in LDS ([u][row] and [v][row], from 16-byte
+// row loads) and every lane then reads its 8 consecutive rows of one u (A)
+// and one v (B) in one access. Widths and offsets are multiples of 8.
+__global__ __launch_bounds__(kLinThreads) void lin_dw_bf16_kernel(const bf16* __restrict__ X, int64_t ldx,
+                                                                const bf16* __restrict__ G, int64_t ldg,
+                                                                float* __restrict__ part, int64_t w_numel,
+                                                                int64_t rows, int64_t rows_per_chunk,
+                                                                const LinDW* __restrict__ jobs) {
+  __shared__ __attribute__((aligned(16))) uint16_t xt[2][kLinURows * kBTP];
+  __shared__ __attribute__((aligned(16))) uint16_t gt[2][kLinCols * kBTP];
+  const LinDW jb = ldc(jobs + blockIdx.y);
+  const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
+  const int li = lane & 15, lk = lane >> 4;
+  const int64_t z0 = int64_t(blockIdx.x) * rows_per_chunk;
+  const int64_t z1 = z0 + rows_per_chunk < rows ? z0 + rows_per_chunk : rows;
+  const int ub = 32 * wave;  // this wave's weight rows within the tile
+  v4f acc[2][8];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[s][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  const u16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  const uint16_t* __restrict__ Xs = reinterpret_cast<const uint16_t*>(X);
+  const uint16_t* __restrict__ Gs = reinterpret_cast<const uint16_t*>(G);
+  // one 32-row step: 512 runs of 8 for x (row, u run) and as many for g,
+  // two of each per thread, requested from clamped addresses, masked when stashed
+  u16x8 px[2], pg[2];
+  auto unit = [&](int q, int& r, int& n) {
+    const int u = int(threadIdx.x) + q * kLinThreads;
+    r = u >> 4;
+    n = (u & 15) * 8;
+  };
+  const int nsteps = int((z1 - z0 + kKB - 1) / kKB);
+  const int total = jb.nm * nsteps;
+  auto fetch = [&](int it) {
+    const int m = it / nsteps;
+    const int64_t zs = z0 + int64_t(it - m * nsteps) * kKB;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      int r, n;
+      unit(q, r, n);
+      const int64_t z = zs + r;
+      const bool zok = it < total && z < z1;
+      const int64_t zr = zok ? z : z0;
+      const int mm = it < total ? m : 0;
+      px[q] = *reinterpret_cast<const u16x8*>(Xs + zr * ldx + jb.x_off + int64_t(mm) * jb.mu +
+                                              (jb.u0 + n < jb.mu ? jb.u0 + n : 0));
+      pg[q] = *reinterpret_cast<const u16x8*>(Gs + zr * ldg + jb.g_off + int64_t(mm) * jb.mv +
+                                              (jb.v0 + n < jb.mv ? jb.v0 + n : 0));
+    }
+  };
+  auto stash = [&](int it, int buf) {
+    const int m = it / nsteps;
+    const int64_t zs = z0 + int64_t(it - m * nsteps) * kKB;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      int r, n;
+      unit(q, r, n);
+      const bool zok = it < total && zs + r < z1;
+      const u16x8 vx = (zok && jb.u0 + n < jb.mu) ? px[q] : zero8;
+      const u16x8 vg = (zok && jb.v0 + n < jb.mv) ? pg[q] : zero8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        xt[buf][(n + j) * kBTP + r] = vx[j];
+        gt[buf][(n + j) * kBTP + r] = vg[j];
+      }
+    }
+  };
+  if (total > 0) {
+    fetch(0);
+    stash(0, 0);
+    __syncthreads();
+    for (int it = 0; it < total; ++it) {
+      fetch(it + 1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the MFMAs
+      const uint16_t* __restrict__ xc = xt[it & 1];
+      const uint16_t* __restrict__ gc = gt[it & 1];
+      bf16x8 av[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        av[s2] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(xc + (ub + 16 * s2 + li) * kBTP + 8 * lk));
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(gc + (16 * tt + li) * kBTP + 8 * lk));
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+          acc[s2][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s2], bv, acc[s2][tt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // the requests complete behind the MFMAs
+      stash(it + 1, (it + 1) & 1);
+      __syncthreads();
+    }
+  }
+  float* __restrict__ pc = part + int64_t(blockIdx.x) * w_numel + jb.w_off;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int u = jb.u0 + ub + 16 * s + 4 * lk + r, v = jb.v0 + 16 * tt + li;
+        if (u < jb.mu && v < jb.mv) pc[int64_t(u) * jb.mv + v] = acc[s][tt][r];
+      }
+}
+
 // grad_W[j] = sum over chunks c (ascending) of part[c][j]
 template <typename T>
 __global__ __launch_bounds__(kLinThreads) void lin_colsum_kernel(const float* __restrict__ part, T* __restrict__ out,
@@ -442,7 +549,7 @@ struct LinTables {
   LinDW* wjobs = nullptr;
   int nf = 0, nx = 0, nw = 0;
   bool avec_f = true, avec_x = true;  // 4-aligned A offsets and K (row strides checked per call)
-  bool v8_f = true, v8_x = true;      // every offset and width a multiple of 8 (bf16 matrix-core kernel)
+  bool v8_f = true, v8_x = true, v8_w = true;  // offsets and widths multiples of 8 (bf16 matrix-core kernels)
 };
 
 std::mutex g_lin_mu;
@@ -508,6 +615,9 @@ const LinTables& lin_tables(const cgtp_linear_s* lin) {
       for (int v0 = 0; v0 < p.mv; v0 += kLinCols)
         wj.push_back(LinDW{int32_t(lin->in_off[size_t(p.i)]), p.mu, int32_t(lin->out_off[size_t(p.o)]), p.mv,
                            2 * p.l + 1, int32_t(p.w_off), u0, v0});
+  for (const auto& p : lin->paths)
+    t.v8_w = t.v8_w && p.mu % 8 == 0 && p.mv % 8 == 0 && lin->in_off[size_t(p.i)] % 8 == 0 &&
+             lin->out_off[size_t(p.o)] % 8 == 0;
   t.fjobs = upload(fj);
   t.fterms = upload(ft);
   t.xjobs = upload(xj);
@@ -581,9 +691,16 @@ void backward_typed(const cgtp_linear_s* lin, int64_t B, const void* x, const vo
     const int64_t nch = dw_chunks(B);
     float* part = static_cast<float*>(ws);
     if (nch > 0 && t.nw > 0) {
-      hipLaunchKernelGGL((lin_dw_kernel<T>), dim3(unsigned(nch), unsigned(t.nw)), dim3(kLinThreads), 0, s,
-                         static_cast<const T*>(x), lin->dim_in, static_cast<const T*>(g), lin->dim_out, part,
-                         lin->w_numel, B, dw_rows_per_chunk(B), t.wjobs);
+      const bool mfma16 = std::is_same<T, bf16>::value && CGTP_LINEAR_BF16_MFMA && t.v8_w && lin->dim_in % 8 == 0 &&
+                          lin->dim_out % 8 == 0 && aligned16(x, 16) && aligned16(g, 16);
+      if (mfma16)
+        hipLaunchKernelGGL(lin_dw_bf16_kernel, dim3(unsigned(nch), unsigned(t.nw)), dim3(kLinThreads), 0, s,
+                           static_cast<const bf16*>(x), lin->dim_in, static_cast<const bf16*>(g), lin->dim_out, part,
+                           lin->w_numel, B, dw_rows_per_chunk(B), t.wjobs);
+      else
+        hipLaunchKernelGGL((lin_dw_kernel<T>), dim3(unsigned(nch), unsigned(t.nw)), dim3(kLinThreads), 0, s,
+                           static_cast<const T*>(x), lin->dim_in, static_cast<const T*>(g), lin->dim_out, part,
+                           lin->w_numel, B, dw_rows_per_chunk(B), t.wjobs);
       CGTP_CHECK_HIP(hipGetLastError());
     }
     hipLaunchKernelGGL((lin_colsum_kernel<T>), dim3(unsigned((lin->w_numel + kLinThreads - 1) / kLinThreads)),
