@@ -42,6 +42,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 WORKLOADS = ["tp_large", "tp_large_bf16", "conv_water1k", "conv_water8k", "conv_uniform100k", "linear_large",
              "linear_large_bf16", "tp_large_collapsed", "conv_collapsed_l3", "conv_collapsed_l4"]
 MFMA_FP32_PEAK_TFS = 157.3
+MFMA_BF16_PEAK_TFS = 2500.0
 
 
 def parse():
@@ -514,8 +515,9 @@ def tp_variants_bench(args, torch, cgtp, synth):
 
 
 def linear_bench(args, torch, cgtp, synth, dtype):
-    """Equivariant linear map (fp32 MFMA) on the tensor-product rows: call times,
-    TFLOP/s against the fp32 matrix-core peak, and algorithmic GB/s."""
+    """Equivariant linear map on the tensor-product rows (fp32 matrix cores for fp32
+    storage, bf16 matrix cores for bf16 storage): call times, TFLOP/s against the
+    matching matrix-core peak, and algorithmic GB/s."""
     wl = LinearWorkload(torch, cgtp, synth, dtype)
     B = wl.B
     tf, tx, tw = KernelTimer(torch), KernelTimer(torch), KernelTimer(torch)
@@ -535,9 +537,14 @@ def linear_bench(args, torch, cgtp, synth, dtype):
                                  ("bwd_w", tw, wl.es * B * 2 * dim, "lin_dw_kernel")):
         ms = t.mean_ms()
         tfs = wl.flops / (ms * 1e-3) / 1e12
-        res[key] = dict(kernel=kern, ms=round(ms, 3), TFLOPs=round(tfs, 1),
-                        frac_of_fp32_mfma_peak=round(tfs / MFMA_FP32_PEAK_TFS, 3),
-                        algorithmic_GBs=round(nbytes / (ms * 1e-3) / 1e9, 1), traffic=traffic_for(kern, wname, B))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        # fp32 storage: fp32 matrix cores; bf16 storage (this shape): bf16 matrix cores
+        peak = MFMA_FP32_PEAK_TFS if dtype == "f32" else MFMA_BF16_PEAK_TFS
+        res[key] = dict(kernel=kern if dtype == "f32" else kern.replace("_kernel", "_bf16_kernel"), ms=round(ms, 3),
+                        TFLOPs=round(tfs, 1), mfma_peak_TFLOPs=peak, frac_of_mfma_peak=round(tfs / peak, 3),
+                        algorithmic_GBs=round(gbs, 1), frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 3),
+                        traffic=traffic_for(kern if dtype == "f32" else kern.replace("_kernel", "_bf16_kernel"),
+                                            wname, B))
     del wl
     torch.cuda.empty_cache()
     return res
