@@ -41,6 +41,12 @@
 // and largest degree <= 3 ask the allocator for CGTP_TP_BWD_WAVES waves per
 // SIMD (tp_large fp32 backward 27.7 -> 25.6 ms, bf16 23.2 -> 20.0 ms against
 // registers and no request); the others make no request.
+// The one-launch backward with 2-byte storage keeps its registers (no spill)
+// at 2 waves per SIMD: 3 waves spilled 47 VGPRs and were slower (18.5 vs
+// 17.7 ms on tp_large bf16).
+#ifndef CGTP_TP_BWD_WAVES_BF16_ALL
+#define CGTP_TP_BWD_WAVES_BF16_ALL 2
+#endif
 #ifndef CGTP_TP_BWD_DX_LDS
 #define CGTP_TP_BWD_DX_LDS 1
 #endif
@@ -448,8 +454,8 @@ struct TPBwd {
 // (requested only where the spill it costs stays small: largest degree <= 3)
 template <typename T, int L1, int LM>
 struct BwdWaves {
-  static constexpr int value =
-      ((L1 >= 0 || L1 == -2) && LM <= 3 && sizeof(T) <= 4 && CGTP_TP_BWD_WAVES > 1) ? CGTP_TP_BWD_WAVES : 1;
+  static constexpr int waves = sizeof(T) == 2 && L1 == -2 ? CGTP_TP_BWD_WAVES_BF16_ALL : CGTP_TP_BWD_WAVES;
+  static constexpr int value = ((L1 >= 0 || L1 == -2) && LM <= 3 && sizeof(T) <= 4 && waves > 1) ? waves : 1;
 };
 
 template <typename T, typename A, int VEC, int L1, int LM>
