@@ -652,15 +652,14 @@ void rows_launch(const T* A, int64_t lda, const T* W, T* C, int64_t ldc, int64_t
 }
 
 // bf16 with 8-aligned offsets, widths and row strides: the bf16 matrix-core kernel
-bool rows_bf16_mfma(const void* A, int64_t lda, const void* W, void* C, int64_t ldc, int64_t rows,
+bool rows_bf16_mfma(const void* A, int64_t lda, const void* W, void* C, int64_t ldcr, int64_t rows,
                     const LinJob* jobs, const LinTerm* terms, int njobs, bool v8, hipStream_t s) {
   if (!v8 || lda % 8 != 0 || !aligned16(A, 16) || !aligned16(W, 16) || CGTP_LINEAR_BF16_MFMA == 0) return false;
   if (rows == 0 || njobs == 0) return true;
   const dim3 grid(unsigned((rows + kLinRows - 1) / kLinRows), unsigned(njobs));
   hipLaunchKernelGGL(lin_rows_bf16_kernel, grid, dim3(kLinThreads), 0, s, static_cast<const bf16*>(A), lda,
-                     static_cast<const bf16*>(W), static_cast<bf16*>(C), ldc, rows, jobs, terms);
+                     static_cast<const bf16*>(W), static_cast<bf16*>(C), ldcr, rows, jobs, terms);
   CGTP_CHECK_HIP(hipGetLastError());
-  (void)ldc;
   return true;
 }
 
