@@ -160,8 +160,7 @@ cgtp_status cgtp_tp_backward(cgtp_plan plan, int64_t B, const void* x, const voi
     if (B == 0) {
       // an empty batch still defines a (zero) gradient for shared weights
       if (grad_w && plan->wkind == CGTP_W_SHARED)
-        CGTP_CHECK_HIP(hipMemsetAsync(grad_w, 0, size_t(plan->w_numel) * dtype_size(plan->dtype),
-                                      as_stream(stream)));
+        zero_rows(grad_w, plan->w_numel, dtype_size(plan->dtype), as_stream(stream));
       return;
     }
     need(x && y && w && grad_out, "NULL input tensor with B > 0");
@@ -178,7 +177,12 @@ cgtp_status cgtp_tp_double_backward(cgtp_plan plan, int64_t B, const void* x, co
   return guarded([&] {
     need(plan != nullptr, "NULL plan");
     need(B >= 0, "B < 0");
-    if (B == 0) return;
+    if (B == 0) {
+      // shared weights still get their (zero) cotangent from an empty batch
+      if (out_w && plan->wkind == CGTP_W_SHARED)
+        zero_rows(out_w, plan->w_numel, dtype_size(plan->dtype), as_stream(stream));
+      return;
+    }
     need(x && y && w && grad_out, "NULL input tensor");
     tp_double_backward_launch(plan, B, x, y, w, grad_out, gg_x, gg_y, gg_w, out_x, out_y, out_w, out_grad_out, ws,
                               ws_bytes, as_stream(stream));

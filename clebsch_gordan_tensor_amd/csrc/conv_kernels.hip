@@ -202,7 +202,7 @@ bool conv_backward_fused(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x
 void conv_forward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x, const void* sh,
                          const void* w, double scale, void* out, hipStream_t s) {
   if (g->E == 0) {
-    CGTP_CHECK_HIP(hipMemsetAsync(out, 0, size_t(g->N) * plan->dim_out * dtype_size(plan->dtype), s));
+    zero_rows(out, g->N * plan->dim_out, dtype_size(plan->dtype), s);
     return;
   }
   const DevTables& t = plan_tables(plan);
@@ -228,7 +228,7 @@ void conv_backward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* 
                           void* grad_sh, void* grad_w, void* ws, size_t ws_bytes, hipStream_t s) {
   if (g->E == 0) {
     if (grad_x && g->N > 0)
-      CGTP_CHECK_HIP(hipMemsetAsync(grad_x, 0, size_t(g->N) * plan->dim_x * dtype_size(plan->dtype), s));
+      zero_rows(grad_x, g->N * plan->dim_x, dtype_size(plan->dtype), s);
     return;
   }
   if (grad_x) {

@@ -162,7 +162,8 @@ cgtp_status cgtp_tp_forward(cgtp_plan plan, int64_t B, const void* x, const void
  *   grad_w[(z,)p,u]   = sum_{(z),m1,m2,m3} C x[m1,u] y[m2] g[m3,u]
  * A SHARED plan sums grad_w over rows in a fixed two-stage order; that needs
  * a workspace of cgtp_workspace_size(plan, NULL, B, CGTP_OP_TP_BACKWARD)
- * bytes (0 for PER_ROW). Errors: WORKSPACE if ws is NULL or too small. */
+ * bytes (0 for PER_ROW). B = 0 writes a zero grad_w for SHARED plans and is
+ * otherwise a no-op. Errors: WORKSPACE if ws is NULL or too small. */
 cgtp_status cgtp_tp_backward(cgtp_plan plan, int64_t B, const void* x, const void* y, const void* w,
                              const void* grad_out, void* grad_x, void* grad_y, void* grad_w,
                              void* ws, size_t ws_bytes, void* stream);
@@ -181,7 +182,8 @@ cgtp_status cgtp_tp_backward(cgtp_plan plan, int64_t B, const void* x, const voi
  * are [W] for SHARED plans). A NULL cotangent counts as zero; a NULL output is
  * not computed; outputs no cotangent reaches are written as zeros. Needs
  * cgtp_workspace_size(plan, NULL, B, CGTP_OP_TP_DOUBLE_BACKWARD) bytes of
- * workspace (partial results). Errors: WORKSPACE, INVALID_ARG (null inputs). */
+ * workspace (partial results). B = 0 writes a zero out_w for SHARED plans and
+ * is otherwise a no-op. Errors: WORKSPACE, INVALID_ARG (null inputs). */
 cgtp_status cgtp_tp_double_backward(cgtp_plan plan, int64_t B, const void* x, const void* y, const void* w,
                                     const void* grad_out, const void* gg_x, const void* gg_y, const void* gg_w,
                                     void* out_x, void* out_y, void* out_w, void* out_grad_out, void* ws,

@@ -166,3 +166,37 @@ def test_conv_water1k_force_training_sampled():
     rhs = torch.sum(gY.double() * dY.double()).item() + torch.sum(gw.double() * dw.double()).item()
     scale = torch.sum((gY.double() * dY.double()).abs()).item() + torch.sum((gw.double() * dw.double()).abs()).item()
     assert abs(lhs - rhs) <= 1e-5 * scale
+
+
+def test_empty_batch_and_edgeless_graph():
+    """B = 0: a shared-weight plan still gets a zero cotangent for w; a graph
+    without edges gives zero cotangents for x and grad_out (outputs are
+    pre-filled with NaN so an unwritten one fails)."""
+    c = synth.CONFIGS["tp_small"]
+    plan = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"], wkind="shared")
+    z = lambda *s: torch.zeros(s, device="cuda")
+    nan = lambda *s: torch.full(s, float("nan"), device="cuda")
+    x, y, g = z(0, plan.dim_x), z(0, plan.dim_y), z(0, plan.dim_out)
+    w = torch.randn(plan.w_numel, device="cuda")
+    gw = torch.randn(plan.w_numel, device="cuda")
+    ddw = nan(plan.w_numel)
+    outs = plan.tp_double_backward(x, y, w, g, gg=(None, None, gw),
+                                   out=(None, None, ddw, None))
+    torch.cuda.synchronize()
+    assert outs[2] is ddw and float(ddw.abs().max()) == 0.0
+    assert outs[0].shape == (0, plan.dim_x) and outs[3].shape == (0, plan.dim_out)
+
+    cp = synth.CONFIGS["conv_water1k"]
+    plan = cgtp.Plan(cp["irreps_x"], cp["irreps_y"], cp["irreps_out"])
+    N = 5
+    graph = cgtp.Graph(N, torch.zeros(N + 1, dtype=torch.int32, device="cuda"),
+                       torch.zeros(0, dtype=torch.int32, device="cuda"))
+    x, g = torch.randn(N, plan.dim_x, device="cuda"), torch.randn(N, plan.dim_out, device="cuda")
+    sh, w = z(0, plan.dim_y), z(0, plan.w_numel)
+    gx = torch.randn(N, plan.dim_x, device="cuda")
+    ddx, ddg = nan(N, plan.dim_x), nan(N, plan.dim_out)
+    outs = plan.conv_double_backward(graph, x, sh, w, 0.5, g, gg=(gx, z(0, plan.dim_y), z(0, plan.w_numel)),
+                                     out=(ddx, None, None, ddg))
+    torch.cuda.synchronize()
+    assert float(ddx.abs().max()) == 0.0 and float(ddg.abs().max()) == 0.0
+    assert outs[1].shape == (0, plan.dim_y) and outs[2].shape == (0, plan.w_numel)
