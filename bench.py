@@ -40,7 +40,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "TP pairs/s + conv edges/s (fwd, fwd+bwd) as HBM GB/s and % of MI355X peak"
 PROFILES = os.path.join(ROOT, "profiles")
 WORKLOADS = ["tp_large", "tp_large_bf16", "conv_water1k", "conv_water8k", "conv_uniform100k", "linear_large",
-             "linear_large_bf16", "tp_large_collapsed", "conv_collapsed_l3", "conv_collapsed_l4"]
+             "linear_large_bf16", "tp_large_collapsed", "conv_collapsed_l3", "conv_collapsed_l4",
+             "conv_uniform100k_f64"]
 MFMA_FP32_PEAK_TFS = 157.3
 MFMA_BF16_PEAK_TFS = 2500.0
 
@@ -161,16 +162,20 @@ class TPWorkload:
 
 
 class ConvWorkload:
-    """One convolution workload at full size, fp32: graph, harmonics and radial
+    """One convolution workload at full size: graph, harmonics and radial
     weights built as the benchmark description states (weights by the caller's
-    radial network, not timed), then forward / backward calls."""
+    radial network, not timed), then forward / backward calls. fp32 by default;
+    ``dtype="f64"`` builds the inputs in fp64 for the forward alone (the grads
+    of the 100k-point workload would not fit beside fp64 weights)."""
 
-    def __init__(self, torch, cgtp, synth, name):
+    def __init__(self, torch, cgtp, synth, name, dtype="f32"):
         import numpy as np
         c = synth.CONFIGS[name]
         self.torch, self.cgtp, self.c = torch, cgtp, c
+        self.es = 8 if dtype == "f64" else 4
+        td = torch.float64 if dtype == "f64" else torch.float32
         dev = torch.device("cuda:0")
-        self.plan = p = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"], dtype="f32", wkind="per_row",
+        self.plan = p = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"], dtype=dtype, wkind="per_row",
                                   collapse=c.get("collapse", False))
         pos = synth.positions_for(c, 0)
         src, dst, vec = synth.radius_graph(pos, c["box"], c["r_cut"])
@@ -179,20 +184,22 @@ class ConvWorkload:
                                                  torch.from_numpy(dst.astype(np.int32)).to(dev))
         self.row_ptr, self.src_s = row_ptr, src_s
         self.graph = cgtp.Graph(N, row_ptr, src_s)
-        self.vec = torch.from_numpy(vec).to(dev)[perm.long()].float().contiguous()
+        self.vec = torch.from_numpy(vec).to(dev)[perm.long()].to(td).contiguous()
         self.Y = cgtp.sh_forward(c["L"], self.vec)
         W1, W2 = synth.mlp_params(8, 64, p.w_numel, 0)
-        W1, W2 = torch.from_numpy(W1).float().to(dev), torch.from_numpy(W2).float().to(dev)
+        W1, W2 = torch.from_numpy(W1).to(td).to(dev), torch.from_numpy(W2).to(td).to(dev)
         r = self.vec.norm(dim=1)
-        self.w = torch.empty((E, p.w_numel), device=dev)
+        self.w = torch.empty((E, p.w_numel), device=dev, dtype=td)
         for a in range(0, E, 1 << 20):
             self.w[a:a + (1 << 20)] = synth.radial_weights_torch(r[a:a + (1 << 20)], c["r_cut"], W1, W2)
         gen = torch.Generator(device=dev)
         gen.manual_seed(0)
-        self.x = torch.randn((N, p.dim_x), generator=gen, device=dev)
-        self.gout = torch.randn((N, p.dim_out), generator=gen, device=dev)
+        self.x = torch.randn((N, p.dim_x), generator=gen, device=dev, dtype=td)
         self.scale = 1.0 / math.sqrt(E / N)
-        self.out = torch.empty((N, p.dim_out), device=dev)
+        self.out = torch.empty((N, p.dim_out), device=dev, dtype=td)
+        if dtype == "f64":
+            return
+        self.gout = torch.randn((N, p.dim_out), generator=gen, device=dev)
         self.dx, self.dY, self.dw = torch.empty_like(self.x), torch.empty_like(self.Y), torch.empty_like(self.w)
         self.ws = torch.empty(p.workspace_size(cgtp.OP_CONV_BACKWARD, graph=self.graph), dtype=torch.uint8,
                               device=dev)
@@ -211,9 +218,9 @@ class ConvWorkload:
     def sh_bwd(self):
         self.cgtp.sh_backward(self.c["L"], self.vec, self.dY, out=self.gvec)
 
-    def bytes_fwd(self):  # w, sh, src read per edge; x read and out written per node; row_ptr
+    def bytes_fwd(self):  # w, sh read per edge; x read and out written per node; src, row_ptr
         p = self.plan
-        return 4 * (p.w_numel + p.dim_y + 1) * self.E + 4 * (p.dim_out + p.dim_x + 1) * self.N
+        return (self.es * (p.w_numel + p.dim_y) + 4) * self.E + (self.es * (p.dim_out + p.dim_x) + 4) * self.N
 
     def bytes_bwd(self):  # + grad w, grad sh written per edge; grad_out read, grad x written per node
         p = self.plan
@@ -260,6 +267,8 @@ def make_workload(torch, cgtp, synth, name):
         return TPWorkload(torch, cgtp, synth, "bf16")
     if name == "tp_large_collapsed":
         return TPWorkload(torch, cgtp, synth, "f32", collapse=True)
+    if name.endswith("_f64"):
+        return ConvWorkload(torch, cgtp, synth, name[:-4], "f64")
     return ConvWorkload(torch, cgtp, synth, name)
 
 
@@ -268,6 +277,8 @@ def profile(torch, cgtp, synth, name):
     wl = make_workload(torch, cgtp, synth, name)
     if name.startswith("linear"):
         ops = [wl.fwd, wl.bwd_x, wl.bwd_w]
+    elif name.endswith("_f64"):
+        ops = [wl.fwd]
     else:
         ops = [wl.sh, wl.fwd, wl.bwd] if name.startswith("tp") else [wl.sh_fwd, wl.fwd, wl.bwd, wl.sh_bwd]
     for _ in range(3):
@@ -392,6 +403,27 @@ def conv_bench(args, torch, cgtp, synth, name, steps, forces=False):
     if forces:
         res.update(sh_fwd_ms=round(tsf.mean_ms(), 4), sh_bwd_ms=round(tsb.mean_ms(), 4),
                    fwd_bwd_forces_edges_per_s=E / ((msf + msb + tsf.mean_ms() + tsb.mean_ms()) * 1e-3))
+    del wl
+    torch.cuda.empty_cache()
+    return res
+
+
+def conv_f64_forward_bench(args, torch, cgtp, synth, name="conv_uniform100k"):
+    """The convolution forward with fp64 storage and arithmetic on one full-size
+    workload (the 100k-point stress case asks for it), three timed calls."""
+    wl = ConvWorkload(torch, cgtp, synth, name, "f64")
+    E = wl.E
+    tf = KernelTimer(torch)
+    wl.fwd()
+    for _ in range(3):
+        tf(wl.fwd)
+    torch.cuda.synchronize()
+    bf, ms = wl.bytes_fwd(), tf.mean_ms()
+    res = dict(N=wl.N, E=E, paths=wl.plan.num_paths, fwd_ms=round(ms, 3), fwd_edges_per_s=E / (ms * 1e-3),
+               fwd_algorithmic_GBs=round(bf / (ms * 1e-3) / 1e9, 1),
+               fwd_frac_of_hbm_peak=round(bf / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               fwd_bytes_per_edge=bf / E,
+               fwd_traffic_bytes=traffic_for("conv_fwd_fused_kernel", name + "_f64", E))
     del wl
     torch.cuda.empty_cache()
     return res
@@ -604,6 +636,7 @@ def main():
         for name in ("conv_water1k", "conv_water8k", "conv_uniform100k", "conv_collapsed_l3", "conv_collapsed_l4"):
             extra[name] = conv_bench(args, torch, cgtp, synth, name, max(2, min(args.steps, 5)),
                                      forces=name == "conv_water8k")
+        extra["conv_uniform100k_f64"] = conv_f64_forward_bench(args, torch, cgtp, synth)
         extra["conv_water8k_double_backward"] = double_backward_bench(args, torch, cgtp, synth)
         extra["conv_water1k_padded"] = padding_bench(args, torch, cgtp, synth)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, synth)

@@ -366,8 +366,26 @@ __device__ __forceinline__ void fwd_fused_chunk(const ConvArgs& a, int64_t n, co
 // one workgroup's waves read the same rows. With collapsed outputs (COL) the
 // chunks hold whole output types, so no two waves of a launch add into the
 // same block.
+#ifndef CGTP_CONV_FWD_WAVES
+#define CGTP_CONV_FWD_WAVES 0
+#endif
+// waves per SIMD a forward kernel is compiled for (0 in the macro: per
+// kernel). The fp64 kernels of x blocks of degree 2-4 at L = 4 take 173-175
+// VGPRs (2 waves) when left alone and fit under the 3-wave line (168) without
+// spilling: 12 % faster on the 100k-point workload. Kernels already under the
+// line are left alone: the hint made the compiler squeeze the degree-1 one
+// (167 -> 149 VGPRs at the same occupancy) and it ran 35 % slower; the
+// collapsed-output kernels would spill.
+template <typename T, int L1, int L, bool COL>
+struct ConvFwdWaves {
+  static constexpr int value = CGTP_CONV_FWD_WAVES != 0 ? CGTP_CONV_FWD_WAVES
+                               : (std::is_same<T, double>::value && !COL && L == 4 && L1 >= 2) ? 3
+                                                                                              : 1;
+};
+
 template <typename T, typename A, int VEC, int L1, int L, bool COL>
-__global__ __launch_bounds__(kBlock) void conv_fwd_fused_kernel(ConvArgs a) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(ConvFwdWaves<T, L1, L, COL>::value)))
+void conv_fwd_fused_kernel(ConvArgs a) {
   using CK = Chunks<SlotsOf<L1, L, COL>, conv_budget<A, VEC>()>;
   const int64_t item = xcd_block() * kWaves + conv_wave_id();
   const int64_t per_node = int64_t(CK::NCH) * a.nchunks;
@@ -482,8 +500,23 @@ struct ConvBwdArgs {
 //   grad_w  = sum_m1 x[m1] q[m1]                          -> stored per edge
 //   dx_e   += w q[m1]                                     -> per-edge partial
 //   dy[m2] += C sum_u w x[m1] g[m3]                       -> reduced over the group
+#ifndef CGTP_CONV_BWD_WAVES
+#define CGTP_CONV_BWD_WAVES 0
+#endif
+// waves per SIMD the backward is compiled for (0 in the macro: per kernel).
+// The fp32 (l1, L) = (2, 4) kernel needs two registers more than the 3-wave
+// line when left alone and fits under it without spilling; the larger ones
+// would spill.
+template <typename T, int L1, int L>
+struct ConvBwdWaves {
+  static constexpr int value = CGTP_CONV_BWD_WAVES != 0                                      ? CGTP_CONV_BWD_WAVES
+                               : (std::is_same<T, float>::value && L1 == 2 && L == 4) ? 3
+                                                                                          : 1;
+};
+
 template <typename T, typename A, int VEC, int L1, int L>
-__global__ __launch_bounds__(kBlock) void conv_bwd_fused_kernel(ConvArgs a, ConvBwdArgs bw) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(ConvBwdWaves<T, L1, L>::value)))
+void conv_bwd_fused_kernel(ConvArgs a, ConvBwdArgs bw) {
   using S = Slots<L1, L>;
   constexpr int NS = S::NS;
   constexpr int NY = (L + 1) * (L + 1);
