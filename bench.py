@@ -612,7 +612,7 @@ def cpu_baseline(args, synth):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d refused)"
+        print("bench.py measures one GPU only: the library has no multi-GPU path (--gpus %d refused)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch

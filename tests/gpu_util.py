@@ -10,8 +10,10 @@ from the HIP path.
 import numpy as np
 
 # Relative error bars: max |gpu - ref| / max |ref| over each output block
-# (fp32 and fp64 from the benchmark description; bf16 derived in the design doc:
-# bf16 outputs round to 2^-9 relative, fp32 accumulation adds ~1e-6).
+# (fp32 and fp64 from the benchmark description; bf16 derived from its
+# arithmetic: bf16 outputs round to 2^-9 relative, inputs stored in bf16 are
+# exact on both sides, and fp32 accumulation adds ~1e-6; 2^-7 leaves a factor
+# of 4 for the relative error of a block's largest element).
 TOL = {"f32": 1e-5, "f64": 1e-12, "bf16": 2.0 ** -7}
 
 
