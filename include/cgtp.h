@@ -43,6 +43,13 @@
  *    A NULL gradient pointer skips that gradient.
  *  - Results are deterministic: every sum has a fixed order, no atomics touch
  *    floating-point data, and repeated calls are bitwise identical.
+ *  - Graph capture: a plan's (or linear map's) first compute call on a device
+ *    uploads its tables (allocation and a synchronous copy); after it, the
+ *    compute calls (tensor product, convolution, harmonics, linear map and
+ *    their backward / double backward) only launch kernels on `stream` (fills
+ *    by kernel, no memset nodes), so they can be captured in a HIP graph and
+ *    replayed. cgtp_csr_from_coo, graph create and graph transpose allocate
+ *    or synchronise and are not capturable.
  *  - Errors are status codes; cgtp_last_error() returns a thread-local
  *    message for the last failure. Nothing else escapes the ABI.
  */
