@@ -123,6 +123,16 @@ def _need(t, shape, dtype, name):
     return t
 
 
+def _ws_bytes(ws):
+    """Size in bytes of a caller-provided workspace (any dtype), which must be
+    a contiguous device tensor."""
+    if not ws.is_cuda:
+        raise ValueError("workspace must be a device tensor")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return ws.numel() * ws.element_size()
+
+
 _SEL = {"all": 0, "symmetric": 1, "skew": 2}
 
 
@@ -225,7 +235,7 @@ class Plan:
             ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
         _check(_lib.cgtp_tp_backward(self._h, B, _ptr(x), _ptr(y), _ptr(w), _ptr(grad_out),
                                      _ptr(res[0]), _ptr(res[1]), _ptr(res[2]),
-                                     _ptr(ws) if nws else _vp(0), ws.numel() if nws else 0, _stream(x)),
+                                     _ptr(ws) if nws else _vp(0), _ws_bytes(ws) if nws else 0, _stream(x)),
                "cgtp_tp_backward")
         return tuple(res)
 
@@ -272,7 +282,7 @@ class Plan:
         if ws is None:
             ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device)
         _check(_lib.cgtp_tp_double_backward(self._h, B, _ptr(x), _ptr(y), _ptr(w), _ptr(grad_out),
-                                            *[_ptr(t) for t in gg], *[_ptr(t) for t in res], _ptr(ws), ws.numel(),
+                                            *[_ptr(t) for t in gg], *[_ptr(t) for t in res], _ptr(ws), _ws_bytes(ws),
                                             _stream(x)), "cgtp_tp_double_backward")
         return tuple(res)
 
@@ -294,7 +304,7 @@ class Plan:
             ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device)
         _check(_lib.cgtp_conv_double_backward(self._h, graph._h, _ptr(x), _ptr(sh), _ptr(w), float(scale),
                                               _ptr(grad_out), *[_ptr(t) for t in gg], *[_ptr(t) for t in res],
-                                              _ptr(ws), ws.numel(), _stream(x)), "cgtp_conv_double_backward")
+                                              _ptr(ws), _ws_bytes(ws), _stream(x)), "cgtp_conv_double_backward")
         return tuple(res)
 
     def conv_backward(self, graph, x, sh, w, scale, grad_out, need=(True, True, True),
@@ -318,7 +328,7 @@ class Plan:
             ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
         _check(_lib.cgtp_conv_backward(self._h, graph._h, _ptr(x), _ptr(sh), _ptr(w), float(scale),
                                        _ptr(grad_out), _ptr(res[0]), _ptr(res[1]), _ptr(res[2]),
-                                       _ptr(ws) if nws else _vp(0), ws.numel() if nws else 0,
+                                       _ptr(ws) if nws else _vp(0), _ws_bytes(ws) if nws else 0,
                                        _stream(x)), "cgtp_conv_backward")
         return tuple(res)
 
@@ -388,7 +398,7 @@ class Linear:
         if nws and ws is None:
             ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
         _check(_lib.cgtp_linear_backward(self._h, B, _ptr(x), _ptr(w), _ptr(grad_out), _ptr(res[0]), _ptr(res[1]),
-                                         _ptr(ws) if nws else _vp(0), ws.numel() if nws else 0, _stream(x)),
+                                         _ptr(ws) if nws else _vp(0), _ws_bytes(ws) if nws else 0, _stream(x)),
                "cgtp_linear_backward")
         return tuple(res)
 

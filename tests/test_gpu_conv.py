@@ -297,7 +297,17 @@ def test_conv_error_paths():
         plan.conv_backward(case.graph, x, Y, w, 1.0, torch.zeros((case.N, L.dim_out), device="cuda"), ws=small_ws)
     assert e.value.status == 5
     # the workspace size is the per-edge grad_x partials in the accumulation type
-    assert plan.workspace_size(cgtp.OP_CONV_BACKWARD, graph=case.graph) == case.E * L.dim_x * 4
+    nws = plan.workspace_size(cgtp.OP_CONV_BACKWARD, graph=case.graph)
+    assert nws == case.E * L.dim_x * 4
+    g = torch.zeros((case.N, L.dim_out), device="cuda")
+    # a host workspace is refused before any launch; a workspace of another
+    # dtype counts in bytes
+    with pytest.raises(ValueError):
+        plan.conv_backward(case.graph, x, Y, w, 1.0, g, ws=torch.empty(nws, dtype=torch.uint8))
+    dx, _, _ = plan.conv_backward(case.graph, x, Y, w, 1.0, g,
+                                  ws=torch.empty(nws // 4, dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    assert float(dx.abs().max()) == 0.0
 
 
 def radial_chain(vec_d, r_cut, W1, W2, dw, chunk=1 << 18):
