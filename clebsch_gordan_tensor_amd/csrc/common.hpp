@@ -94,6 +94,8 @@ struct cgtp_plan_s {
   // block b are every (l2, l3) with l2, l3 <= conv_L and |l1-l2| <= l3 <= l1+l2,
   // ordered by l2 then l3; slot_paths maps them to path indices (-1 = absent).
   bool conv_fused = false;
+  // collapsed outputs may use the fused forward (y parities are s (-1)^l)
+  bool conv_col_fused = false;
   int conv_L = 0;
   int lm = 0;  // largest degree among y blocks and output paths (kernel specialisation)
   int yoff_by_l[CGTP_LMAX + 1] = {-1, -1, -1, -1, -1};

@@ -81,9 +81,11 @@ struct Slots {
 };
 
 // Slots of a plan with outputs collapsed by (l3, p3). Within one x block the
-// output parity of a slot is fixed by the parity of l2 (harmonics of degree
-// l2 have parity (-1)^l2), so the slots of one output type are those with
-// equal (l2 mod 2, l3): they are listed together and share one accumulator.
+// output parity of a slot is fixed by the parity of l2 when every y block has
+// parity s (-1)^l2 for one sign s (harmonics: s = +1; the planner sends other
+// plans to the general kernel), so the slots of one output type are those
+// with equal (l2 mod 2, l3): they are listed together and share one
+// accumulator.
 constexpr int slot_regs_collapsed(int L1, int L) {
   int n = 0;
   for (int par = 0; par < 2; ++par)

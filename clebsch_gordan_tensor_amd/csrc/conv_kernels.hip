@@ -80,8 +80,9 @@ bool aligned_to(const void* p, size_t bytes) { return (reinterpret_cast<uintptr_
 template <typename T>
 void fwd_typed(cgtp_plan_s* plan, ConvArgs a, hipStream_t s) {
   const size_t vb = size_t(conv_vec(plan->dtype)) * dtype_size(plan->dtype);
-  const bool fused = plan->conv_fused && plan->vec == conv_vec(plan->dtype) && aligned_to(a.x, vb) &&
-                     aligned_to(a.w, vb) && aligned_to(a.out, vb);
+  const bool fused = plan->conv_fused && (!plan->collapse || plan->conv_col_fused) &&
+                     plan->vec == conv_vec(plan->dtype) && aligned_to(a.x, vb) && aligned_to(a.w, vb) &&
+                     aligned_to(a.out, vb);
   if (plan->collapse) {  // the kernels add into the output
     zero_rows(a.out, a.N * int64_t(a.dim_out), dtype_size(plan->dtype), s);
     a.collapse = 1;

@@ -7,10 +7,17 @@
 // Here the integer layout is bit-exact and independent of thread timing:
 // positions are first claimed with integer atomics (whose final counts are
 // exact), then every segment is ordered by a unique key - (src, input index)
-// for the CSR, the CSR position for the transpose - by counting, for each
-// element, the elements of its segment with a smaller key. The cost is
-// O(sum of squared degrees), which suits bounded-degree radius graphs.
+// for the CSR, the CSR position for the transpose. Segments are sorted in
+// runs of kRun elements (each element's rank is the count of smaller keys in
+// its run), then runs are merged pairwise until the longest segment is one
+// run (each element's place in the merged run is its index in its own run
+// plus the count of smaller keys in the partner run, by binary search). With
+// unique keys every step has one result, and the cost is
+// O(E (kRun + log^2 max degree)): a padding node receiving most of the edges
+// (one segment of any length) costs no more than ordinary receivers.
+#include <algorithm>
 #include <memory>
+#include <utility>
 #include <vector>
 
 #include "graph.hpp"
@@ -109,47 +116,87 @@ struct DevBuf {
 unsigned blocks_for(int64_t n, int threads) { return unsigned((n + threads - 1) / threads); }
 
 // ---- CSR by destination
+// flag[0]: invalid index seen; flag[1]: largest destination degree
 __global__ void coo_count(const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
-                          int32_t* __restrict__ counts, int32_t* __restrict__ bad, int64_t N, int64_t E) {
+                          int32_t* __restrict__ counts, int32_t* __restrict__ flag, int64_t N, int64_t E) {
   const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= E) return;
   const int32_t s = src[e], d = dst[e];
   if (s < 0 || s >= N || d < 0 || d >= N) {
-    atomicOr(bad, 1);
+    atomicOr(flag, 1);
     return;
   }
-  atomicAdd(&counts[d], 1);
+  atomicMax(flag + 1, atomicAdd(&counts[d], 1) + 1);
+}
+
+// Sort key of a CSR edge: (src, input index), unique per edge.
+__device__ __forceinline__ uint64_t csr_key(int32_t s, int32_t e) {
+  return (uint64_t(uint32_t(s)) << 32) | uint64_t(uint32_t(e));
 }
 
 __global__ void coo_scatter(const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
                             const int32_t* __restrict__ row_ptr, int32_t* __restrict__ fill,
-                            int32_t* __restrict__ t_src, int32_t* __restrict__ t_dst,
-                            int32_t* __restrict__ t_idx, int64_t E) {
+                            uint64_t* __restrict__ key, int32_t* __restrict__ seg, int64_t E) {
   const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= E) return;
   const int32_t d = dst[e];
   const int32_t pos = row_ptr[d] + atomicAdd(&fill[d], 1);
-  t_src[pos] = src[e];
-  t_dst[pos] = d;
-  t_idx[pos] = int32_t(e);
+  key[pos] = csr_key(src[e], int32_t(e));
+  seg[pos] = d;
 }
 
-// Order each destination segment by (src, input index): rank by counting.
-__global__ void csr_rank(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ t_src,
-                         const int32_t* __restrict__ t_dst, const int32_t* __restrict__ t_idx,
-                         int32_t* __restrict__ src_sorted, int32_t* __restrict__ perm, int64_t E) {
+__global__ void csr_unpack(const uint64_t* __restrict__ key, int32_t* __restrict__ src_sorted,
+                           int32_t* __restrict__ perm, int64_t E) {
   const int64_t k = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (k >= E) return;
-  const int32_t d = t_dst[k];
-  const int32_t lo = row_ptr[d], hi = row_ptr[d + 1];
-  const int32_t ks = t_src[k], ki = t_idx[k];
+  const uint64_t v = key[k];
+  src_sorted[k] = int32_t(v >> 32);
+  perm[k] = int32_t(v & 0xffffffffu);
+}
+
+// ---- segmented sort of unique keys (positions never leave their segment)
+constexpr int kRun = 256;
+
+// Sort runs of kRun consecutive elements of each segment (the last run of a
+// segment may be shorter): an element's place is the count of smaller keys.
+__global__ void seg_sort_runs(const int32_t* __restrict__ seg_ptr, const int32_t* __restrict__ seg,
+                              const uint64_t* __restrict__ in, uint64_t* __restrict__ out, int64_t n) {
+  const int64_t k = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (k >= n) return;
+  const int32_t d = seg[k];
+  const int64_t lo = seg_ptr[d], hi = seg_ptr[d + 1];
+  const int64_t r0 = lo + ((k - lo) / kRun) * kRun;
+  const int64_t r1 = r0 + kRun < hi ? r0 + kRun : hi;
+  const uint64_t v = in[k];
   int32_t rank = 0;
-  for (int32_t j = lo; j < hi; ++j) {
-    const int32_t js = t_src[j], ji = t_idx[j];
-    rank += (js < ks || (js == ks && ji < ki)) ? 1 : 0;
+  for (int64_t j = r0; j < r1; ++j) rank += in[j] < v ? 1 : 0;
+  out[r0 + rank] = v;
+}
+
+// Merge sorted runs of length R pairwise (runs 2i and 2i+1 of a segment).
+__global__ void seg_merge_runs(const int32_t* __restrict__ seg_ptr, const int32_t* __restrict__ seg,
+                               const uint64_t* __restrict__ in, uint64_t* __restrict__ out, int64_t n, int64_t R) {
+  const int64_t k = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (k >= n) return;
+  const int32_t d = seg[k];
+  const int64_t lo = seg_ptr[d], hi = seg_ptr[d + 1];
+  const int64_t r = (k - lo) / R;
+  const int64_t ps = lo + (r ^ 1) * R;
+  const uint64_t v = in[k];
+  if (ps >= hi) {  // no partner run: the element stays
+    out[k] = v;
+    return;
   }
-  src_sorted[lo + rank] = ks;
-  perm[lo + rank] = ki;
+  const int64_t pe = ps + R < hi ? ps + R : hi;
+  int64_t a = ps, b = pe;  // first partner key not below v
+  while (a < b) {
+    const int64_t m = (a + b) >> 1;
+    if (in[m] < v)
+      a = m + 1;
+    else
+      b = m;
+  }
+  out[lo + (r & ~int64_t(1)) * R + (k - lo - r * R) + (a - ps)] = v;
 }
 
 // ---- validation and transpose
@@ -176,27 +223,21 @@ __global__ void src_count(const int32_t* __restrict__ src, int32_t* __restrict__
   if (e < E && (e < pe0 || e >= pe1)) atomicAdd(&counts[src[e]], 1);
 }
 
+// key of a transposed edge: its CSR position (unique)
 __global__ void src_scatter(const int32_t* __restrict__ src, const int32_t* __restrict__ col_ptr,
-                            int32_t* __restrict__ fill, int32_t* __restrict__ t_src,
-                            int32_t* __restrict__ t_pos, int64_t E, int64_t pe0, int64_t pe1) {
+                            int32_t* __restrict__ fill, int32_t* __restrict__ seg,
+                            uint64_t* __restrict__ key, int64_t E, int64_t pe0, int64_t pe1) {
   const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= E || (e >= pe0 && e < pe1)) return;
   const int32_t s = src[e];
   const int32_t pos = col_ptr[s] + atomicAdd(&fill[s], 1);
-  t_src[pos] = s;
-  t_pos[pos] = int32_t(e);
+  seg[pos] = s;
+  key[pos] = uint64_t(e);
 }
 
-__global__ void transpose_rank(const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ t_src,
-                               const int32_t* __restrict__ t_pos, int32_t* __restrict__ eid, int64_t E) {
+__global__ void key_to_i32(const uint64_t* __restrict__ key, int32_t* __restrict__ out, int64_t n) {
   const int64_t k = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (k >= E) return;
-  const int32_t s = t_src[k];
-  const int32_t lo = col_ptr[s], hi = col_ptr[s + 1];
-  const int32_t kp = t_pos[k];
-  int32_t rank = 0;
-  for (int32_t j = lo; j < hi; ++j) rank += t_pos[j] < kp ? 1 : 0;
-  eid[lo + rank] = kp;
+  if (k < n) out[k] = int32_t(key[k]);
 }
 
 __global__ void fill_dst(const int32_t* __restrict__ row_ptr, int32_t* __restrict__ dst, int64_t N) {
@@ -233,29 +274,54 @@ void exclusive_scan_i32(const int32_t* counts, int32_t* out, int64_t n, hipStrea
   CGTP_CHECK_HIP(hipGetLastError());
 }
 
+namespace {
+
+// Sort the unique keys of every segment of seg_ptr (key[k] lies in segment
+// seg[k]); the result is in *a or *b, returned. max_deg bounds the segment
+// lengths (it sets the number of merge passes).
+uint64_t* segmented_sort(const int32_t* seg_ptr, const int32_t* seg, uint64_t* a, uint64_t* b, int64_t n,
+                         int64_t max_deg, hipStream_t s) {
+  if (n == 0) return a;
+  hipLaunchKernelGGL(seg_sort_runs, dim3(blocks_for(n, 256)), dim3(256), 0, s, seg_ptr, seg, a, b, n);
+  CGTP_CHECK_HIP(hipGetLastError());
+  std::swap(a, b);
+  for (int64_t R = kRun; R < max_deg; R *= 2) {
+    hipLaunchKernelGGL(seg_merge_runs, dim3(blocks_for(n, 256)), dim3(256), 0, s, seg_ptr, seg, a, b, n, R);
+    CGTP_CHECK_HIP(hipGetLastError());
+    std::swap(a, b);
+  }
+  return a;
+}
+
+}  // namespace
+
 void csr_from_coo_launch(int64_t N, int64_t E, const int32_t* src, const int32_t* dst,
                          int32_t* row_ptr, int32_t* src_sorted, int32_t* perm, hipStream_t s) {
-  DevBuf counts(size_t(N + 1) * 4), flag(4);
+  DevBuf counts(size_t(N + 1) * 4), flag(8);
   CGTP_CHECK_HIP(hipMemsetAsync(counts.p, 0, size_t(N + 1) * 4, s));
-  CGTP_CHECK_HIP(hipMemsetAsync(flag.p, 0, 4, s));
+  CGTP_CHECK_HIP(hipMemsetAsync(flag.p, 0, 8, s));
   if (E > 0) {
     hipLaunchKernelGGL(coo_count, dim3(blocks_for(E, 256)), dim3(256), 0, s, src, dst,
                        counts.as<int32_t>(), flag.as<int32_t>(), N, E);
     CGTP_CHECK_HIP(hipGetLastError());
   }
-  if (read_flag(flag.as<int32_t>(), s)) throw Error{CGTP_ERR_INDEX, "csr_from_coo: src/dst outside [0, N)"};
+  int32_t hflag[2] = {0, 0};
+  CGTP_CHECK_HIP(hipMemcpyAsync(hflag, flag.p, sizeof(hflag), hipMemcpyDeviceToHost, s));
+  CGTP_CHECK_HIP(hipStreamSynchronize(s));
+  if (hflag[0]) throw Error{CGTP_ERR_INDEX, "csr_from_coo: src/dst outside [0, N)"};
   exclusive_scan_i32(counts.as<int32_t>(), row_ptr, N, s);
   if (E == 0) {
     CGTP_CHECK_HIP(hipStreamSynchronize(s));
     return;
   }
-  DevBuf fill(size_t(N) * 4 + 4), ts(size_t(E) * 4), td(size_t(E) * 4), ti(size_t(E) * 4);
+  DevBuf fill(size_t(N) * 4 + 4), seg(size_t(E) * 4), ka(size_t(E) * 8), kb(size_t(E) * 8);
   CGTP_CHECK_HIP(hipMemsetAsync(fill.p, 0, size_t(N) * 4 + 4, s));
   hipLaunchKernelGGL(coo_scatter, dim3(blocks_for(E, 256)), dim3(256), 0, s, src, dst, row_ptr,
-                     fill.as<int32_t>(), ts.as<int32_t>(), td.as<int32_t>(), ti.as<int32_t>(), E);
+                     fill.as<int32_t>(), ka.as<uint64_t>(), seg.as<int32_t>(), E);
   CGTP_CHECK_HIP(hipGetLastError());
-  hipLaunchKernelGGL(csr_rank, dim3(blocks_for(E, 256)), dim3(256), 0, s, row_ptr, ts.as<int32_t>(),
-                     td.as<int32_t>(), ti.as<int32_t>(), src_sorted, perm, E);
+  const uint64_t* sorted =
+      segmented_sort(row_ptr, seg.as<int32_t>(), ka.as<uint64_t>(), kb.as<uint64_t>(), E, hflag[1], s);
+  hipLaunchKernelGGL(csr_unpack, dim3(blocks_for(E, 256)), dim3(256), 0, s, sorted, src_sorted, perm, E);
   CGTP_CHECK_HIP(hipGetLastError());
   CGTP_CHECK_HIP(hipStreamSynchronize(s));
 }
@@ -283,6 +349,7 @@ cgtp_graph_s* graph_create(int64_t N, int64_t E, const int32_t* row_ptr, const i
                                       "): need row_ptr[0]=0, non-decreasing, row_ptr[N]=E, src in [0,N)"};
   }
   std::vector<int32_t> order;
+  int64_t max_src_deg = 0;
   {
     std::vector<int32_t> hrp(static_cast<size_t>(N + 1));
     std::vector<int32_t> hsrc(static_cast<size_t>(E));
@@ -294,6 +361,10 @@ cgtp_graph_s* graph_create(int64_t N, int64_t E, const int32_t* row_ptr, const i
       g->pad_e0 = hrp[size_t(pad)];
       g->pad_e1 = hrp[size_t(pad) + 1];
     }
+    // largest source degree of the transpose (sets its merge passes)
+    std::vector<int32_t> deg(size_t(N), 0);
+    for (int64_t e = 0; e < E; ++e)
+      if (e < g->pad_e0 || e >= g->pad_e1) max_src_deg = std::max<int64_t>(max_src_deg, ++deg[size_t(hsrc[size_t(e)])]);
   }
   CGTP_CHECK_HIP(hipMalloc(&g->col_ptr, size_t(N + 1) * 4));
   if (hipMalloc(&g->order, size_t(N) * 4 + 4) != hipSuccess) {
@@ -320,16 +391,18 @@ cgtp_graph_s* graph_create(int64_t N, int64_t E, const int32_t* row_ptr, const i
       CGTP_CHECK_HIP(hipMemcpyAsync(g->order, order.data(), size_t(N) * 4, hipMemcpyHostToDevice, s));
     exclusive_scan_i32(counts.as<int32_t>(), g->col_ptr, N, s);
     if (E > 0) {
-      DevBuf fill(size_t(N) * 4 + 4), ts(size_t(E) * 4), tp(size_t(E) * 4);
+      DevBuf fill(size_t(N) * 4 + 4), seg(size_t(E) * 4), ka(size_t(E) * 8), kb(size_t(E) * 8);
       CGTP_CHECK_HIP(hipMemsetAsync(fill.p, 0, size_t(N) * 4 + 4, s));
       hipLaunchKernelGGL(src_scatter, dim3(blocks_for(E, 256)), dim3(256), 0, s, src, g->col_ptr,
-                         fill.as<int32_t>(), ts.as<int32_t>(), tp.as<int32_t>(), E, g->pad_e0, g->pad_e1);
+                         fill.as<int32_t>(), seg.as<int32_t>(), ka.as<uint64_t>(), E, g->pad_e0, g->pad_e1);
       CGTP_CHECK_HIP(hipGetLastError());
       const int64_t Et = g->E_t();
-      if (Et > 0)
-        hipLaunchKernelGGL(transpose_rank, dim3(blocks_for(Et, 256)), dim3(256), 0, s, g->col_ptr,
-                           ts.as<int32_t>(), tp.as<int32_t>(), g->eid, Et);
-      CGTP_CHECK_HIP(hipGetLastError());
+      if (Et > 0) {
+        const uint64_t* sorted = segmented_sort(g->col_ptr, seg.as<int32_t>(), ka.as<uint64_t>(),
+                                                kb.as<uint64_t>(), Et, max_src_deg, s);
+        hipLaunchKernelGGL(key_to_i32, dim3(blocks_for(Et, 256)), dim3(256), 0, s, sorted, g->eid, Et);
+        CGTP_CHECK_HIP(hipGetLastError());
+      }
       hipLaunchKernelGGL(fill_dst, dim3(blocks_for(N, 256)), dim3(256), 0, s, row_ptr, g->dst, N);
       CGTP_CHECK_HIP(hipGetLastError());
     }

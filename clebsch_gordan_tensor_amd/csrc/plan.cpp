@@ -358,6 +358,21 @@ cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const ch
   }
   for (const PathInfo& p : plan->paths) lo = std::max(lo, p.l3);
   plan->conv_fused = distinct;
+  // The collapsed fused forward groups the slots of one x block by
+  // (l2 mod 2, l3), which equals grouping by output type only when every y
+  // block has parity s (-1)^l2 for one common sign s (harmonics: s = +1).
+  // Otherwise two output types could share an accumulator, so such plans
+  // take the general kernel.
+  {
+    int s = 0;
+    bool same = true;
+    for (const Irrep& r : plan->Y) {
+      const int t = r.p * ((r.l % 2) ? -1 : 1);
+      if (s == 0) s = t;
+      same = same && t == s;
+    }
+    plan->conv_col_fused = distinct && same;
+  }
   plan->conv_L = std::max(ly, lo);
   plan->lm = plan->conv_L;
   if (distinct) {

@@ -83,6 +83,7 @@ struct TPArgs {
   int lpr_log2;  // lanes per row = 1 << lpr_log2
   int ngroups;   // channel groups per row = ceil(max_mul / VEC)
   int block;     // x block of a degree-specialised launch
+  int max_l1;    // largest x degree of the plan (LDS rows of the all-blocks backward)
   int dy_accum;  // add grad_y to what an earlier launch on the stream wrote
   // collapsed outputs: the output parity this launch writes and, per parity
   // (index 0: even, 1: odd) and degree l3, the block offset (-1 if absent)
@@ -585,12 +586,20 @@ void tp_fwd_typed(const TPArgs& a, int l1, int lm, hipStream_t s) {
   }
 }
 
+// Dynamic LDS of tp_bwd_kernel: grad_y columns [dim_y][kBlock] and, for the
+// degree-specialised (l1 >= 0) and all-blocks (l1 = -2) kernels with grad_x in
+// LDS, 2 l1 + 1 (all blocks: 2 max_l1 + 1) rows of VEC accumulators per lane.
+inline size_t tp_bwd_lds_bytes(int dim_y, int l1, int max_l1, int vec, size_t acc) {
+  const size_t dx_rows =
+      !CGTP_TP_BWD_DX_LDS || vec == 1 ? 0 : (l1 >= 0 ? 2 * l1 + 1 : l1 == -2 ? 2 * max_l1 + 1 : 0);
+  return size_t(dim_y) * kBlock * acc + dx_rows * kBlock * size_t(vec) * acc;
+}
+
 template <typename T, int VEC>
 void tp_bwd_typed(const TPArgs& a, int l1, int lm, hipStream_t s) {
   using A = typename AccOf<T>::type;
   const dim3 grid = grid_for(a.B, a.lpr_log2);
-  const size_t dx_rows = !CGTP_TP_BWD_DX_LDS || VEC == 1 ? 0 : (l1 >= 0 ? 2 * l1 + 1 : l1 == -2 ? 2 * kLmax + 1 : 0);
-  const size_t lds = size_t(a.dim_y) * kBlock * sizeof(A) + dx_rows * kBlock * VEC * sizeof(A);
+  const size_t lds = tp_bwd_lds_bytes(a.dim_y, l1, a.max_l1, VEC, sizeof(A));
   if constexpr (VEC == 1) {
     (void)l1;
     (void)lm;

@@ -60,6 +60,14 @@ int ilog2_ceil(int v) {
 
 bool aligned(const void* p, size_t bytes) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
 
+// Dynamic LDS a workgroup may take on the current device.
+size_t device_lds_limit() {
+  int dev = 0, v = 0;
+  CGTP_CHECK_HIP(hipGetDevice(&dev));
+  CGTP_CHECK_HIP(hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
+  return size_t(v);
+}
+
 TPArgs make_args(cgtp_plan_s* plan, const DevTables& t, int64_t B, int vec) {
   TPArgs a{};
   a.g_scale = 1.0;
@@ -73,6 +81,8 @@ TPArgs make_args(cgtp_plan_s* plan, const DevTables& t, int64_t B, int vec) {
   a.dim_out = int(plan->dim_out);
   a.W = int(plan->w_numel);
   a.nblocks = int(plan->blocks.size());
+  a.max_l1 = 0;
+  for (const BlockInfo& b : plan->blocks) a.max_l1 = b.l1 > a.max_l1 ? b.l1 : a.max_l1;
   a.ngroups = (plan->max_mul + vec - 1) / vec;
   a.lpr_log2 = ilog2_ceil(a.ngroups < 64 ? a.ngroups : 64);
   return a;
@@ -227,6 +237,17 @@ void tp_backward_rows(cgtp_plan_s* plan, const TPBackwardRows& r, hipStream_t st
       !aligned(r.dx, vec * es) || !aligned(r.dw, vec * es) || !aligned(r.dx_ws, vec * as) ||
       !aligned(r.dw_ws, vec * as))
     vec = 1;
+  // LDS: the vectorised kernels hold grad_y columns and grad_x rows of up to
+  // the largest x degree; when that exceeds the device limit the one-channel
+  // kernel (grad_y columns only) runs, and a plan whose grad_y columns alone
+  // do not fit (many repeated y blocks) is refused
+  int max_l1 = 0;
+  for (const BlockInfo& b : plan->blocks) max_l1 = b.l1 > max_l1 ? b.l1 : max_l1;
+  const size_t lds_max = device_lds_limit();
+  if (vec > 1 && tp_bwd_lds_bytes(int(plan->dim_y), max_l1, max_l1, vec, as) > lds_max) vec = 1;
+  if (tp_bwd_lds_bytes(int(plan->dim_y), -1, max_l1, vec, as) > lds_max)
+    throw Error{CGTP_ERR_UNSUPPORTED, "tp_backward: per-lane grad_y columns of " + std::to_string(plan->dim_y) +
+                                          " harmonic components do not fit the device's LDS"};
   TPArgs a = make_args(plan, t, r.rows, vec);
   a.w_stride = r.w_stride;
   a.x = r.x;

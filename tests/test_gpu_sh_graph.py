@@ -66,6 +66,34 @@ def test_csr_from_coo_bit_exact(N, E, seed):
     assert np.array_equal(eid.cpu().numpy(), r_eid)
 
 
+@pytest.mark.parametrize("N,E,big,seed", [(60, 300000, 200000, 4), (9, 70000, 69000, 5), (3000, 12345, 700, 6)])
+def test_csr_with_one_large_segment(N, E, big, seed):
+    """A padding-like receiver with most of the edges and a source with many
+    outgoing edges: segments far longer than one sorting run (merge passes)."""
+    rng = np.random.default_rng(seed)
+    src = rng.integers(0, N, E)
+    dst = rng.integers(0, N, E)
+    dst[rng.choice(E, big, replace=False)] = N // 3
+    src[rng.choice(E, big // 2, replace=False)] = N - 1
+    row_ptr, s, perm = cgtp.csr_from_coo(N, to_dev_i32(src), to_dev_i32(dst))
+    r_row, r_s, r_perm = ograph.csr_from_coo(N, src, dst)
+    assert np.array_equal(row_ptr.cpu().numpy(), r_row)
+    assert np.array_equal(s.cpu().numpy(), r_s)
+    assert np.array_equal(perm.cpu().numpy(), r_perm)
+    for pad in (None, N // 3):
+        g = cgtp.Graph(N, row_ptr, s, pad_node=pad)
+        col_ptr, eid = g.transpose()
+        keep = np.ones(E, bool)
+        if pad is not None:
+            keep[r_row[pad]:r_row[pad + 1]] = False
+        # reference transpose of the kept edges (CSR positions grouped by source, ascending)
+        pos = np.nonzero(keep)[0]
+        order = np.lexsort((pos, r_s[pos]))
+        r_col = np.concatenate([[0], np.cumsum(np.bincount(r_s[pos], minlength=N))])
+        assert np.array_equal(col_ptr.cpu().numpy(), r_col)
+        assert np.array_equal(eid.cpu().numpy(), pos[order])
+
+
 def test_radius_graph_csr_bit_exact():
     c = synth.CONFIGS["conv_water1k"]
     pos = synth.positions_for(c, 0)

@@ -152,3 +152,21 @@ def test_tp_large_full_size_sampled():
     assert_close(host(dw[ri]), rdw, w_blocks(L), "f32", "full-size grad_w")
     del x, y, w, g, dx, dy, dw
     torch.cuda.empty_cache()
+
+
+def test_many_repeated_y_blocks_lds_limit():
+    """130 harmonic components (y blocks repeated): the backward's per-lane grad_y
+    columns take 130 KB of LDS in fp32, so the vectorised kernels (plus grad_x
+    rows) would exceed the device limit and the one-channel kernel runs; in fp64
+    the columns alone exceed it and the call is refused, not launched."""
+    props = torch.cuda.get_device_properties(0)
+    print("LDS per workgroup reported by the device:", getattr(props, "shared_memory_per_block", "n/a"), flush=True)
+    ix, iy, io = "8x0e+8x4e", "+".join(["0e+1o+2e+3o+4e"] * 5 + ["0e"] * 5), "0e+4e"
+    run_case(ix, iy, io, 300, "f32", shared=False)
+    L = Layout(ix, iy, io)
+    assert L.dim_y == 130
+    plan = cgtp.Plan(ix, iy, io, dtype="f64")
+    (x, y, w, g), _ = host_inputs(L, 64, 1, False, "f64")
+    with pytest.raises(cgtp.CgtpError) as e:
+        plan.tp_backward(x, y, w, g)
+    assert e.value.status == 3
