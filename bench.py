@@ -447,7 +447,13 @@ def padding_bench(args, torch, cgtp, synth, name="conv_water1k"):
     dst = np.concatenate([dst, np.full(npad, pad)]).astype(np.int32)
     vec = np.concatenate([vec, rng.standard_normal((npad, 3)) + 1.0])
     N, E = N0 + 1, src.shape[0]
-    row_ptr, s, perm = cgtp.csr_from_coo(N, torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda())
+    d_src, d_dst = torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda()
+    cgtp.csr_from_coo(N, d_src, d_dst)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    row_ptr, s, perm = cgtp.csr_from_coo(N, d_src, d_dst)
+    torch.cuda.synchronize()
+    t_csr = time.perf_counter() - t0
     v = torch.from_numpy(vec).cuda()[perm.long()].float().contiguous()
     Y = cgtp.sh_forward(c["L"], v)
     gen = torch.Generator(device="cuda")
@@ -456,7 +462,8 @@ def padding_bench(args, torch, cgtp, synth, name="conv_water1k"):
     x = torch.randn((N, p.dim_x), generator=gen, device="cuda")
     g = torch.randn((N, p.dim_out), generator=gen, device="cuda")
     sc = 1.0 / math.sqrt(E0 / N0)
-    res = dict(workload=name, E=E, padding_edges=npad, padding_fraction=round(npad / E, 3))
+    res = dict(workload=name, E=E, padding_edges=npad, padding_fraction=round(npad / E, 3),
+               csr_from_coo_s=round(t_csr, 4))
     for key, pn in (("skipped", pad), ("not_skipped", None)):
         t0 = time.perf_counter()
         graph = cgtp.Graph(N, row_ptr, s, pad_node=pn)
@@ -582,31 +589,187 @@ def linear_bench(args, torch, cgtp, synth, dtype):
     return res
 
 
-def cpu_baseline(args, synth):
-    """The oracle as it stands, tp_large fwd+bwd on a bounded row sample."""
+def tp_small_bench(args, torch, cgtp, synth):
+    """tp_small (4096 rows of 32x(0e+1o+2e), SH L = 2, 15 paths, shared weights,
+    fp32): forward and backward call times. Its 31.6 MB working set fits the
+    256 MB Infinity Cache, so it is timed twice: back to back (cache-resident)
+    and with a 1 GiB buffer written between calls (caches flushed, every input
+    from HBM)."""
+    c = synth.CONFIGS["tp_small"]
+    p = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"], wkind="shared")
+    B = c["B"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    x = torch.randn((B, p.dim_x), generator=gen, device="cuda")
+    v = torch.randn((B, 3), generator=gen, device="cuda")
+    y = cgtp.sh_forward(2, v / v.norm(dim=1, keepdim=True))
+    w = torch.randn((p.w_numel,), generator=gen, device="cuda")
+    g = torch.randn((B, p.dim_out), generator=gen, device="cuda")
+    out = torch.empty((B, p.dim_out), device="cuda")
+    dx, dy, dw = torch.empty_like(x), torch.empty_like(y), torch.empty_like(w)
+    ws = torch.empty(p.workspace_size(cgtp.OP_TP_BACKWARD, B), dtype=torch.uint8, device="cuda")
+    flush = torch.empty(1 << 28, device="cuda")  # 1 GiB
+    fwd = lambda: p.tp_forward(x, y, w, out=out)
+    bwd = lambda: p.tp_backward(x, y, w, g, out=(dx, dy, dw), ws=ws)
+    res = {"rows": B, "paths": p.num_paths, "weights": "shared"}
+    es = 4
+    bytes_fwd = es * (B * (p.dim_x + p.dim_y + p.dim_out) + p.w_numel)
+    bytes_bwd = es * (B * (2 * p.dim_x + 2 * p.dim_y + p.dim_out) + 2 * p.w_numel)
+    for key, flushed in (("resident", False), ("flushed", True)):
+        tf, tb = KernelTimer(torch), KernelTimer(torch)
+        fwd()
+        bwd()
+        for _ in range(20):
+            if flushed:
+                flush.fill_(1.0)
+            tf(fwd)
+            if flushed:
+                flush.fill_(2.0)
+            tb(bwd)
+        torch.cuda.synchronize()
+        f, b = tf.mean_ms(), tb.mean_ms()
+        res[key] = dict(fwd_ms=round(f, 4), bwd_ms=round(b, 4), fwd_pairs_per_s=B / (f * 1e-3),
+                        fwd_bwd_pairs_per_s=B / ((f + b) * 1e-3),
+                        fwd_algorithmic_GBs=round(bytes_fwd / (f * 1e-3) / 1e9, 1),
+                        bwd_algorithmic_GBs=round(bytes_bwd / (b * 1e-3) / 1e9, 1))
+    res["bytes_fwd"], res["bytes_bwd"] = bytes_fwd, bytes_bwd
+    del flush, x, y, w, g, out, dx, dy, dw, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def hbm_ceiling(torch):
+    """Plain streaming rates of this device, HIP events around torch's own
+    kernels: a 4 GiB elementwise copy (4 GiB read + 4 GiB written), a 4 GiB
+    fill (write only) and row sums of a [2^20, 1024] view (4 GiB read, 4 MiB
+    written), best of 5."""
+    n = 1 << 30
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    res = {}
+    for key, fn, nbytes in (("copy", lambda: torch.mul(a, 1.0, out=b), 8 * n),
+                            ("write", lambda: b.fill_(3.0), 4 * n),
+                            ("read", lambda: a.view(1 << 20, 1024).sum(dim=1), 4 * n + 4 * (1 << 20))):
+        fn()
+        best = None
+        for _ in range(5):
+            t = KernelTimer(torch)
+            t(fn)
+            torch.cuda.synchronize()
+            ms = t.mean_ms()
+            best = ms if best is None else min(best, ms)
+        res[key] = dict(ms=round(best, 3), GBs=round(nbytes / (best * 1e-3) / 1e9, 1),
+                        frac_of_8TBs=round(nbytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, 3))
+    del a, b
+    torch.cuda.empty_cache()
+    return res
+
+
+def _host_cores():
+    """Worker count for the host-side oracle (the GPU machine's CPU share is 16
+    cores whatever the OS reports) and the CPU model."""
+    n = min(16, os.cpu_count() or 1)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
+def _oracle_tp_chunk(job):
+    """Worker: the oracle's tensor-product forward + backward on one chunk of
+    rows of the tp_large shapes, its inputs drawn from the chunk's own seed."""
+    seed, rows = job
+    from clebsch_gordan_tensor_amd import synth
     from oracle import sh as osh
     from oracle import tp as otp
     from oracle.irreps import Layout
     c = synth.CONFIGS["tp_large"]
     L = Layout(c["irreps_x"], c["irreps_y"], c["irreps_out"])
+    x = synth.gaussian((rows, L.dim_x), seed, synth.S_X)
+    y = osh.real_sh(3, synth.unit_vectors(rows, seed))
+    w = synth.gaussian((rows, L.w_numel), seed, synth.S_W)
+    g = synth.gaussian((rows, L.dim_out), seed, synth.S_G)
+    t0 = time.perf_counter()
+    otp.forward(L, x, y, w)
+    otp.backward(L, x, y, w, g)
+    return time.perf_counter() - t0
 
-    def run(rows):
-        x = synth.gaussian((rows, L.dim_x), 1, synth.S_X)
-        y = osh.real_sh(3, synth.unit_vectors(rows, 1))
-        w = synth.gaussian((rows, L.w_numel), 1, synth.S_W)
-        g = synth.gaussian((rows, L.dim_out), 1, synth.S_G)
-        t0 = time.perf_counter()
-        otp.forward(L, x, y, w)
-        otp.backward(L, x, y, w, g)
-        return time.perf_counter() - t0
 
+def _oracle_conv_chunk(job):
+    """Worker: the oracle's convolution forward + backward on the CSR segments of
+    receivers [n0, n1) of the water1k graph (their edges and cotangents)."""
+    n0, n1 = job
+    import numpy as np
+    from clebsch_gordan_tensor_amd import synth
+    from oracle import conv as oconv
+    from oracle import graph as ograph
+    from oracle import sh as osh
+    from oracle.irreps import Layout
+    c = synth.CONFIGS["conv_water1k"]
+    L = Layout(c["irreps_x"], c["irreps_y"], c["irreps_out"])
+    pos = synth.positions_for(c, 0)
+    src, dst, vec = synth.radius_graph(pos, c["box"], c["r_cut"])
+    N = pos.shape[0]
+    row, s, perm = ograph.csr_from_coo(N, src, dst)
+    e0, e1 = row[n0], row[n1]
+    sub_row = row[n0:n1 + 1] - e0
+    x = synth.gaussian((N, L.dim_x), 0, synth.S_X)
+    v = vec[perm][e0:e1]
+    Y = osh.real_sh(c["L"], v)
+    W1, W2 = synth.mlp_params(8, 64, L.w_numel, 0)
+    w = synth.radial_weights_np(np.linalg.norm(v, axis=1), c["r_cut"], W1, W2)
+    g = synth.gaussian((N, L.dim_out), 0, synth.S_G)[n0:n1]
+    scale = oconv.avg_neighbors_scale(N, len(src))
+    t0 = time.perf_counter()
+    oconv.forward(L, sub_row, s[e0:e1], x, Y, w, scale)
+    oconv.backward(L, sub_row, s[e0:e1], x, Y, w, scale, g)
+    return time.perf_counter() - t0, int(e1 - e0)
+
+
+def cpu_baseline(args, synth):
+    """The oracle as it stands (fp64 NumPy, not tuned), on the host cores: a
+    process pool over row chunks of a bounded tp_large sample, forward +
+    backward; rate = rows / wall time of the pool."""
+    import concurrent.futures as cf
+    cores, model = _host_cores()
     probe = 64
-    dt = run(probe)
-    rows = int(min(65536, max(probe, probe * args.cpu_seconds / max(dt, 1e-3))))
-    dt = run(rows)
-    return {"value": rows / dt, "unit": "pairs/s", "cores": 1, "kind": "oracle",
-            "sample": "tp_large fwd+bwd (harmonics excluded) on %d rows, fp64 NumPy, single thread, %.1f s"
-                      % (rows, dt)}
+    dt = _oracle_tp_chunk((1, probe))
+    per = int(min(16384, max(probe, probe * args.cpu_seconds / max(dt, 1e-3))))
+    with cf.ProcessPoolExecutor(max_workers=cores) as ex:
+        list(ex.map(_oracle_tp_chunk, [(1, 8)] * cores))  # import and warm every worker
+        t0 = time.perf_counter()
+        times = list(ex.map(_oracle_tp_chunk, [(1 + k, per) for k in range(cores)]))
+        wall = time.perf_counter() - t0
+    rows = per * cores
+    return {"value": rows / wall, "unit": "pairs/s", "cores": cores, "kind": "oracle",
+            "sample": "tp_large fwd+bwd (harmonics excluded) on %d rows, fp64 NumPy, %d worker processes of "
+                      "%d rows each, %.1f s wall (of which the slowest worker's oracle arithmetic %.1f s, its input "
+                      "draws the rest); CPU %s" % (rows, cores, per, wall, max(times), model)}
+
+
+def cpu_baseline_conv(args, synth):
+    """The oracle's convolution forward + backward on the water1k graph, on
+    the host cores (a process pool over receiver ranges), in edges/s."""
+    import concurrent.futures as cf
+    cores, model = _host_cores()
+    nodes = 480  # receivers in the sample (about 25,000 edges)
+    per = (nodes + cores - 1) // cores
+    jobs = [(n, min(n + per, nodes)) for n in range(0, nodes, per)]
+    with cf.ProcessPoolExecutor(max_workers=cores) as ex:
+        list(ex.map(_oracle_conv_chunk, [(0, 1)] * cores))
+        t0 = time.perf_counter()
+        res = list(ex.map(_oracle_conv_chunk, jobs))
+        wall = time.perf_counter() - t0
+    edges = sum(e for _, e in res)
+    return {"value": edges / wall, "unit": "edges/s", "cores": cores, "kind": "oracle",
+            "sample": "conv_water1k fwd+bwd on the %d edges into receivers 0-%d, fp64 NumPy, %d worker "
+                      "processes over receiver ranges, %.1f s wall; CPU %s" % (edges, nodes - 1, cores, wall, model)}
 
 
 def main():
@@ -628,6 +791,8 @@ def main():
     extra = {"device": torch.cuda.get_device_name(0)}
     value, ms_step, roofline, plan = tp_large_bench(args, torch, cgtp, synth, extra)
     if not args.no_extra:
+        extra["hbm_ceiling"] = hbm_ceiling(torch)
+        extra["tp_small"] = tp_small_bench(args, torch, cgtp, synth)
         extra["tp_large_bf16"] = tp_large_bf16(args, torch, cgtp, synth)
         extra["tp_large_collapsed"] = tp_variants_bench(args, torch, cgtp, synth)
         extra["linear_large"] = linear_bench(args, torch, cgtp, synth, "f32")
@@ -640,6 +805,8 @@ def main():
         extra["conv_water8k_double_backward"] = double_backward_bench(args, torch, cgtp, synth)
         extra["conv_water1k_padded"] = padding_bench(args, torch, cgtp, synth)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, synth)
+    if not args.no_cpu_baseline and not args.no_extra:
+        extra["cpu_baseline_conv"] = cpu_baseline_conv(args, synth)
     line = {
         "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
