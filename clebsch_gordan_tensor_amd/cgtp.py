@@ -44,6 +44,7 @@ _SIGS = {
     "cgtp_tp_forward": ([_vp, _c_i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "cgtp_tp_backward": ([_vp, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
                          ctypes.c_int),
+    "cgtp_tp_backward_noalloc": ([_vp, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "cgtp_csr_from_coo": ([_c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "cgtp_graph_create": ([_c_i64, _c_i64, _vp, _vp, _vp, ctypes.POINTER(_vp)], ctypes.c_int),
     "cgtp_graph_destroy": ([_vp], ctypes.c_int),
@@ -237,6 +238,29 @@ class Plan:
                                      _ptr(res[0]), _ptr(res[1]), _ptr(res[2]),
                                      _ptr(ws) if nws else _vp(0), _ws_bytes(ws) if nws else 0, _stream(x)),
                "cgtp_tp_backward")
+        return tuple(res)
+
+    def tp_backward_noalloc(self, x, y, w, grad_out, need=(True, True, True), out=(None, None, None)):
+        """cgtp_tp_backward_noalloc: the backward with shared-weight partials in the
+        library's device scratch (no workspace; outputs may be passed in)."""
+        torch = _torch()
+        B = x.shape[0]
+        dt = self.torch_dtype
+        _need(x, (B, self.dim_x), dt, "x")
+        _need(y, (B, self.dim_y), dt, "y")
+        _need(w, self._w_shape(B), dt, "w")
+        _need(grad_out, (B, self.dim_out), dt, "grad_out")
+        shapes = [(B, self.dim_x), (B, self.dim_y), self._w_shape(B)]
+        res = []
+        for k in range(3):
+            if not need[k]:
+                res.append(None)
+                continue
+            t = out[k] if out[k] is not None else torch.empty(shapes[k], dtype=dt, device=x.device)
+            res.append(_need(t, shapes[k], dt, "grad"))
+        _check(_lib.cgtp_tp_backward_noalloc(self._h, B, _ptr(x), _ptr(y), _ptr(w), _ptr(grad_out),
+                                             _ptr(res[0]), _ptr(res[1]), _ptr(res[2]), _stream(x)),
+               "cgtp_tp_backward_noalloc")
         return tuple(res)
 
     # -------------------------------------------------------------- convolution

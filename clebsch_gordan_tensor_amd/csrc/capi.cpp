@@ -170,6 +170,23 @@ cgtp_status cgtp_tp_backward(cgtp_plan plan, int64_t B, const void* x, const voi
   });
 }
 
+cgtp_status cgtp_tp_backward_noalloc(cgtp_plan plan, int64_t B, const void* x, const void* y, const void* w,
+                                     const void* grad_out, void* grad_x, void* grad_y, void* grad_w,
+                                     void* stream) {
+  return guarded([&] {
+    need(plan != nullptr, "plan is NULL");
+    need(B >= 0, "B < 0");
+    if (B == 0) {
+      if (grad_w && plan->wkind == CGTP_W_SHARED)
+        zero_rows(grad_w, plan->w_numel, dtype_size(plan->dtype), as_stream(stream));
+      return;
+    }
+    need(x && y && w && grad_out, "NULL input tensor with B > 0");
+    if (!grad_x && !grad_y && !grad_w) return;
+    tp_backward_noalloc_launch(plan, B, x, y, w, grad_out, grad_x, grad_y, grad_w, as_stream(stream));
+  });
+}
+
 cgtp_status cgtp_tp_double_backward(cgtp_plan plan, int64_t B, const void* x, const void* y, const void* w,
                                     const void* grad_out, const void* gg_x, const void* gg_y, const void* gg_w,
                                     void* out_x, void* out_y, void* out_w, void* out_grad_out, void* ws,

@@ -130,6 +130,11 @@ void tp_backward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void*
                         const void* w, const void* g, void* dx, void* dy, void* dw, void* ws,
                         size_t ws_bytes, hipStream_t stream);
 size_t tp_backward_ws_bytes(const cgtp_plan_s* plan, int64_t B);
+// The same backward with the shared-weight partials in the library's
+// file-scope device scratch (CGTP_NOALLOC_SCRATCH_BYTES per device).
+constexpr size_t kNoallocScratchBytes = CGTP_NOALLOC_SCRATCH_BYTES;
+void tp_backward_noalloc_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* y, const void* w,
+                                const void* g, void* dx, void* dy, void* dw, hipStream_t stream);
 // Double backward (double_backward.hip).
 size_t tp_double_backward_ws_bytes(const cgtp_plan_s* plan, int64_t B);
 void tp_double_backward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* y, const void* w,

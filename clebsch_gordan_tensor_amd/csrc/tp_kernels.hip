@@ -1,4 +1,8 @@
 // Launchers of the row-parallel tensor product (kernels in tp_impl.hpp).
+#include <algorithm>
+#include <map>
+#include <mutex>
+
 #include "tp_impl.hpp"
 
 namespace cgtp {
@@ -324,6 +328,109 @@ void tp_backward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void*
     }
     CGTP_CHECK_HIP(hipGetLastError());
   }
+}
+
+
+// ---------------------------------------------- backward without allocation
+// For callers that cannot allocate (work under HIP graph capture, serving
+// loops, harnesses that forbid hipMalloc): the shared-weight backward with its
+// per-row grad_w partials and per-chunk sums in a file-scope device array
+// instead of a caller workspace. Rows run in passes of a multiple of
+// kRowsPerChunk rows, so the chunks and their order are those of
+// tp_backward_launch and the results are bitwise the same. Every call on one
+// device uses that device's one copy of the array: calls that overlap on a
+// device race (the caller serialises them, e.g. on one stream).
+namespace {
+
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_addr;  // device id -> that device's copy of scratch
+
+// Device address of scratch on the current device, looked up once per device
+// (in host code the array's name is a host-side stand-in, not the address).
+char* scratch_address() {
+  int dev = 0;
+  CGTP_CHECK_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_addr.find(dev);
+  if (it != g_scratch_addr.end()) return static_cast<char*>(it->second);
+  void* p = nullptr;
+  CGTP_CHECK_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+  g_scratch_addr[dev] = p;
+  return static_cast<char*>(p);
+}
+
+template <typename T>
+void colsum_rows_into(const void* in, void* part, int64_t rows, int W, hipStream_t s) {
+  using A = typename AccOf<T>::type;
+  const int nchunks = int((rows + kRowsPerChunk - 1) / kRowsPerChunk);
+  const unsigned gx = unsigned((W + kBlock - 1) / kBlock);
+  hipLaunchKernelGGL((colsum_stage1<A>), dim3(gx, unsigned(nchunks)), dim3(kBlock), 0, s,
+                     static_cast<const A*>(in), static_cast<A*>(part), rows, W);
+}
+
+template <typename T>
+void colsum_chunks(const void* part, void* out, int64_t nchunks, int W, hipStream_t s) {
+  using A = typename AccOf<T>::type;
+  const unsigned gx = unsigned((W + kBlock - 1) / kBlock);
+  hipLaunchKernelGGL((colsum_stage2<T, A>), dim3(gx), dim3(kBlock), 0, s, static_cast<const A*>(part),
+                     static_cast<T*>(out), int(nchunks), W);
+}
+
+}  // namespace
+
+void tp_backward_noalloc_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* y, const void* w,
+                                const void* g, void* dx, void* dy, void* dw, hipStream_t stream) {
+  if (plan->wkind != CGTP_W_SHARED || !dw) {  // no partials needed
+    tp_backward_launch(plan, B, x, y, w, g, dx, dy, dw, nullptr, 0, stream);
+    return;
+  }
+  const size_t es = dtype_size(plan->dtype);
+  const size_t wb = size_t(plan->w_numel) * acc_size(plan->dtype);  // one row of partials
+  const int64_t nchunks = (B + kRowsPerChunk - 1) / kRowsPerChunk;
+  const size_t part_bytes = (size_t(nchunks) * wb + 255) / 256 * 256;
+  const int64_t rows_fit = part_bytes < kNoallocScratchBytes ? int64_t((kNoallocScratchBytes - part_bytes) / wb) : 0;
+  const int64_t pass = B <= rows_fit ? B : rows_fit / kRowsPerChunk * kRowsPerChunk;
+  if (pass == 0)
+    throw Error{CGTP_ERR_WORKSPACE,
+                "tp_backward_noalloc: " + std::to_string(B) + " rows of " + std::to_string(plan->w_numel) +
+                    " shared weights need " + std::to_string(part_bytes + size_t(std::min<int64_t>(B, kRowsPerChunk)) * wb) +
+                    " bytes of scratch; the library's scratch holds " + std::to_string(kNoallocScratchBytes)};
+  char* base = scratch_address();
+  char* part = base;               // [nchunks][W] chunk sums
+  char* rows_ws = base + part_bytes;  // [pass][W] per-row partials
+  for (int64_t r0 = 0; r0 < B; r0 += pass) {
+    const int64_t n = std::min(pass, B - r0);
+    auto at = [&](const void* p, int64_t per) -> const void* {
+      return p ? static_cast<const char*>(p) + size_t(r0) * size_t(per) * es : nullptr;
+    };
+    TPBackwardRows r;
+    r.rows = n;
+    r.x = at(x, plan->dim_x);
+    r.y = at(y, plan->dim_y);
+    r.w = w;
+    r.w_stride = 0;
+    r.g = at(g, plan->dim_out);
+    r.dx = const_cast<void*>(at(dx, plan->dim_x));
+    r.dy = const_cast<void*>(at(dy, plan->dim_y));
+    r.dw_ws = rows_ws;
+    tp_backward_rows(plan, r, stream);
+    char* pdst = part + size_t(r0 / kRowsPerChunk) * wb;
+    switch (plan->dtype) {
+      case CGTP_F32: colsum_rows_into<float>(rows_ws, pdst, n, int(plan->w_numel), stream); break;
+      case CGTP_BF16: colsum_rows_into<bf16>(rows_ws, pdst, n, int(plan->w_numel), stream); break;
+      case CGTP_F64: colsum_rows_into<double>(rows_ws, pdst, n, int(plan->w_numel), stream); break;
+    }
+    CGTP_CHECK_HIP(hipGetLastError());
+  }
+  zero_unread_x(plan, dx, B, es, stream);
+  switch (plan->dtype) {
+    case CGTP_F32: colsum_chunks<float>(part, dw, nchunks, int(plan->w_numel), stream); break;
+    case CGTP_BF16: colsum_chunks<bf16>(part, dw, nchunks, int(plan->w_numel), stream); break;
+    case CGTP_F64: colsum_chunks<double>(part, dw, nchunks, int(plan->w_numel), stream); break;
+  }
+  CGTP_CHECK_HIP(hipGetLastError());
 }
 
 }  // namespace cgtp

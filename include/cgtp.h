@@ -175,6 +175,26 @@ cgtp_status cgtp_tp_backward(cgtp_plan plan, int64_t B, const void* x, const voi
                              const void* grad_out, void* grad_x, void* grad_y, void* grad_w,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of the device scratch array behind cgtp_tp_backward_noalloc (one
+ * copy per device, held until the process ends). */
+#define CGTP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* cgtp_tp_backward without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * shared-weight grad_w partials live in a file-scope device array of
+ * CGTP_NOALLOC_SCRATCH_BYTES bytes on each device (its address is looked up
+ * on the first call on a device); rows run in passes of whole 256-row chunks,
+ * so the summation order and the results are bitwise those of
+ * cgtp_tp_backward. Every call on one device shares that array: calls that
+ * overlap on a device (different streams, threads) race, so callers serialise
+ * them. PER_ROW plans need no scratch. Errors: WORKSPACE when
+ * ceil(B / 256) + min(B, 256) rows of W partials (accumulation type) exceed
+ * the array; otherwise as cgtp_tp_backward. */
+cgtp_status cgtp_tp_backward_noalloc(cgtp_plan plan, int64_t B, const void* x, const void* y, const void* w,
+                                     const void* grad_out, void* grad_x, void* grad_y, void* grad_w,
+                                     void* stream);
+
 /* Double backward: the reverse mode of cgtp_tp_backward (needed to train on
  * quantities that are themselves gradients, such as forces). For cotangents
  * (gg_x, gg_y, gg_w) of (grad_x, grad_y, grad_w) it writes the cotangents of
