@@ -26,6 +26,8 @@ Modules:
   tp      - uvu tensor product forward/backward (sparse + dense)[COURSE 03b; E3J E.1]
   graph   - CSR by destination, transpose, brute-force radius graph [V2106; COURSE 05a]
   conv    - TFN convolution forward/backward                    [COURSE 06a; E3J E.2.2, E.3]
+  linear  - equivariant linear map (channel mixing)             [E3J A.3; COURSE 03b]
+  modes   - connection modes uvu (any y multiplicity) and uvw   [COURSE 03b; E3J E.1]
 
 Parity status: every function here is pinned by tests/test_oracle_*.py against
 closed forms, textbook values, invariants or brute force; none is "parity
