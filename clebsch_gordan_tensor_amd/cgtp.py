@@ -138,12 +138,16 @@ _SEL = {"all": 0, "symmetric": 1, "skew": 2}
 
 
 class Plan:
-    """A uvu tensor-product plan (cgtp_plan_create, or cgtp_plan_create_ex for a
-    path selection "symmetric" / "skew" or collapsed outputs)."""
+    """A tensor-product plan in the "uvu" (channel-wise) or "uvw" (fully
+    connected) mode (cgtp_plan_create, or cgtp_plan_create_ex for a path
+    selection "symmetric" / "skew" or collapsed outputs)."""
 
     def __init__(self, irreps_x, irreps_y, irreps_out, mode="uvu", dtype="f32", wkind="per_row",
                  select="all", collapse=False):
         self.irreps_x, self.irreps_y, self.irreps_out = irreps_x, irreps_y, irreps_out
+        self.mode = mode
+        self._ymul = max([int(t.split("x")[0]) if "x" in t else 1 for t in irreps_y.replace(" ", "").split("+") if t]
+                         or [1])
         self.dtype_code = _DT[dtype]
         self.wkind = _WK[wkind]
         self.select, self.collapse = select, bool(collapse)
@@ -231,7 +235,8 @@ class Plan:
                 continue
             t = out[k] if out[k] is not None else torch.empty(shapes[k], dtype=dt, device=x.device)
             res.append(_need(t, shapes[k], dt, "grad"))
-        nws = self.workspace_size(OP_TP_BACKWARD, B) if need[2] else 0
+        # uvw plans and y multiplicities > 1 use the workspace for every gradient
+        nws = self.workspace_size(OP_TP_BACKWARD, B) if (need[2] or self.mode != "uvu" or self._ymul > 1) else 0
         if nws and ws is None:
             ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
         _check(_lib.cgtp_tp_backward(self._h, B, _ptr(x), _ptr(y), _ptr(w), _ptr(grad_out),

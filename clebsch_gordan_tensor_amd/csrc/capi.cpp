@@ -44,6 +44,13 @@ inline void need(bool ok, const char* what) {
 
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// uvw plans and uvu plans with y multiplicity > 1 run the tensor product's
+// forward and backward only (their own kernels).
+inline void need_plain_uvu(const cgtp_plan_s* plan, const char* what) {
+  if (plan->mode != 0 || plan->max_ymul > 1)
+    throw Error{CGTP_ERR_UNSUPPORTED, std::string(what) + ": only for uvu plans with y multiplicity 1"};
+}
+
 }  // namespace cgtp
 
 using namespace cgtp;
@@ -101,11 +108,7 @@ cgtp_status cgtp_plan_outputs(cgtp_plan plan, int64_t* num_outputs, int32_t* hos
 }
 
 cgtp_status cgtp_plan_destroy(cgtp_plan plan) {
-  return guarded([&] {
-    if (!plan) return;
-    free_plan_tables(plan);
-    delete plan;
-  });
+  return guarded([&] { destroy_plan(plan); });
 }
 
 cgtp_status cgtp_plan_query(cgtp_plan plan, int64_t* dim_x, int64_t* dim_y, int64_t* dim_out,
@@ -147,7 +150,12 @@ cgtp_status cgtp_tp_forward(cgtp_plan plan, int64_t B, const void* x, const void
     need(B >= 0, "B < 0");
     if (B == 0) return;
     need(x && y && w && out, "NULL tensor with B > 0");
-    tp_forward_launch(plan, B, x, y, w, out, as_stream(stream));
+    if (plan->mode == 1)
+      uvw_forward_launch(plan, B, x, y, w, out, as_stream(stream));
+    else if (plan->max_ymul > 1)
+      uvuv_forward_launch(plan, B, x, y, w, out, as_stream(stream));
+    else
+      tp_forward_launch(plan, B, x, y, w, out, as_stream(stream));
   });
 }
 
@@ -165,8 +173,13 @@ cgtp_status cgtp_tp_backward(cgtp_plan plan, int64_t B, const void* x, const voi
     }
     need(x && y && w && grad_out, "NULL input tensor with B > 0");
     if (!grad_x && !grad_y && !grad_w) return;
-    tp_backward_launch(plan, B, x, y, w, grad_out, grad_x, grad_y, grad_w, ws, ws_bytes,
-                       as_stream(stream));
+    if (plan->mode == 1)
+      uvw_backward_launch(plan, B, x, y, w, grad_out, grad_x, grad_y, grad_w, ws, ws_bytes, as_stream(stream));
+    else if (plan->max_ymul > 1)
+      uvuv_backward_launch(plan, B, x, y, w, grad_out, grad_x, grad_y, grad_w, ws, ws_bytes, as_stream(stream));
+    else
+      tp_backward_launch(plan, B, x, y, w, grad_out, grad_x, grad_y, grad_w, ws, ws_bytes,
+                         as_stream(stream));
   });
 }
 
@@ -183,6 +196,7 @@ cgtp_status cgtp_tp_backward_noalloc(cgtp_plan plan, int64_t B, const void* x, c
     }
     need(x && y && w && grad_out, "NULL input tensor with B > 0");
     if (!grad_x && !grad_y && !grad_w) return;
+    need_plain_uvu(plan, "tp_backward_noalloc");
     tp_backward_noalloc_launch(plan, B, x, y, w, grad_out, grad_x, grad_y, grad_w, as_stream(stream));
   });
 }
@@ -193,6 +207,7 @@ cgtp_status cgtp_tp_double_backward(cgtp_plan plan, int64_t B, const void* x, co
                                     size_t ws_bytes, void* stream) {
   return guarded([&] {
     need(plan != nullptr, "NULL plan");
+    need_plain_uvu(plan, "tp_double_backward");
     need(B >= 0, "B < 0");
     if (B == 0) {
       // shared weights still get their (zero) cotangent from an empty batch
@@ -212,6 +227,7 @@ cgtp_status cgtp_conv_double_backward(cgtp_plan plan, cgtp_graph graph, const vo
                                       void* out_grad_out, void* ws, size_t ws_bytes, void* stream) {
   return guarded([&] {
     need(plan != nullptr && graph != nullptr, "NULL plan or graph");
+    need_plain_uvu(plan, "the convolution");
     if (plan->wkind != CGTP_W_PER_ROW)
       throw Error{CGTP_ERR_UNSUPPORTED, "the convolution needs per-edge weights (CGTP_W_PER_ROW)"};
     if (graph->N == 0) return;
@@ -226,15 +242,20 @@ cgtp_status cgtp_workspace_size(cgtp_plan plan, cgtp_graph graph, int64_t B, int
     need(plan != nullptr && bytes != nullptr, "NULL argument");
     if (op == CGTP_OP_TP_BACKWARD) {
       need(B >= 0, "B < 0");
-      *bytes = tp_backward_ws_bytes(plan, B);
+      *bytes = plan->mode == 1       ? uvw_backward_ws_bytes(plan, B)
+               : plan->max_ymul > 1 ? uvuv_backward_ws_bytes(plan, B)
+                                    : tp_backward_ws_bytes(plan, B);
     } else if (op == CGTP_OP_CONV_BACKWARD) {
       need(graph != nullptr, "graph is NULL");
+      need_plain_uvu(plan, "the convolution");
       *bytes = conv_backward_ws_bytes(plan, graph);
     } else if (op == CGTP_OP_TP_DOUBLE_BACKWARD) {
       need(B >= 0, "B < 0");
+      need_plain_uvu(plan, "tp_double_backward");
       *bytes = tp_double_backward_ws_bytes(plan, B);
     } else if (op == CGTP_OP_CONV_DOUBLE_BACKWARD) {
       need(graph != nullptr, "graph is NULL");
+      need_plain_uvu(plan, "the convolution");
       *bytes = conv_double_backward_ws_bytes(plan, graph);
     } else {
       throw Error{CGTP_ERR_INVALID_ARG, "unknown op"};
@@ -297,6 +318,7 @@ cgtp_status cgtp_conv_forward(cgtp_plan plan, cgtp_graph graph, const void* x, c
                               const void* w, double scale, void* out, void* stream) {
   return guarded([&] {
     need(plan != nullptr && graph != nullptr, "NULL plan or graph");
+    need_plain_uvu(plan, "the convolution");
     if (plan->wkind != CGTP_W_PER_ROW)
       throw Error{CGTP_ERR_UNSUPPORTED, "the convolution needs per-edge weights (CGTP_W_PER_ROW)"};
     if (graph->N == 0) return;
@@ -311,6 +333,7 @@ cgtp_status cgtp_conv_backward(cgtp_plan plan, cgtp_graph graph, const void* x, 
                                void* grad_sh, void* grad_w, void* ws, size_t ws_bytes, void* stream) {
   return guarded([&] {
     need(plan != nullptr && graph != nullptr, "NULL plan or graph");
+    need_plain_uvu(plan, "the convolution");
     if (plan->wkind != CGTP_W_PER_ROW)
       throw Error{CGTP_ERR_UNSUPPORTED, "the convolution needs per-edge weights (CGTP_W_PER_ROW)"};
     need(graph->E == 0 || (x && sh && w && grad_out), "NULL input tensor");

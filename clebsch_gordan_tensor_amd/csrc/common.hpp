@@ -36,9 +36,12 @@ struct Irrep {
 
 // One path in path order. Offsets are element offsets inside a row.
 struct PathInfo {
-  int i1, i2, l1, l2, l3, p3, mul;
+  int i1, i2, l1, l2, l3, p3, mul;  // mul: x multiplicity u
   int x_off, y_off, out_off, w_off, coef_off;
   int i2_end;  // one past the last path of the run with the same (i1, i2)
+  int v;        // y multiplicity
+  int out_mul;  // output multiplicity (uvu: u; uvw: from irreps_out)
+  int w_len;    // weights of the path (uvu: u v; uvw: u v w)
 };
 
 // One x block with the contiguous range of paths that read it.
@@ -56,7 +59,7 @@ struct OutBlock {
 struct alignas(16) PathDev {
   int32_t l2, l3, y_off, out_off;
   int32_t w_off, coef_off, i2_end, mul;
-  int32_t l1, x_off, p3, pad1;
+  int32_t l1, x_off, p3, pad1;  // pad1: y multiplicity v of the path
 };
 struct alignas(16) BlockDev {
   int32_t l1, mul, x_off, path_begin;
@@ -67,13 +70,24 @@ struct DevTables {
   PathDev* paths = nullptr;
   BlockDev* blocks = nullptr;
   void* coef = nullptr;          // float (f32/bf16 plans) or double (f64 plans)
+  void* ones = nullptr;          // unit shared weights [w_numel] in the storage type (uvw sub-plans)
   int32_t* slot_paths = nullptr;  // fused convolution: path index per (block, slot), -1 = none
   int32_t* slot_off = nullptr;    // first slot of each block
 };
 
 }  // namespace cgtp
 
+struct cgtp_linear_s;
+
 struct cgtp_plan_s {
+  // connection mode: 0 = uvu (channel-wise), 1 = uvw (fully connected)
+  int mode = 0;
+  int max_ymul = 1;  // largest y multiplicity (uvu with > 1: the generic kernels)
+  // uvw: the unit-weight uvu product over the same paths (its output rows are
+  // the path outputs T) and the channel mixing T -> out as a linear map
+  cgtp_plan_s* unit = nullptr;
+  cgtp_linear_s* mix = nullptr;
+  bool with_ones = false;  // upload unit weights with the device tables
   std::vector<cgtp::Irrep> X, Y, O;
   std::vector<cgtp::PathInfo> paths;
   std::vector<cgtp::BlockInfo> blocks;
@@ -114,6 +128,8 @@ std::vector<Irrep> irreps_from_string(const char* s);
 cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const char* mode,
                         cgtp_dtype dtype, cgtp_wkind wkind, cgtp_paths select = CGTP_PATHS_ALL,
                         bool collapse = false);
+// Release a plan and what it owns (device tables, uvw sub-plan and mixing map).
+void destroy_plan(cgtp_plan_s* plan);
 // Real CG block by the ladder construction, [2l1+1][2l2+1][2l3+1], fp64.
 std::vector<double> real_cg_ladder(int l1, int l2, int l3);
 // Device tables of a plan on the current device (uploaded on first use).
@@ -140,6 +156,22 @@ size_t tp_double_backward_ws_bytes(const cgtp_plan_s* plan, int64_t B);
 void tp_double_backward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* y, const void* w,
                                const void* g, const void* gx, const void* gy, const void* gw, void* ddx,
                                void* ddy, void* ddw, void* ddg, void* ws, size_t ws_bytes, hipStream_t s);
+
+// Fully connected (uvw) product (uvw_kernels.hip): fused forward on the matrix
+// cores; backward composed through the workspace.
+void uvw_forward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* y, const void* w, void* out,
+                        hipStream_t s);
+size_t uvw_backward_ws_bytes(const cgtp_plan_s* plan, int64_t B);
+void uvw_backward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* y, const void* w, const void* g,
+                         void* dx, void* dy, void* dw, void* ws, size_t ws_bytes, hipStream_t s);
+void free_uvw_tables(const cgtp_plan_s* plan);
+// uvu with y multiplicity > 1 (uvuv_kernels.hip): generic kernels.
+void uvuv_forward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* y, const void* w, void* out,
+                         hipStream_t s);
+size_t uvuv_backward_ws_bytes(const cgtp_plan_s* plan, int64_t B);
+void uvuv_backward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* y, const void* w, const void* g,
+                          void* dx, void* dy, void* dw, void* ws, size_t ws_bytes, hipStream_t s);
+void free_uvuv_tables(const cgtp_plan_s* plan);
 
 // Backward over generic rows: row r reads x row x_idx[r] (or r), grad_out row
 // g_idx[r] (or r) times g_scale, y/w row r; writes grad_x row r either in the

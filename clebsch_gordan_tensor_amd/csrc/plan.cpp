@@ -12,12 +12,14 @@
 #include <cmath>
 #include <complex>
 #include <cstring>
+#include <map>
 #include <memory>
 #include <set>
 #include <utility>
 
 #include "cg_pattern.h"
 #include "common.hpp"
+#include "linear.hpp"
 
 namespace cgtp {
 
@@ -234,15 +236,18 @@ void pack_path(int l1, int l2, int l3, const std::vector<double>& C, std::vector
 cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const char* mode,
                         cgtp_dtype dtype, cgtp_wkind wkind, cgtp_paths select, bool collapse) {
   if (!ix || !iy || !io || !mode) throw Error{CGTP_ERR_INVALID_ARG, "null irreps or mode"};
-  if (std::strcmp(mode, "uvu") != 0)
-    throw Error{CGTP_ERR_UNSUPPORTED, std::string("mode '") + mode + "' (only uvu)"};
+  int md = -1;
+  if (std::strcmp(mode, "uvu") == 0) md = 0;
+  if (std::strcmp(mode, "uvw") == 0) md = 1;
+  if (md < 0) throw Error{CGTP_ERR_UNSUPPORTED, std::string("mode '") + mode + "' (uvu or uvw)"};
   if (dtype != CGTP_F32 && dtype != CGTP_F64 && dtype != CGTP_BF16)
     throw Error{CGTP_ERR_INVALID_ARG, "bad dtype"};
   if (wkind != CGTP_W_SHARED && wkind != CGTP_W_PER_ROW)
     throw Error{CGTP_ERR_INVALID_ARG, "bad weight kind"};
   if (select != CGTP_PATHS_ALL && select != CGTP_PATHS_SYMMETRIC && select != CGTP_PATHS_SKEW)
     throw Error{CGTP_ERR_INVALID_ARG, "bad path selection"};
-  auto plan = std::make_unique<cgtp_plan_s>();
+  auto plan = std::unique_ptr<cgtp_plan_s, void (*)(cgtp_plan_s*)>(new cgtp_plan_s, destroy_plan);
+  plan->mode = md;
   plan->select = select;
   plan->collapse = collapse;
   plan->X = parse_irreps(ix);
@@ -253,10 +258,26 @@ cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const ch
   for (auto* v : {&plan->X, &plan->Y, &plan->O})
     for (const Irrep& r : *v)
       if (r.l > kLmax) throw Error{CGTP_ERR_UNSUPPORTED, "degree " + std::to_string(r.l) + " > CGTP_LMAX"};
-  for (const Irrep& r : plan->Y)
-    if (r.mul != 1) throw Error{CGTP_ERR_UNSUPPORTED, "uvu needs multiplicity 1 on the second operand"};
+  for (const Irrep& r : plan->Y) plan->max_ymul = std::max(plan->max_ymul, r.mul);
+  if (md == 1) {
+    // the fully connected product runs on the matrix cores with y of
+    // multiplicity 1, shared weights, fp32 or bf16 storage, channel counts in
+    // multiples of 4
+    if (plan->max_ymul != 1) throw Error{CGTP_ERR_UNSUPPORTED, "uvw needs multiplicity 1 on the second operand"};
+    if (wkind != CGTP_W_SHARED) throw Error{CGTP_ERR_UNSUPPORTED, "uvw takes shared weights (CGTP_W_SHARED)"};
+    if (dtype == CGTP_F64) throw Error{CGTP_ERR_UNSUPPORTED, "uvw: fp64 is not supported (fp32, bf16)"};
+    for (const auto* v : {&plan->X, &plan->O})
+      for (const Irrep& r : *v)
+        if (r.mul % 4 != 0) throw Error{CGTP_ERR_UNSUPPORTED, "uvw: multiplicities must be multiples of 4"};
+  }
+  if (md == 0 && plan->max_ymul > 1 && collapse)
+    throw Error{CGTP_ERR_UNSUPPORTED, "uvu with y multiplicity > 1: collapsed outputs are not supported"};
   std::set<std::pair<int, int>> allowed;
-  for (const Irrep& r : plan->O) allowed.insert({r.l, r.p});
+  std::map<std::pair<int, int>, int> first_mul;  // (l, p) -> multiplicity of its first irreps_out entry
+  for (const Irrep& r : plan->O) {
+    allowed.insert({r.l, r.p});
+    first_mul.insert({{r.l, r.p}, r.mul});
+  }
 
   std::vector<int> xoff, yoff;
   int64_t o = 0;
@@ -269,7 +290,7 @@ cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const ch
   o = 0;
   for (const Irrep& r : plan->Y) {
     yoff.push_back(int(o));
-    o += 2 * r.l + 1;
+    o += int64_t(r.mul) * (2 * r.l + 1);
   }
   plan->dim_y = o;
 
@@ -289,6 +310,9 @@ cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const ch
         if ((select == CGTP_PATHS_SYMMETRIC && !sym) || (select == CGTP_PATHS_SKEW && sym)) continue;
         PathInfo p{};
         p.i1 = i1; p.i2 = i2; p.l1 = a.l; p.l2 = b.l; p.l3 = l3; p.p3 = p3; p.mul = a.mul;
+        p.v = b.mul;
+        p.out_mul = md == 0 ? a.mul : first_mul.at({l3, p3});
+        p.w_len = md == 0 ? a.mul * b.mul : a.mul * b.mul * p.out_mul;
         p.x_off = xoff[i1];
         p.y_off = yoff[i2];
         p.out_off = int(out_off);
@@ -297,8 +321,8 @@ cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const ch
         std::vector<double> C = real_cg_checked(a.l, b.l, l3);
         pack_path(a.l, b.l, l3, C, coef);
         plan->cg_dense.push_back(std::move(C));
-        out_off += int64_t(a.mul) * (2 * l3 + 1);
-        w_off += a.mul;
+        out_off += int64_t(p.out_mul) * (2 * l3 + 1);
+        w_off += p.w_len;
         plan->paths.push_back(p);
       }
       for (int k = run_begin; k < int(plan->paths.size()); ++k) plan->paths[k].i2_end = int(plan->paths.size());
@@ -311,7 +335,7 @@ cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const ch
   }
   if (plan->paths.empty()) throw Error{CGTP_ERR_UNSUPPORTED, "no path connects the irreps"};
   if (!collapse) {
-    for (const PathInfo& p : plan->paths) plan->outputs.push_back(OutBlock{p.l3, p.p3, p.mul, p.out_off});
+    for (const PathInfo& p : plan->paths) plan->outputs.push_back(OutBlock{p.l3, p.p3, p.out_mul, p.out_off});
   } else {
     // one block per (l3, p3) that a path reaches, in irreps_out order (first
     // occurrence); the paths feeding it must share their multiplicity
@@ -322,10 +346,10 @@ cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const ch
       int mul = -1;
       for (const PathInfo& p : plan->paths)
         if (p.l3 == r.l && p.p3 == r.p) {
-          if (mul >= 0 && p.mul != mul)
+          if (mul >= 0 && p.out_mul != mul)
             throw Error{CGTP_ERR_UNSUPPORTED, "collapsed output " + std::to_string(r.l) + (r.p > 0 ? "e" : "o") +
                                                   " is fed by x blocks of different multiplicities"};
-          mul = p.mul;
+          mul = p.out_mul;
         }
       if (mul < 0) continue;
       for (PathInfo& p : plan->paths)
@@ -334,7 +358,7 @@ cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const ch
       out_off += int64_t(mul) * (2 * r.l + 1);
     }
   }
-  if (out_off > INT32_MAX || w_off > INT32_MAX || plan->dim_x > INT32_MAX)
+  if (out_off > INT32_MAX || w_off > INT32_MAX || plan->dim_x > INT32_MAX || plan->dim_y > INT32_MAX)
     throw Error{CGTP_ERR_UNSUPPORTED, "row too large for 32-bit offsets"};
   plan->dim_out = out_off;
   plan->w_numel = w_off;
@@ -347,9 +371,39 @@ cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const ch
   for (const Irrep& r : plan->X) ok = ok && (r.mul % vmax == 0);
   plan->vec = ok ? vmax : 1;
 
-  // Fused-convolution slot tables.
+  if (md == 1) {
+    // the path outputs T: the unit-weight uvu product over the same paths
+    plan->unit = build_plan(ix, iy, io, "uvu", dtype, CGTP_W_SHARED, select, false);
+    plan->unit->with_ones = true;
+    // channel mixing T -> out: path p's T block (u, l3, p3) into its output
+    // block with W_p [u][1][w] = [u][w] (the linear map's [mu][mv] layout)
+    auto mix = std::make_unique<cgtp_linear_s>();
+    mix->dtype = dtype;
+    for (size_t k = 0; k < plan->paths.size(); ++k) {
+      const PathInfo& p = plan->paths[k];
+      mix->I.push_back(Irrep{p.mul, p.l3, p.p3});
+      mix->in_off.push_back(plan->unit->paths[k].out_off);
+    }
+    for (const OutBlock& ob : plan->outputs) {
+      mix->O.push_back(Irrep{ob.mul, ob.l3, ob.p3});
+      mix->out_off.push_back(ob.out_off);
+    }
+    for (size_t k = 0; k < plan->paths.size(); ++k) {
+      const PathInfo& p = plan->paths[k];
+      int o = -1;
+      for (size_t j = 0; j < plan->outputs.size(); ++j)
+        if (plan->outputs[j].out_off == p.out_off) o = int(j);
+      mix->paths.push_back(cgtp_linear_s::Path{int(k), o, p.l3, p.mul, p.out_mul, int64_t(p.w_off)});
+    }
+    mix->dim_in = plan->unit->dim_out;
+    mix->dim_out = plan->dim_out;
+    mix->w_numel = plan->w_numel;
+    plan->mix = mix.release();
+  }
+
+  // Fused-convolution slot tables (uvu with y of multiplicity 1).
   int ly = 0, lo = 0;
-  bool distinct = true;
+  bool distinct = md == 0 && plan->max_ymul == 1;
   for (int i2 = 0; i2 < int(plan->Y.size()); ++i2) {
     const int l = plan->Y[i2].l;
     if (plan->yoff_by_l[l] >= 0) distinct = false;
@@ -392,6 +446,19 @@ cgtp_plan_s* build_plan(const char* ix, const char* iy, const char* io, const ch
   return plan.release();
 }
 
+void destroy_plan(cgtp_plan_s* plan) {
+  if (!plan) return;
+  free_plan_tables(plan);
+  free_uvw_tables(plan);
+  free_uvuv_tables(plan);
+  if (plan->mix) {
+    free_linear_tables(plan->mix);
+    delete plan->mix;
+  }
+  destroy_plan(plan->unit);
+  delete plan;
+}
+
 const DevTables& plan_tables(cgtp_plan_s* plan) {
   int dev = 0;
   CGTP_CHECK_HIP(hipGetDevice(&dev));
@@ -401,7 +468,7 @@ const DevTables& plan_tables(cgtp_plan_s* plan) {
   std::vector<PathDev> pd;
   for (const PathInfo& p : plan->paths)
     pd.push_back(PathDev{p.l2, p.l3, p.y_off, p.out_off, p.w_off, p.coef_off, p.i2_end, p.mul,
-                         p.l1, p.x_off, p.p3, 0});
+                         p.l1, p.x_off, p.p3, p.v});
   std::vector<BlockDev> bd;
   for (const BlockInfo& b : plan->blocks)
     bd.push_back(BlockDev{b.l1, b.mul, b.x_off, b.path_begin, b.path_end, 0, 0, 0});
@@ -425,6 +492,24 @@ const DevTables& plan_tables(cgtp_plan_s* plan) {
     CGTP_CHECK_HIP(hipMemcpy(t.blocks, bd.data(), bd.size() * sizeof(BlockDev), hipMemcpyHostToDevice));
     CGTP_CHECK_HIP(hipMemcpy(t.coef, f64 ? static_cast<const void*>(c64.data()) : static_cast<const void*>(c32.data()),
                              cbytes, hipMemcpyHostToDevice));
+    if (plan->with_ones) {
+      const size_t es = dtype_size(plan->dtype), n = size_t(plan->w_numel);
+      std::vector<unsigned char> ones(n * es);
+      for (size_t i = 0; i < n; ++i) {
+        if (es == 8) {
+          const double one = 1.0;
+          std::memcpy(&ones[i * 8], &one, 8);
+        } else if (es == 4) {
+          const float one = 1.0f;
+          std::memcpy(&ones[i * 4], &one, 4);
+        } else {
+          const uint16_t one = 0x3f80;  // bf16 1.0
+          std::memcpy(&ones[i * 2], &one, 2);
+        }
+      }
+      CGTP_CHECK_HIP(hipMalloc(&t.ones, ones.size()));
+      CGTP_CHECK_HIP(hipMemcpy(t.ones, ones.data(), ones.size(), hipMemcpyHostToDevice));
+    }
     if (plan->conv_fused) {
       CGTP_CHECK_HIP(hipMalloc(&t.slot_paths, plan->slot_paths.size() * 4 + 4));
       CGTP_CHECK_HIP(hipMalloc(&t.slot_off, plan->slot_off.size() * 4));
@@ -437,6 +522,7 @@ const DevTables& plan_tables(cgtp_plan_s* plan) {
     (void)hipFree(t.paths);
     (void)hipFree(t.blocks);
     (void)hipFree(t.coef);
+    (void)hipFree(t.ones);
     (void)hipFree(t.slot_paths);
     (void)hipFree(t.slot_off);
     throw;
@@ -452,6 +538,7 @@ void free_plan_tables(cgtp_plan_s* plan) {
       (void)hipFree(kv.second.paths);
       (void)hipFree(kv.second.blocks);
       (void)hipFree(kv.second.coef);
+      (void)hipFree(kv.second.ones);
       (void)hipFree(kv.second.slot_paths);
       (void)hipFree(kv.second.slot_off);
     }

@@ -86,9 +86,10 @@ def test_error_codes():
     assert status_of(lambda: cgtp.Plan("1x1q", "0e", "0e")) == ERR_PARSE
     assert status_of(lambda: cgtp.Plan("1e++1o", "0e", "0e")) == ERR_PARSE
     assert status_of(lambda: cgtp.Plan("0x1e", "0e", "1e")) == ERR_PARSE
-    assert status_of(lambda: cgtp.Plan("1x1o", "1o", "0e", mode="uvw")) == ERR_UNSUPPORTED
+    assert status_of(lambda: cgtp.Plan("4x1o", "1o", "4x0e", mode="uvw")) == ERR_UNSUPPORTED  # per-row uvw
+    assert status_of(lambda: cgtp.Plan("1x1o", "1o", "0e", mode="uvx")) == ERR_UNSUPPORTED
     assert status_of(lambda: cgtp.Plan("1x5o", "0e", "5o")) == ERR_UNSUPPORTED
-    assert status_of(lambda: cgtp.Plan("1x1o", "2x1o", "0e")) == ERR_UNSUPPORTED
+    assert status_of(lambda: cgtp.Plan("1x1o", "2x1o", "0e", collapse=True)) == ERR_UNSUPPORTED
     assert status_of(lambda: cgtp.Plan("1x1o", "1o", "1o")) == ERR_UNSUPPORTED  # no path survives
     p = cgtp.Plan("1x1o", "1o", "0e")
     buf = np.zeros(27)
@@ -171,3 +172,44 @@ def ctypes_plan_ex(ix, iy, io, select, collapse):
     if st == 0:
         cgtp._lib.cgtp_plan_destroy(h)
     return st
+
+
+# ------------------------------------------------------- connection modes
+
+@pytest.mark.parametrize("ix,iy,io,mode,wkind,collapse", [
+    ("4x0e+4x1o+8x2e", "0e+1o+2e", "8x0e+4x0o+12x1e+4x1o+8x2e+4x2o", "uvw", "shared", False),
+    ("4x0e+4x1o+8x2e", "0e+1o+2e", "8x0e+4x0o+12x1e+4x1o+8x2e+4x2o", "uvw", "shared", True),
+    ("128x0e+128x1o+128x2e+128x3o", "0e+1o+2e+3o", "128x0e+128x0o+128x1e+128x1o+128x2e+128x2o+128x3e+128x3o",
+     "uvw", "shared", True),
+    ("3x0e+5x1o+2x2e", "2x0e+3x1o+1x2e", "0e+0o+1e+1o+2e+2o", "uvu", "per_row", False),
+    ("3x0e+5x1o+2x2e", "2x0e+3x1o+1x2e", "0e+0o+1e+1o+2e+2o", "uvu", "shared", False),
+])
+def test_mode_plans_equal_oracle(ix, iy, io, mode, wkind, collapse):
+    from oracle.modes import ModeLayout
+    p = cgtp.Plan(ix, iy, io, mode=mode, wkind=wkind, collapse=collapse)
+    ML = ModeLayout(ix, iy, io, mode, collapse=collapse)
+    assert (p.dim_x, p.dim_y, p.dim_out, p.num_paths, p.w_numel) == (ML.dim_x, ML.dim_y, ML.dim_out, len(ML.paths),
+                                                                      ML.w_numel)
+    assert p.paths().tolist() == [[q["i1"], q["i2"], q["l1"], q["l2"], q["l3"], q["p3"]] for q in ML.paths]
+    assert p.outputs().tolist() == [[g["l3"], g["p3"], g["mul"], g["out_off"]] for g in ML.groups]
+
+
+def test_mode_errors():
+    ERR_UNSUPPORTED, ERR_WORKSPACE = 3, 5
+    full = ("4x0e+4x1o", "0e+1o", "4x0e+4x1o+4x1e")
+    assert status_of(lambda: cgtp.Plan(*full, mode="uvw", wkind="shared", dtype="f64")) == ERR_UNSUPPORTED
+    assert status_of(lambda: cgtp.Plan("4x0e", "2x0e", "4x0e", mode="uvw", wkind="shared")) == ERR_UNSUPPORTED
+    assert status_of(lambda: cgtp.Plan("3x0e", "0e", "4x0e", mode="uvw", wkind="shared")) == ERR_UNSUPPORTED
+    assert status_of(lambda: cgtp.Plan("4x0e", "0e", "3x0e", mode="uvw", wkind="shared")) == ERR_UNSUPPORTED
+    # uvw and y multiplicities > 1 run the tensor product only: the convolution,
+    # the double backward and the allocation-free backward refuse them
+    pw = cgtp.Plan(*full, mode="uvw", wkind="shared")
+    pv = cgtp.Plan("4x0e+4x1o", "2x0e+2x1o", "0e+1o+1e", wkind="per_row")
+    for p in (pw, pv):
+        assert cgtp._lib.cgtp_conv_forward(p._h, None, None, None, None, 1.0, None, None) in (1, ERR_UNSUPPORTED)
+        assert cgtp._lib.cgtp_tp_double_backward(p._h, 0, *([None] * 12), 0, None) == ERR_UNSUPPORTED
+        assert cgtp._lib.cgtp_tp_backward_noalloc(p._h, 1, *([None] * 8)) in (1, ERR_UNSUPPORTED)
+    # workspaces: uvw holds the path outputs and their cotangent (plus grad_W
+    # partials); uvu with v > 1 the per-path grad of the mixed y
+    assert pw.workspace_size(cgtp.OP_TP_BACKWARD, 1000) >= 2 * 1000 * (4 * 1 + 4 * 3 + 4 * 3 + 4 * 1 + 4 * 3) * 4
+    assert pv.workspace_size(cgtp.OP_TP_BACKWARD, 100) >= 100 * (4 * 1 + 4 * 3 + 4 * 3 + 4 * 1 + 4 * 3) * 4
