@@ -589,6 +589,120 @@ def linear_bench(args, torch, cgtp, synth, dtype):
     return res
 
 
+def uvw_bench(args, torch, cgtp, synth, dtype):
+    """Fully connected (uvw) product on the tp_large rows: 2^20 rows of
+    128x(0e+1o+2e+3o), harmonics L = 3, every output type (l <= 3, both
+    parities) at 128 channels, shared 128 x 128 weights per path. Collapsed
+    outputs (the fully connected product, 4,096 outputs per row): the fused
+    forward against the same product as two library calls (unit-weight uvu
+    forward writing the 19,968 path outputs per row, then the linear map from
+    them to the outputs), and the backward. Uncollapsed outputs (one 128-channel
+    block per path, 19,968 per row): forward. MFMA work: 2 sum_p (2 l3 + 1) u w
+    flops per row."""
+    c = synth.CONFIGS["tp_large"]
+    ix, iy = c["irreps_x"], c["irreps_y"]
+    io = "+".join("128x%d%s" % (l, p) for l in range(4) for p in "eo")
+    B = c["B"]
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    es = 4 if dtype == "f32" else 2
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    res = {"rows": B, "irreps_x": ix, "irreps_out": io, "dtype": dtype,
+           "mfma": "v_mfma_f32_16x16x4_f32 (bf16 storage widened exactly)"}
+    x = torch.randn((B, 2048), generator=gen, device="cuda").to(td)
+    v = torch.randn((B, 3), generator=gen, device="cuda")
+    y = cgtp.sh_forward(3, v / v.norm(dim=1, keepdim=True)).to(td)
+    del v
+    for collapse in (True, False):
+        p = cgtp.Plan(ix, iy, io, mode="uvw", dtype=dtype, wkind="shared", collapse=collapse)
+        flops = 2 * B * sum((2 * int(r[4]) + 1) * 128 * 128 for r in p.paths())
+        w = (torch.randn((p.w_numel,), generator=gen, device="cuda") / 16.0).to(td)
+        out = torch.empty((B, p.dim_out), device="cuda", dtype=td)
+        fwd = lambda: p.tp_forward(x, y, w, out=out)
+        tf = KernelTimer(torch)
+        fwd()
+        for _ in range(3):
+            tf(fwd)
+        torch.cuda.synchronize()
+        ms = tf.mean_ms()
+        nbytes = es * B * (p.dim_x + p.dim_y + p.dim_out) + es * p.w_numel
+        key = "collapsed" if collapse else "uncollapsed"
+        res[key] = dict(paths=p.num_paths, dim_out=p.dim_out, fwd_ms=round(ms, 3), fwd_pairs_per_s=B / (ms * 1e-3),
+                        fwd_TFLOPs=round(flops / (ms * 1e-3) / 1e12, 1),
+                        fwd_frac_of_fp32_mfma_peak=round(flops / (ms * 1e-3) / 1e12 / MFMA_FP32_PEAK_TFS, 3),
+                        fwd_algorithmic_GBs=round(nbytes / (ms * 1e-3) / 1e9, 1), flops=flops)
+        if collapse:
+            # the same product as two calls: unit-weight uvu forward, then the linear map
+            unit = cgtp.Plan(ix, iy, io, dtype=dtype, wkind="shared")
+            ones = torch.ones((unit.w_numel,), device="cuda", dtype=td)
+            t_irreps = "+".join("128x%d%s" % (int(r[4]), "e" if int(r[5]) > 0 else "o") for r in unit.paths())
+            o_irreps = "+".join("%dx%d%s" % (int(r[2]), int(r[0]), "e" if int(r[1]) > 0 else "o") for r in p.outputs())
+            lin = cgtp.Linear(t_irreps, o_irreps, dtype=dtype)
+            T = torch.empty((B, unit.dim_out), device="cuda", dtype=td)
+            out2 = torch.empty_like(out)
+            comp = lambda: (unit.tp_forward(x, y, ones, out=T), lin.forward(T, w, out=out2))
+            tc = KernelTimer(torch)
+            comp()
+            for _ in range(3):
+                tc(comp)
+            torch.cuda.synchronize()
+            res[key]["composition_fwd_ms"] = round(tc.mean_ms(), 3)
+            res[key]["composition_matches"] = bool(torch.allclose(out.float(), out2.float(), rtol=1e-2, atol=1e-2))
+            del T, out2, ones
+            torch.cuda.empty_cache()
+            g = torch.randn((B, p.dim_out), generator=gen, device="cuda").to(td)
+            dx, dy, dw = torch.empty_like(x), torch.empty_like(y), torch.empty_like(w)
+            ws = torch.empty(p.workspace_size(cgtp.OP_TP_BACKWARD, B), dtype=torch.uint8, device="cuda")
+            bwd = lambda: p.tp_backward(x, y, w, g, out=(dx, dy, dw), ws=ws)
+            tb = KernelTimer(torch)
+            bwd()
+            for _ in range(2):
+                tb(bwd)
+            torch.cuda.synchronize()
+            res[key]["bwd_ms"] = round(tb.mean_ms(), 3)
+            res[key]["bwd"] = "unit-weight uvu forward + linear backward + unit-weight uvu backward (workspace)"
+            del g, dx, dy, dw, ws
+        del out, w, p
+        torch.cuda.empty_cache()
+    del x, y
+    torch.cuda.empty_cache()
+    return res
+
+
+def uvu_ymul_bench(args, torch, cgtp, synth):
+    """uvu with y of multiplicity 4 (generic kernels): 2^18 rows of
+    32x(0e+1o+2e) with y = 4x(0e+1o+2e), per-row weights [u][v] per path."""
+    ix, iy, io = "32x0e+32x1o+32x2e", "4x0e+4x1o+4x2e", "0e+0o+1e+1o+2e+2o"
+    p = cgtp.Plan(ix, iy, io, wkind="per_row")
+    B = 1 << 18
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    x = torch.randn((B, p.dim_x), generator=gen, device="cuda")
+    y = torch.randn((B, p.dim_y), generator=gen, device="cuda")
+    w = torch.randn((B, p.w_numel), generator=gen, device="cuda")
+    g = torch.randn((B, p.dim_out), generator=gen, device="cuda")
+    out = torch.empty((B, p.dim_out), device="cuda")
+    dx, dy, dw = torch.empty_like(x), torch.empty_like(y), torch.empty_like(w)
+    ws = torch.empty(p.workspace_size(cgtp.OP_TP_BACKWARD, B), dtype=torch.uint8, device="cuda")
+    tf, tb = KernelTimer(torch), KernelTimer(torch)
+    fwd = lambda: p.tp_forward(x, y, w, out=out)
+    bwd = lambda: p.tp_backward(x, y, w, g, out=(dx, dy, dw), ws=ws)
+    fwd()
+    bwd()
+    for _ in range(3):
+        tf(fwd)
+        tb(bwd)
+    torch.cuda.synchronize()
+    f, b = tf.mean_ms(), tb.mean_ms()
+    bytes_f = 4 * B * (p.dim_x + p.dim_y + p.w_numel + p.dim_out)
+    res = dict(rows=B, irreps_x=ix, irreps_y=iy, paths=p.num_paths, w_per_row=p.w_numel, fwd_ms=round(f, 3),
+               bwd_ms=round(b, 3), fwd_algorithmic_GBs=round(bytes_f / (f * 1e-3) / 1e9, 1),
+               fwd_bwd_pairs_per_s=B / ((f + b) * 1e-3))
+    del x, y, w, g, out, dx, dy, dw, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def tp_small_bench(args, torch, cgtp, synth):
     """tp_small (4096 rows of 32x(0e+1o+2e), SH L = 2, 15 paths, shared weights,
     fp32): forward and backward call times. Its 31.6 MB working set fits the
@@ -797,6 +911,9 @@ def main():
         extra["tp_large_collapsed"] = tp_variants_bench(args, torch, cgtp, synth)
         extra["linear_large"] = linear_bench(args, torch, cgtp, synth, "f32")
         extra["linear_large_bf16"] = linear_bench(args, torch, cgtp, synth, "bf16")
+        extra["uvw_tp_large"] = uvw_bench(args, torch, cgtp, synth, "f32")
+        extra["uvw_tp_large_bf16"] = uvw_bench(args, torch, cgtp, synth, "bf16")
+        extra["uvu_ymul4"] = uvu_ymul_bench(args, torch, cgtp, synth)
     if not args.no_conv and not args.no_extra:
         for name in ("conv_water1k", "conv_water8k", "conv_uniform100k", "conv_collapsed_l3", "conv_collapsed_l4"):
             extra[name] = conv_bench(args, torch, cgtp, synth, name, max(2, min(args.steps, 5)),

@@ -12,17 +12,17 @@
 // path of one (l3, p3) into one block o (the fully connected product).
 //
 // Forward, one kernel: a workgroup owns 16 rows and walks every output block
-// and every path into it. Per path (and chunk of 128 x channels) the 256
-// lanes first form T_p for the 16 rows in LDS on the vector ALUs (lane =
-// (row, 4 channels), the coefficient sparsity pattern fixed at compile time,
-// as in the channel-wise product), then the four waves run
-// v_mfma_f32_16x16x4_f32 on D[k][z] += sum_a W_p[a][k] T_p[z, m3, a] for
-// every m3: wave w owns output channels [32w, 32w + 32) of a 128-channel
-// column tile (two 16-row A tiles, W read from L2, the next K step requested
-// before the current one's products), all 2 l3 + 1 N tiles (16 rows each).
-// D stays in the accumulators over all paths of the block; each lane then
-// stores 4 consecutive output channels of one (row, m3). bf16 storage is
-// widened exactly to fp32, so both storage types run the same fp32 products.
+// and every path into it. Per path (and chunk of 128 x channels) each lane
+// first requests its W operands for the whole chunk (from L2), then the 512
+// lanes form T_p for the 16 rows in LDS on the vector ALUs (lane = (row, 4
+// channels), the coefficient sparsity pattern fixed at compile time, as in
+// the channel-wise product), then the eight waves run the matrix cores on
+// D[k][z] += sum_a W_p[a][k] T_p[z, m3, a] for every m3: wave w owns output
+// channels [16w, 16w + 16) of a 128-channel column tile (one 16-row A tile),
+// all 2 l3 + 1 N tiles (16 rows each). D stays in the accumulators
+// over all paths of the block; each lane then stores 4 consecutive output
+// channels of one (row, m3). fp32 storage: v_mfma_f32_16x16x4_f32 on fp32 T;
+// bf16 storage: v_mfma_f32_16x16x32_bf16 on T rounded to bf16 in LDS.
 //
 // Backward, composed from the library's kernels through the workspace:
 //   T  = unit-weight uvu forward (the path outputs)
@@ -32,6 +32,7 @@
 #include <algorithm>
 #include <map>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "cg_pattern.h"
@@ -67,25 +68,54 @@ struct UvwArgs {
   int dim_x, dim_y, dim_out, ngroups;
 };
 
-constexpr int kUvwThreads = 256;
-constexpr int kUvwRows = 16;         // rows per workgroup: the MFMA's N tile
-constexpr int kUvwK = 128;           // x channels of one T chunk
-constexpr int kUvwTP = kUvwK + 4;    // padded LDS row of T (floats)
-constexpr int kUvwCols = 128;        // output channels per column tile (4 waves x 32)
+constexpr int kUvwThreads = 512;
+constexpr int kUvwRows = 16;   // rows per workgroup: the MFMA's N tile
+constexpr int kUvwK = 128;     // x channels of one T chunk
+constexpr int kUvwCols = 128;  // output channels per column tile (8 waves x 16)
 
-size_t uvw_lds_bytes(int max_l3) { return size_t(2 * max_l3 + 1) * kUvwRows * kUvwTP * sizeof(float); }
+// How T and W meet on the matrix cores. fp32 storage: T as fp32 in LDS,
+// v_mfma_f32_16x16x4_f32, lane slot lk of step j takes contraction index
+// 16 kc + 4 lk + j (8 steps of 16 per chunk). bf16 storage: T rounded to bf16
+// in LDS (as a bf16 store of the path outputs would round it) and
+// v_mfma_f32_16x16x32_bf16, lane slot lk takes 32 kc + 8 lk + j, j < 8 (4 steps
+// of 32); bf16 x bf16 products are exact in fp32 and sum in fp32.
+template <typename T>
+struct UvwMma {
+  static constexpr int KS = 16;               // contraction per step
+  static constexpr int NK = kUvwK / KS;       // steps per chunk
+  static constexpr int TP = kUvwK + 4;        // padded LDS row of T, in elements
+  using TL = float;                           // LDS element of T
+  using AW = float __attribute__((ext_vector_type(4)));  // one step's W operand of one A tile
+};
+template <>
+struct UvwMma<bf16> {
+  static constexpr int KS = 32;
+  static constexpr int NK = kUvwK / KS;
+  static constexpr int TP = kUvwK + 8;
+  using TL = uint16_t;
+  using AW = uint16_t __attribute__((ext_vector_type(8)));
+};
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+template <typename T>
+size_t uvw_lds_bytes(int max_l3) {
+  using M = UvwMma<T>;
+  return size_t(2 * max_l3 + 1) * kUvwRows * M::TP * sizeof(typename M::TL);
+}
 
 // T_p for rows z0..z0+15 and x channels k0..k0+127 into LDS [m3][row][channel]
-// (zeros past u). Lane (zt, rt) takes row zt and channel quads 4 rt, 4 rt + 64.
+// (zeros past u). Lane (zt, rt) takes row zt and the channel quad 4 rt.
 template <typename T, int L1, int L2, int L3>
 __device__ __forceinline__ void uvw_t_chunk(const UvwArgs& a, const UvwPathDev& pd, const T* __restrict__ xr,
-                                            const T* __restrict__ yr, int k0, int zt, int rt, float* tl) {
+                                            const T* __restrict__ yr, int k0, int zt, int rt,
+                                            typename UvwMma<T>::TL* tl) {
+  using M = UvwMma<T>;
   float yb[2 * L2 + 1];
 #pragma unroll
   for (int m = 0; m < 2 * L2 + 1; ++m) yb[m] = to_acc<float>(yr[pd.y_off + m]);
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int al = 4 * rt + 64 * q, ag = k0 + al;
+  {
+    const int al = 4 * rt, ag = k0 + al;
     const bool ok = ag < pd.u;  // u is a multiple of 4: a quad is wholly inside or past it
     float xb[2 * L1 + 1][4];
 #pragma unroll
@@ -94,70 +124,67 @@ __device__ __forceinline__ void uvw_t_chunk(const UvwArgs& a, const UvwPathDev& 
     fwd_core<L1, L2, L3, 4, float>(xb, yb, a.coef + pd.coef_off, o);
 #pragma unroll
     for (int m = 0; m < 2 * L3 + 1; ++m) {
-      const v4f v = ok ? v4f{o[m][0], o[m][1], o[m][2], o[m][3]} : v4f{0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<v4f*>(tl + (m * kUvwRows + zt) * kUvwTP + al) = v;
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = ok ? o[m][i] : 0.f;
+      VecIO<T, 4>::store(reinterpret_cast<T*>(tl + (m * kUvwRows + zt) * M::TP + al), v);
     }
   }
 }
 
-// W_p[a][k] for this lane's 4 contraction slots of K step kc (a = k0 + 16 kc
-// + 4 lk + j) and its two output channels; clamped in-bounds addresses, zeros
-// past u or w_out.
+// This lane's W operands of a whole chunk: W_p[a][k] for its contraction
+// slots of every step and its output channel, requested at once (before the
+// T phase, so their latency hides behind it); zeros past u or w_out.
 template <typename T>
-__device__ __forceinline__ void uvw_load_w(const T* __restrict__ W, int u, int w_out, int k0, int kc, int lk,
-                                           const int (&kout)[2], const bool (&kok)[2], float (&av)[2][4]) {
+__device__ __forceinline__ void uvw_load_w(const T* __restrict__ W, int u, int w_out, int k0, int lk, int kout,
+                                           bool kok, typename UvwMma<T>::AW (&aw)[UvwMma<T>::NK]) {
+  using M = UvwMma<T>;
+  constexpr int J = M::KS / 4;  // contraction values per lane and step
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ka = k0 + 16 * kc + 4 * lk + j;
-    const bool aok = ka < u;
+  for (int kc = 0; kc < M::NK; ++kc)
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const float v = to_acc<float>(W[int64_t(aok ? ka : 0) * w_out + (kok[s] ? kout[s] : 0)]);
-      av[s][j] = aok && kok[s] ? v : 0.f;
+    for (int j = 0; j < J; ++j) {
+      const int ka = k0 + M::KS * kc + J * lk + j;
+      const bool aok = ka < u;
+      const T v = W[int64_t(aok ? ka : 0) * w_out + (kok ? kout : 0)];
+      if constexpr (std::is_same<T, bf16>::value)
+        aw[kc][j] = aok && kok ? v.bits : uint16_t(0);
+      else
+        aw[kc][j] = aok && kok ? v : 0.f;
     }
-  }
 }
 
 template <typename T, int L3>
-__device__ __forceinline__ void uvw_mix_chunk(const UvwArgs& a, const UvwPathDev& pd, int w_out, int k0, int c0,
-                                              const float* tl, v4f (&acc)[2][2 * L3 + 1], int wave, int li, int lk) {
-  const T* __restrict__ W = static_cast<const T*>(a.w) + pd.w_off;
-  int kout[2];
-  bool kok[2];
+__device__ __forceinline__ void uvw_mix_chunk(int kn, const typename UvwMma<T>::TL* tl,
+                                              const typename UvwMma<T>::AW (&aw)[UvwMma<T>::NK],
+                                              v4f (&acc)[2 * L3 + 1], int li, int lk) {
+  using M = UvwMma<T>;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    kout[s] = c0 + 32 * wave + 16 * s + li;
-    kok[s] = kout[s] < w_out;
-  }
-  const int kn = pd.u - k0 < kUvwK ? pd.u - k0 : kUvwK;
-  const int nk = (kn + 15) / 16;
-  float av[2][4], an[2][4];
-  uvw_load_w<T>(W, pd.u, w_out, k0, 0, lk, kout, kok, av);
-  for (int kc = 0; kc < nk; ++kc) {
-    uvw_load_w<T>(W, pd.u, w_out, k0, kc + 1, lk, kout, kok, an);  // next step's operands (zeros past u)
-    __builtin_amdgcn_sched_barrier(0);
+  for (int kc = 0; kc < M::NK; ++kc) {
+    if (kc * M::KS >= kn) break;  // uniform: past the chunk's channels
 #pragma unroll
     for (int nt = 0; nt < 2 * L3 + 1; ++nt) {
-      const v4f b = *reinterpret_cast<const v4f*>(tl + (nt * kUvwRows + li) * kUvwTP + 16 * kc + 4 * lk);
+      if constexpr (std::is_same<T, bf16>::value) {
+        const bf16x8 b = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u16x8*>(tl + (nt * kUvwRows + li) * M::TP + M::KS * kc + 8 * lk));
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aw[kc]), b, acc[nt], 0, 0, 0);
+      } else {
+        const v4f b = *reinterpret_cast<const v4f*>(tl + (nt * kUvwRows + li) * M::TP + M::KS * kc + 4 * lk);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) acc[s][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s][j], b[j], acc[s][nt], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[kc][j], b[j], acc[nt], 0, 0, 0);
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) av[s][j] = an[s][j];
   }
 }
 
 template <typename T>
 __global__ __launch_bounds__(kUvwThreads) void uvw_fwd_kernel(UvwArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float tl[];  // [2 l3 + 1][16 rows][kUvwTP]
+  using M = UvwMma<T>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char uvw_smem[];
+  typename M::TL* tl = reinterpret_cast<typename M::TL*>(uvw_smem);  // [2 l3 + 1][16 rows][M::TP]
   const int tid = int(threadIdx.x), lane = tid & 63, wave = tid >> 6, li = lane & 15, lk = lane >> 4;
   const int64_t z0 = int64_t(blockIdx.x) * kUvwRows;
-  const int zt = tid >> 4, rt = tid & 15;
+  const int zt = tid >> 5, rt = tid & 31;
   // rows past B compute from the last row; their results are not stored
   const int64_t rowt = z0 + zt < a.B ? z0 + zt : a.B - 1;
   const T* __restrict__ xr = static_cast<const T*>(a.x) + rowt * a.dim_x;
@@ -170,14 +197,17 @@ __global__ __launch_bounds__(kUvwThreads) void uvw_fwd_kernel(UvwArgs a) {
       constexpr int L3 = decltype(L3c)::value;
       if (gd.l3 != L3) return;
       for (int c0 = 0; c0 < gd.w_out; c0 += kUvwCols) {
-        v4f acc[2][2 * L3 + 1];
+        const int kout = c0 + 16 * wave + li;
+        const bool kok = kout < gd.w_out;
+        v4f acc[2 * L3 + 1];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int nt = 0; nt < 2 * L3 + 1; ++nt) acc[s][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < 2 * L3 + 1; ++nt) acc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
         for (int pi = gd.p0; pi < gd.p1; ++pi) {
           const UvwPathDev pd = ldc(a.paths + pi);
+          const T* __restrict__ W = static_cast<const T*>(a.w) + pd.w_off;
           for (int k0 = 0; k0 < pd.u; k0 += kUvwK) {
+            typename M::AW aw[M::NK];
+            uvw_load_w<T>(W, pd.u, gd.w_out, k0, lk, kout, kok, aw);
             __syncthreads();  // the previous chunk's T has been read
             static_for<0, kLmax + 1>([&](auto L1c) {
               constexpr int L1 = decltype(L1c)::value;
@@ -189,21 +219,16 @@ __global__ __launch_bounds__(kUvwThreads) void uvw_fwd_kernel(UvwArgs a) {
               });
             });
             __syncthreads();
-            uvw_mix_chunk<T, L3>(a, pd, gd.w_out, k0, c0, tl, acc, wave, li, lk);
+            uvw_mix_chunk<T, L3>(pd.u - k0, tl, aw, acc, li, lk);
           }
         }
-        // lane: output channels c0 + 32 wave + 16 s + 4 lk + r of row z0 + li, component nt
-        if (row_out < a.B) {
+        // lane: output channels c0 + 16 wave + 4 lk + r of row z0 + li, component nt
+        const int kb = c0 + 16 * wave + 4 * lk;
+        if (row_out < a.B && kb < gd.w_out) {
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const int kb = c0 + 32 * wave + 16 * s + 4 * lk;
-            if (kb < gd.w_out) {
-#pragma unroll
-              for (int nt = 0; nt < 2 * L3 + 1; ++nt) {
-                const float o[4] = {acc[s][nt][0], acc[s][nt][1], acc[s][nt][2], acc[s][nt][3]};
-                VecIO<T, 4>::store(orow + gd.out_off + nt * gd.w_out + kb, o);
-              }
-            }
+          for (int nt = 0; nt < 2 * L3 + 1; ++nt) {
+            const float o[4] = {acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]};
+            VecIO<T, 4>::store(orow + gd.out_off + nt * gd.w_out + kb, o);
           }
         }
       }
@@ -296,11 +321,10 @@ void uvw_forward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void*
   a.dim_out = int(plan->dim_out);
   a.ngroups = t.ngroups;
   const dim3 grid(unsigned((B + kUvwRows - 1) / kUvwRows));
-  const size_t lds = uvw_lds_bytes(t.max_l3);
   if (plan->dtype == CGTP_BF16)
-    hipLaunchKernelGGL((uvw_fwd_kernel<bf16>), grid, dim3(kUvwThreads), lds, s, a);
+    hipLaunchKernelGGL((uvw_fwd_kernel<bf16>), grid, dim3(kUvwThreads), uvw_lds_bytes<bf16>(t.max_l3), s, a);
   else
-    hipLaunchKernelGGL((uvw_fwd_kernel<float>), grid, dim3(kUvwThreads), lds, s, a);
+    hipLaunchKernelGGL((uvw_fwd_kernel<float>), grid, dim3(kUvwThreads), uvw_lds_bytes<float>(t.max_l3), s, a);
   CGTP_CHECK_HIP(hipGetLastError());
 }
 
