@@ -28,6 +28,7 @@ Modules:
   conv    - TFN convolution forward/backward                    [COURSE 06a; E3J E.2.2, E.3]
   linear  - equivariant linear map (channel mixing)             [E3J A.3; COURSE 03b]
   modes   - connection modes uvu (any y multiplicity) and uvw   [COURSE 03b; E3J E.1]
+  radial  - radial network's last layer joined to the convolution [COURSE 06a; E3J E.4, F.1; XNN]
 
 Parity status: every function here is pinned by tests/test_oracle_*.py against
 closed forms, textbook values, invariants or brute force; none is "parity
