@@ -589,6 +589,80 @@ def linear_bench(args, torch, cgtp, synth, dtype):
     return res
 
 
+def radial_bench(args, torch, cgtp, synth, name):
+    """The convolution with the radial network's last layer joined to it, on one
+    full-size workload: h = the hidden activations (64 wide) of the radial
+    network, W2 its last layer. Fused forward (w = h W2 formed on the matrix
+    cores inside the kernel) against the same result as two library calls (the
+    linear map writing w to memory, then the convolution reading it), and the
+    backward (composed: grad_x, grad_sh, grad_h, grad_W2)."""
+    import numpy as np
+    c = synth.CONFIGS[name]
+    dev = torch.device("cuda:0")
+    p = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"], wkind="per_row")
+    pos = synth.positions_for(c, 0)
+    src, dst, vec = synth.radius_graph(pos, c["box"], c["r_cut"])
+    N, E = pos.shape[0], src.shape[0]
+    row_ptr, src_s, perm = cgtp.csr_from_coo(N, torch.from_numpy(src.astype(np.int32)).to(dev),
+                                             torch.from_numpy(dst.astype(np.int32)).to(dev))
+    graph = cgtp.Graph(N, row_ptr, src_s)
+    v = torch.from_numpy(vec).to(dev)[perm.long()].float().contiguous()
+    Y = cgtp.sh_forward(c["L"], v)
+    H = 64
+    W1, W2 = synth.mlp_params(8, H, p.w_numel, 0)
+    W1, W2 = torch.from_numpy(W1).float().to(dev), torch.from_numpy(W2).float().to(dev)
+    eye = torch.eye(H, device=dev)
+    r = v.norm(dim=1)
+    h = torch.empty((E, H), device=dev)
+    for a in range(0, E, 1 << 20):
+        h[a:a + (1 << 20)] = synth.radial_weights_torch(r[a:a + (1 << 20)], c["r_cut"], W1, eye)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    x = torch.randn((N, p.dim_x), generator=gen, device=dev)
+    g = torch.randn((N, p.dim_out), generator=gen, device=dev)
+    sc = 1.0 / math.sqrt(E / N)
+    out = torch.empty((N, p.dim_out), device=dev)
+    fused = lambda: p.conv_forward_radial(graph, x, Y, h, W2, sc, out=out)
+    tf = KernelTimer(torch)
+    fused()
+    for _ in range(3):
+        tf(fused)
+    torch.cuda.synchronize()
+    lin = cgtp.Linear("%dx0e" % H, "%dx0e" % p.w_numel)
+    w = torch.empty((E, p.w_numel), device=dev)
+    out2 = torch.empty_like(out)
+    tl, tc = KernelTimer(torch), KernelTimer(torch)
+    W2f = W2.reshape(-1)  # the linear map's flat weights, W_p = W2 [H][W]
+    lin.forward(h, W2f, out=w)
+    p.conv_forward(graph, x, Y, w, sc, out=out2)
+    for _ in range(3):
+        tl(lambda: lin.forward(h, W2f, out=w))
+        tc(lambda: p.conv_forward(graph, x, Y, w, sc, out=out2))
+    torch.cuda.synchronize()
+    rel = float((out - out2).abs().max() / out2.abs().max())
+    del w, out2
+    torch.cuda.empty_cache()
+    ws = torch.empty(p.radial_workspace_size(graph, H), dtype=torch.uint8, device=dev)
+    grads = (torch.empty_like(x), torch.empty_like(Y), torch.empty_like(h), torch.empty_like(W2))
+    bwd = lambda: p.conv_backward_radial(graph, x, Y, h, W2, sc, g, out=grads, ws=ws)
+    tb = KernelTimer(torch)
+    bwd()
+    for _ in range(2):
+        tb(bwd)
+    torch.cuda.synchronize()
+    flops = 2 * E * H * p.w_numel
+    res = dict(workload=name, E=E, hidden=H, W=p.w_numel, last_layer_flops=flops,
+               fused_fwd_ms=round(tf.mean_ms(), 3), fused_fwd_edges_per_s=E / (tf.mean_ms() * 1e-3),
+               unfused_linear_ms=round(tl.mean_ms(), 3), unfused_conv_fwd_ms=round(tc.mean_ms(), 3),
+               unfused_fwd_ms=round(tl.mean_ms() + tc.mean_ms(), 3), fused_vs_unfused_max_rel_diff=rel,
+               bwd_ms=round(tb.mean_ms(), 3),
+               bwd="w = h W2 (linear map) + convolution backward + linear map backward (grad_h, grad_W2)",
+               bytes_not_moved_GB=round(2 * 4 * E * p.w_numel / 1e9, 1))
+    del ws, grads, h, x, g, out, Y, graph
+    torch.cuda.empty_cache()
+    return res
+
+
 def uvw_bench(args, torch, cgtp, synth, dtype):
     """Fully connected (uvw) product on the tp_large rows: 2^20 rows of
     128x(0e+1o+2e+3o), harmonics L = 3, every output type (l <= 3, both
@@ -921,6 +995,8 @@ def main():
         extra["conv_uniform100k_f64"] = conv_f64_forward_bench(args, torch, cgtp, synth)
         extra["conv_water8k_double_backward"] = double_backward_bench(args, torch, cgtp, synth)
         extra["conv_water1k_padded"] = padding_bench(args, torch, cgtp, synth)
+        extra["conv_water8k_radial"] = radial_bench(args, torch, cgtp, synth, "conv_water8k")
+        extra["conv_uniform100k_radial"] = radial_bench(args, torch, cgtp, synth, "conv_uniform100k")
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, synth)
     if not args.no_cpu_baseline and not args.no_extra:
         extra["cpu_baseline_conv"] = cpu_baseline_conv(args, synth)

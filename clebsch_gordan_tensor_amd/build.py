@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcgtp.so")
 SOURCES = ["plan.cpp", "capi.cpp", "tp_kernels.hip", "conv_kernels.hip", "graph_kernels.hip",
-           "sh_kernels.hip", "linear_kernels.hip", "double_backward.hip", "uvw_kernels.hip", "uvuv_kernels.hip"]
+           "sh_kernels.hip", "linear_kernels.hip", "double_backward.hip", "uvw_kernels.hip", "uvuv_kernels.hip", "radial_kernels.hip"]
 # one translation unit per large kernel instantiation, compiled in parallel
 SOURCES += sorted(os.path.join("inst", f) for f in os.listdir(os.path.join(CSRC, "inst")) if f.endswith(".hip"))
 ARCH = "gfx950"

@@ -56,6 +56,10 @@ _SIGS = {
     "cgtp_graph_create_ex": ([_c_i64, _c_i64, _vp, _vp, ctypes.c_int32, _vp, ctypes.POINTER(_vp)], ctypes.c_int),
     "cgtp_conv_backward": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_double, _vp, _vp, _vp, _vp, _vp,
                             ctypes.c_size_t, _vp], ctypes.c_int),
+    "cgtp_conv_forward_radial": ([_vp, _vp, _vp, _vp, _vp, _c_i64, _vp, ctypes.c_double, _vp, _vp], ctypes.c_int),
+    "cgtp_conv_backward_radial": ([_vp, _vp, _vp, _vp, _vp, _c_i64, _vp, ctypes.c_double, _vp, _vp, _vp, _vp, _vp,
+                                   _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+    "cgtp_conv_radial_workspace_size": ([_vp, _vp, _c_i64, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "cgtp_workspace_size": ([_vp, _vp, _c_i64, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "cgtp_sh_forward": ([ctypes.c_int, ctypes.c_int, _c_i64, _vp, _vp, _vp], ctypes.c_int),
     "cgtp_sh_backward": ([ctypes.c_int, ctypes.c_int, _c_i64, _vp, _vp, _vp, _vp], ctypes.c_int),
@@ -359,6 +363,56 @@ class Plan:
                                        _ptr(grad_out), _ptr(res[0]), _ptr(res[1]), _ptr(res[2]),
                                        _ptr(ws) if nws else _vp(0), _ws_bytes(ws) if nws else 0,
                                        _stream(x)), "cgtp_conv_backward")
+        return tuple(res)
+
+
+    # -------------------------------------- convolution with the radial last layer
+    def radial_workspace_size(self, graph, hidden):
+        n = ctypes.c_size_t()
+        _check(_lib.cgtp_conv_radial_workspace_size(self._h, graph._h, int(hidden), ctypes.byref(n)),
+               "cgtp_conv_radial_workspace_size")
+        return n.value
+
+    def conv_forward_radial(self, graph, x, sh, h, W2, scale, out=None):
+        """Convolution with w = h W2 formed inside the kernel (cgtp_conv_forward_radial)."""
+        torch = _torch()
+        dt = self.torch_dtype
+        H = W2.shape[0]
+        _need(x, (graph.N, self.dim_x), dt, "x")
+        _need(sh, (graph.E, self.dim_y), dt, "sh")
+        _need(h, (graph.E, H), dt, "h")
+        _need(W2, (H, self.w_numel), dt, "W2")
+        if out is None:
+            out = torch.empty((graph.N, self.dim_out), dtype=dt, device=x.device)
+        _need(out, (graph.N, self.dim_out), dt, "out")
+        _check(_lib.cgtp_conv_forward_radial(self._h, graph._h, _ptr(x), _ptr(sh), _ptr(h), H, _ptr(W2), float(scale),
+                                             _ptr(out), _stream(x)), "cgtp_conv_forward_radial")
+        return out
+
+    def conv_backward_radial(self, graph, x, sh, h, W2, scale, grad_out, need=(True, True, True, True),
+                             out=(None, None, None, None), ws=None):
+        """(grad_x, grad_sh, grad_h, grad_W2) of the radial convolution (cgtp_conv_backward_radial)."""
+        torch = _torch()
+        dt = self.torch_dtype
+        H = W2.shape[0]
+        _need(x, (graph.N, self.dim_x), dt, "x")
+        _need(sh, (graph.E, self.dim_y), dt, "sh")
+        _need(h, (graph.E, H), dt, "h")
+        _need(W2, (H, self.w_numel), dt, "W2")
+        _need(grad_out, (graph.N, self.dim_out), dt, "grad_out")
+        shapes = [(graph.N, self.dim_x), (graph.E, self.dim_y), (graph.E, H), (H, self.w_numel)]
+        res = []
+        for k in range(4):
+            if not need[k]:
+                res.append(None)
+                continue
+            t = out[k] if out[k] is not None else torch.empty(shapes[k], dtype=dt, device=x.device)
+            res.append(_need(t, shapes[k], dt, "grad"))
+        if ws is None:
+            ws = torch.empty(max(self.radial_workspace_size(graph, H), 1), dtype=torch.uint8, device=x.device)
+        _check(_lib.cgtp_conv_backward_radial(self._h, graph._h, _ptr(x), _ptr(sh), _ptr(h), H, _ptr(W2), float(scale),
+                                              _ptr(grad_out), *[_ptr(t) for t in res], _ptr(ws), _ws_bytes(ws),
+                                              _stream(x)), "cgtp_conv_backward_radial")
         return tuple(res)
 
 

@@ -342,6 +342,45 @@ cgtp_status cgtp_conv_backward(cgtp_plan plan, cgtp_graph graph, const void* x, 
   });
 }
 
+cgtp_status cgtp_conv_forward_radial(cgtp_plan plan, cgtp_graph graph, const void* x, const void* sh,
+                                     const void* h, int64_t hidden, const void* W2, double scale, void* out,
+                                     void* stream) {
+  return guarded([&] {
+    need(plan != nullptr && graph != nullptr, "NULL plan or graph");
+    need_plain_uvu(plan, "the convolution");
+    if (plan->wkind != CGTP_W_PER_ROW)
+      throw Error{CGTP_ERR_UNSUPPORTED, "the convolution needs per-edge weights (CGTP_W_PER_ROW)"};
+    if (graph->N == 0) return;
+    need(out != nullptr && W2 != nullptr, "NULL out or W2");
+    need(graph->E == 0 || (x && sh && h), "NULL input tensor");
+    conv_forward_radial_launch(plan, graph, x, sh, h, hidden, W2, scale, out, as_stream(stream));
+  });
+}
+
+cgtp_status cgtp_conv_backward_radial(cgtp_plan plan, cgtp_graph graph, const void* x, const void* sh,
+                                      const void* h, int64_t hidden, const void* W2, double scale,
+                                      const void* grad_out, void* grad_x, void* grad_sh, void* grad_h,
+                                      void* grad_W2, void* ws, size_t ws_bytes, void* stream) {
+  return guarded([&] {
+    need(plan != nullptr && graph != nullptr, "NULL plan or graph");
+    need_plain_uvu(plan, "the convolution");
+    if (plan->wkind != CGTP_W_PER_ROW)
+      throw Error{CGTP_ERR_UNSUPPORTED, "the convolution needs per-edge weights (CGTP_W_PER_ROW)"};
+    need(W2 != nullptr && grad_out != nullptr, "NULL W2 or grad_out");
+    need(graph->E == 0 || (x && sh && h), "NULL input tensor");
+    conv_backward_radial_launch(plan, graph, x, sh, h, hidden, W2, scale, grad_out, grad_x, grad_sh, grad_h, grad_W2,
+                                ws, ws_bytes, as_stream(stream));
+  });
+}
+
+cgtp_status cgtp_conv_radial_workspace_size(cgtp_plan plan, cgtp_graph graph, int64_t hidden, size_t* bytes) {
+  return guarded([&] {
+    need(plan != nullptr && graph != nullptr && bytes != nullptr, "NULL argument");
+    need(hidden > 0, "hidden <= 0");
+    *bytes = conv_backward_radial_ws_bytes(plan, graph, hidden);
+  });
+}
+
 cgtp_status cgtp_sh_forward(int lmax, cgtp_dtype dtype, int64_t n, const void* vec, void* sh,
                             void* stream) {
   return guarded([&] {

@@ -172,6 +172,8 @@ size_t uvuv_backward_ws_bytes(const cgtp_plan_s* plan, int64_t B);
 void uvuv_backward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* y, const void* w, const void* g,
                           void* dx, void* dy, void* dw, void* ws, size_t ws_bytes, hipStream_t s);
 void free_uvuv_tables(const cgtp_plan_s* plan);
+// Last-layer maps of the radial convolution (radial_kernels.hip).
+void free_radial_maps(const cgtp_plan_s* plan);
 
 // Backward over generic rows: row r reads x row x_idx[r] (or r), grad_out row
 // g_idx[r] (or r) times g_scale, y/w row r; writes grad_x row r either in the

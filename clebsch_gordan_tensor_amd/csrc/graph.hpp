@@ -40,6 +40,17 @@ void conv_double_backward_launch(cgtp_plan_s* plan, const cgtp_graph_s* gr, cons
                                  const void* gw, void* ddx, void* ddsh, void* ddw, void* ddg, void* ws,
                                  size_t ws_bytes, hipStream_t s);
 
+// Convolution with the radial network's last layer joined (radial_kernels.hip):
+// w = h W2 formed on the matrix cores inside the forward; the backward is
+// composed through the workspace.
+void conv_forward_radial_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x, const void* sh, const void* h,
+                                int64_t H, const void* W2, double scale, void* out, hipStream_t s);
+size_t conv_backward_radial_ws_bytes(const cgtp_plan_s* plan, const cgtp_graph_s* g, int64_t H);
+void conv_backward_radial_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x, const void* sh,
+                                 const void* h, int64_t H, const void* W2, double scale, const void* grad_out,
+                                 void* grad_x, void* grad_sh, void* grad_h, void* grad_W2, void* ws, size_t ws_bytes,
+                                 hipStream_t s);
+
 void sh_forward_launch(int lmax, cgtp_dtype dtype, int64_t n, const void* vec, void* sh, hipStream_t s);
 void sh_backward_launch(int lmax, cgtp_dtype dtype, int64_t n, const void* vec, const void* grad_sh,
                         void* grad_vec, hipStream_t s);

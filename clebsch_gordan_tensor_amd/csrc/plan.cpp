@@ -451,6 +451,7 @@ void destroy_plan(cgtp_plan_s* plan) {
   free_plan_tables(plan);
   free_uvw_tables(plan);
   free_uvuv_tables(plan);
+  free_radial_maps(plan);
   if (plan->mix) {
     free_linear_tables(plan->mix);
     delete plan->mix;

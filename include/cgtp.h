@@ -291,6 +291,37 @@ cgtp_status cgtp_conv_double_backward(cgtp_plan plan, cgtp_graph graph, const vo
                                       const void* gg_sh, const void* gg_w, void* out_x, void* out_sh, void* out_w,
                                       void* out_grad_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Convolution with the radial network's last layer joined to it: the per-edge
+ * weights are w[e, k] = sum_j h[e, j] W2[j, k], formed on the matrix cores
+ * inside the kernel and never written to memory (E3J E.4 and F.1: fuse
+ * message formation and avoid materialising edge-wise intermediates; xnn "Run
+ * Models on Fused GPU Kernels", "What to expect from fast implementations":
+ * radial networks above a million edges are recomputed rather than stored).
+ * Otherwise as cgtp_conv_forward.
+ *   h  [E][hidden] hidden activations of the radial network (CSR order)
+ *   W2 [hidden][W] its last layer, row-major (no bias)
+ * fp32 plans only; y degrees distinct, outputs not collapsed, x multiplicities
+ * in {16, 32, 64, 128, 256}, hidden a multiple of 4 up to 1024; otherwise
+ * UNSUPPORTED, as also when a slot chunk's two weight tiles and partial sums
+ * exceed the device's LDS (possible at multiplicity 256). Deterministic; the
+ * sum over a receiver's edges runs in another order than cgtp_conv_forward's
+ * (within rounding). */
+cgtp_status cgtp_conv_forward_radial(cgtp_plan plan, cgtp_graph graph, const void* x, const void* sh,
+                                     const void* h, int64_t hidden, const void* W2, double scale, void* out,
+                                     void* stream);
+
+/* Reverse mode of cgtp_conv_forward_radial: grad_x and grad_sh as in
+ * cgtp_conv_backward, grad_h [E][hidden] = grad_w W2^T and grad_W2
+ * [hidden][W] = h^T grad_w (summed over edges in a fixed order), where grad_w
+ * is the convolution's weight cotangent. Composed through the workspace
+ * (w, grad_w, the convolution's and the linear map's partials) of
+ * cgtp_conv_radial_workspace_size bytes. NULL gradients are skipped. */
+cgtp_status cgtp_conv_backward_radial(cgtp_plan plan, cgtp_graph graph, const void* x, const void* sh,
+                                      const void* h, int64_t hidden, const void* W2, double scale,
+                                      const void* grad_out, void* grad_x, void* grad_sh, void* grad_h,
+                                      void* grad_W2, void* ws, size_t ws_bytes, void* stream);
+cgtp_status cgtp_conv_radial_workspace_size(cgtp_plan plan, cgtp_graph graph, int64_t hidden, size_t* bytes);
+
 /* Workspace bytes for op (graph may be NULL for the tensor product, B is
  * ignored for the convolution). */
 cgtp_status cgtp_workspace_size(cgtp_plan plan, cgtp_graph graph, int64_t B, int op, size_t* bytes);
