@@ -41,7 +41,8 @@ METRIC = "TP pairs/s + conv edges/s (fwd, fwd+bwd) as HBM GB/s and % of MI355X p
 PROFILES = os.path.join(ROOT, "profiles")
 WORKLOADS = ["tp_large", "tp_large_bf16", "conv_water1k", "conv_water8k", "conv_uniform100k", "linear_large",
              "linear_large_bf16", "tp_large_collapsed", "conv_collapsed_l3", "conv_collapsed_l4",
-             "conv_uniform100k_f64"]
+             "conv_uniform100k_f64", "conv_water8k_radial", "conv_uniform100k_radial", "uvw_tp_large",
+             "uvw_tp_large_bf16"]
 MFMA_FP32_PEAK_TFS = 157.3
 MFMA_BF16_PEAK_TFS = 2500.0
 
@@ -258,7 +259,69 @@ class LinearWorkload:
         self.lin.backward(self.x, self.w, self.g, need=(False, True), out=(None, self.dw), ws=self.ws)
 
 
+class RadialWorkload(ConvWorkload):
+    """A convolution workload with the radial network's last layer joined: h
+    [E][64] are the network's hidden activations, W2 [64][W] its last layer."""
+
+    def __init__(self, torch, cgtp, synth, name):
+        super().__init__(torch, cgtp, synth, name)
+        c, p, dev = self.c, self.plan, self.x.device
+        W1, W2 = synth.mlp_params(8, 64, p.w_numel, 0)
+        W1 = torch.from_numpy(W1).float().to(dev)
+        self.W2 = torch.from_numpy(W2).float().to(dev)
+        eye = torch.eye(64, device=dev)
+        r = self.vec.norm(dim=1)
+        del self.w, self.dw, self.ws
+        torch.cuda.empty_cache()
+        self.h = torch.empty((self.E, 64), device=dev)
+        for a in range(0, self.E, 1 << 20):
+            self.h[a:a + (1 << 20)] = synth.radial_weights_torch(r[a:a + (1 << 20)], c["r_cut"], W1, eye)
+        self.dh, self.dW2 = torch.empty_like(self.h), torch.empty_like(self.W2)
+        self.ws = torch.empty(p.radial_workspace_size(self.graph, 64), dtype=torch.uint8, device=dev)
+
+    def fwd(self):
+        self.plan.conv_forward_radial(self.graph, self.x, self.Y, self.h, self.W2, self.scale, out=self.out)
+
+    def bwd(self):
+        self.plan.conv_backward_radial(self.graph, self.x, self.Y, self.h, self.W2, self.scale, self.gout,
+                                       out=(self.dx, self.dY, self.dh, self.dW2), ws=self.ws)
+
+
+class UvwWorkload:
+    """The fully connected (uvw) product on the tp_large rows with collapsed
+    outputs: 2^20 rows of 128x(0e+1o+2e+3o), harmonics L = 3, every output
+    type (l <= 3, both parities) at 128 channels, shared 128 x 128 weights."""
+
+    def __init__(self, torch, cgtp, synth, dtype):
+        c = synth.CONFIGS["tp_large"]
+        io = "+".join("128x%d%s" % (l, p) for l in range(4) for p in "eo")
+        self.B = B = c["B"]
+        td = torch.float32 if dtype == "f32" else torch.bfloat16
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(0)
+        self.plan = p = cgtp.Plan(c["irreps_x"], c["irreps_y"], io, mode="uvw", dtype=dtype, wkind="shared",
+                                  collapse=True)
+        self.x = torch.randn((B, p.dim_x), generator=gen, device="cuda").to(td)
+        v = torch.randn((B, 3), generator=gen, device="cuda")
+        self.y = cgtp.sh_forward(3, v / v.norm(dim=1, keepdim=True)).to(td)
+        self.w = (torch.randn((p.w_numel,), generator=gen, device="cuda") / 16.0).to(td)
+        self.g = torch.randn((B, p.dim_out), generator=gen, device="cuda").to(td)
+        self.out = torch.empty((B, p.dim_out), device="cuda", dtype=td)
+        self.dx, self.dy, self.dw = torch.empty_like(self.x), torch.empty_like(self.y), torch.empty_like(self.w)
+        self.ws = torch.empty(p.workspace_size(cgtp.OP_TP_BACKWARD, B), dtype=torch.uint8, device="cuda")
+
+    def fwd(self):
+        self.plan.tp_forward(self.x, self.y, self.w, out=self.out)
+
+    def bwd(self):
+        self.plan.tp_backward(self.x, self.y, self.w, self.g, out=(self.dx, self.dy, self.dw), ws=self.ws)
+
+
 def make_workload(torch, cgtp, synth, name):
+    if name.startswith("uvw"):
+        return UvwWorkload(torch, cgtp, synth, "bf16" if name.endswith("bf16") else "f32")
+    if name.endswith("_radial"):
+        return RadialWorkload(torch, cgtp, synth, name[:-len("_radial")])
     if name.startswith("linear"):
         return LinearWorkload(torch, cgtp, synth, "bf16" if name.endswith("bf16") else "f32")
     if name == "tp_large":
@@ -279,13 +342,15 @@ def profile(torch, cgtp, synth, name):
         ops = [wl.fwd, wl.bwd_x, wl.bwd_w]
     elif name.endswith("_f64"):
         ops = [wl.fwd]
+    elif name.startswith("uvw") or name.endswith("_radial"):
+        ops = [wl.fwd, wl.bwd]
     else:
         ops = [wl.sh, wl.fwd, wl.bwd] if name.startswith("tp") else [wl.sh_fwd, wl.fwd, wl.bwd, wl.sh_bwd]
     for _ in range(3):
         for op in ops:
             op()
     torch.cuda.synchronize()
-    rowwise = name.startswith("tp") or name.startswith("linear")
+    rowwise = name.startswith("tp") or name.startswith("linear") or name.startswith("uvw")
     units = wl.B if rowwise else wl.E
     print(json.dumps({"profiled": name, "calls": 3, "units": units,
                       "unit": "row" if rowwise else "edge"}), flush=True)
@@ -681,8 +746,11 @@ def uvw_bench(args, torch, cgtp, synth, dtype):
     es = 4 if dtype == "f32" else 2
     gen = torch.Generator(device="cuda")
     gen.manual_seed(0)
+    peak = MFMA_FP32_PEAK_TFS if dtype == "f32" else MFMA_BF16_PEAK_TFS
     res = {"rows": B, "irreps_x": ix, "irreps_out": io, "dtype": dtype,
-           "mfma": "v_mfma_f32_16x16x4_f32 (bf16 storage widened exactly)"}
+           "mfma": ("v_mfma_f32_16x16x4_f32" if dtype == "f32" else
+                    "v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32 sums; path outputs rounded to bf16 in LDS)"),
+           "mfma_peak_TFLOPs": peak}
     x = torch.randn((B, 2048), generator=gen, device="cuda").to(td)
     v = torch.randn((B, 3), generator=gen, device="cuda")
     y = cgtp.sh_forward(3, v / v.norm(dim=1, keepdim=True)).to(td)
@@ -703,7 +771,7 @@ def uvw_bench(args, torch, cgtp, synth, dtype):
         key = "collapsed" if collapse else "uncollapsed"
         res[key] = dict(paths=p.num_paths, dim_out=p.dim_out, fwd_ms=round(ms, 3), fwd_pairs_per_s=B / (ms * 1e-3),
                         fwd_TFLOPs=round(flops / (ms * 1e-3) / 1e12, 1),
-                        fwd_frac_of_fp32_mfma_peak=round(flops / (ms * 1e-3) / 1e12 / MFMA_FP32_PEAK_TFS, 3),
+                        fwd_frac_of_mfma_peak=round(flops / (ms * 1e-3) / 1e12 / peak, 3),
                         fwd_algorithmic_GBs=round(nbytes / (ms * 1e-3) / 1e9, 1), flops=flops)
         if collapse:
             # the same product as two calls: unit-weight uvu forward, then the linear map

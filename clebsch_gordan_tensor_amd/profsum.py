@@ -3,7 +3,7 @@
     python -m clebsch_gordan_tensor_amd.profsum <results.db> [--match SUBSTR] [--pmc] [--json OUT]
     python -m clebsch_gordan_tensor_amd.profsum --traffic OUT --fetch F.json --write W.json
            --calib-fetch CF.json --calib-write CW.json --calib-bytes B --units N --unit NAME
-           --workload NAME --kernel BASE=src1,src2 [--kernel ...]
+           --workload NAME --kernel BASE=src1,src2 [--kernel ...] [--per-call BASE=N ...]
 
 The first form prints, per kernel name (optionally filtered), the dispatch
 count, mean and total duration, and with --pmc the mean of every collected
@@ -12,7 +12,8 @@ figures as JSON. The second form turns FETCH_SIZE / WRITE_SIZE summaries (KiB
 per dispatch) into bytes per unit of work: each counter is scaled by what it
 reads for a plain copy of known size (--calib-bytes read and written per
 copy dispatch), and the dispatches of every instantiation of a kernel template
-are added (one call of an operation launches each instantiation once). The
+are added (one call of an operation launches each instantiation once, or N
+times where --per-call BASE=N says so, e.g. one launch per output parity). The
 entry (keyed kernel@workload) is tagged with a hash of the kernel's source
 files, so a reader can tell when the counters no longer describe the code.
 """
@@ -112,6 +113,10 @@ def traffic(a):
     wf = calib_factor(a.calib_write, "WRITE_SIZE", a.calib_bytes)
     fetch = counter_by_base(a.fetch, "FETCH_SIZE")
     write = counter_by_base(a.write, "WRITE_SIZE")
+    per_call = {}
+    for spec in a.per_call or []:
+        base, n = spec.split("=")
+        per_call[base] = int(n)
     rec = {}
     if os.path.exists(a.traffic):
         with open(a.traffic) as f:
@@ -125,8 +130,9 @@ def traffic(a):
         if base not in fetch or base not in write:
             print("%-28s no counter data, skipped" % base)
             continue
-        fb = fetch.get(base, 0.0) * ff / a.units
-        wb = write.get(base, 0.0) * wf / a.units
+        n = per_call.get(base, 1)
+        fb = n * fetch.get(base, 0.0) * ff / a.units
+        wb = n * write.get(base, 0.0) * wf / a.units
         rec["%s@%s" % (base, a.workload)] = {"bytes_per_unit": round(fb + wb, 1), "fetch_bytes_per_unit": round(fb, 1),
                      "write_bytes_per_unit": round(wb, 1), "unit": a.unit, "workload": a.workload,
                      "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
@@ -153,6 +159,7 @@ def main():
     ap.add_argument("--unit")
     ap.add_argument("--workload")
     ap.add_argument("--kernel", action="append", default=[], help="BASE=src1,src2 (csrc files)")
+    ap.add_argument("--per-call", action="append", default=[], help="BASE=N dispatches of BASE per call (default 1)")
     a = ap.parse_args()
     if a.traffic:
         return traffic(a)

@@ -21,16 +21,25 @@
  *  - Real CG blocks are orthonormal over (m1, m2) for each m3. Sign per path:
  *    even l1+l2+l3 -> C[0,0,0] > 0; odd -> the first nonzero entry in
  *    lexicographic (m1, m2, m3) order (each m from -l) is positive.
- *  - Mode "uvu" (channel-wise): for path p = (i1, i2, l3) with x block i1 of
- *    multiplicity u,
- *      out[z, p, m3, u] = w[(z,) p, u] sum_{m1,m2} C_p[m1,m2,m3] x[z,i1,m1,u] y[z,i2,m2]
- *    Every y block must have multiplicity 1. Paths: every x block i1, every y
- *    block i2, every l3 in |l1-l2|..l1+l2 whose (l3, p1*p2) appears in
- *    irreps_out (multiplicities of irreps_out are ignored); order i1, i2, l3.
- *    One output block per path (not collapsed by degree).
+ *  - Connection modes (lesson 03b names uvw and uvu; the formulas are e3nn's).
+ *    For path p = (i1, i2, l3), x block i1 of multiplicity u, y block i2 of
+ *    multiplicity v, with T_p[z, m3, a, b] = sum_{m1,m2} C_p[m1,m2,m3]
+ *    x[z,i1,m1,a] y[z,i2,m2,b]:
+ *      "uvu" (channel-wise): out[z, p, m3, a] = sum_b w[(z,) p, a, b] T_p[z,m3,a,b]
+ *         (v = 1: out = w[(z,) p, a] C x y, one weight per path and channel)
+ *      "uvw" (fully connected): out[z, p, m3, k] = sum_a W[p, a, k] T_p[z,m3,a,0]
+ *         with the output multiplicity taken from the first irreps_out entry
+ *         of type (l3, p3); y multiplicity 1, shared weights, fp32 or bf16,
+ *         multiplicities in multiples of 4.
+ *    Paths: every x block i1, every y block i2, every l3 in |l1-l2|..l1+l2
+ *    whose (l3, p1*p2) appears in irreps_out; order i1, i2, l3. One output
+ *    block per path (not collapsed by degree) unless the plan collapses them.
+ *    The convolution, the double backward and cgtp_tp_backward_noalloc take
+ *    uvu plans with y multiplicity 1 (others: UNSUPPORTED).
  *  - Row layouts: blocks concatenated in irreps (or path) order; inside a
  *    block [2l+1][mul] (channel index fastest, "ir_mul"). Weights of one row
- *    are [path][mul] concatenated (W = sum_p mul_p elements).
+ *    are [path][mul] concatenated (uvu, v = 1: W = sum_p mul_p elements);
+ *    uvu with v > 1: [path][u][v]; uvw: [path][u][w], row-major.
  *
  * Memory and execution:
  *  - Every tensor argument is a DEVICE pointer owned by the caller, of the
@@ -113,11 +122,12 @@ const char* cgtp_last_error(void);
  * CG values are built with the ladder-operator construction of E3J appendix
  * G.2: the highest-weight vector of each l3 solves a triangular system, lower
  * m3 follow by repeated lowering; then the real-basis change and sign rule.
- *   mode   : "uvu" only.
+ *   mode   : "uvu" or "uvw" (see Connection modes above).
  *   dtype  : storage type of every float tensor (bf16 computes in fp32).
  *   wkind  : see cgtp_wkind.
- * Errors: PARSE (bad string), UNSUPPORTED (mode != "uvu", a y multiplicity
- * != 1, any l > CGTP_LMAX, no path at all), INVALID_ARG (null pointers). */
+ * Errors: PARSE (bad string), UNSUPPORTED (another mode, uvw outside its
+ * limits above, uvu with y multiplicity > 1 and collapsed outputs, any
+ * l > CGTP_LMAX, no path at all), INVALID_ARG (null pointers). */
 cgtp_status cgtp_plan_create(const char* irreps_x, const char* irreps_y, const char* irreps_out,
                              const char* mode, cgtp_dtype dtype, cgtp_wkind wkind, cgtp_plan* out);
 /* cgtp_plan_create with a path selection and, if collapse != 0, outputs
