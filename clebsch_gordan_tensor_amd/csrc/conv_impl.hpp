@@ -624,9 +624,7 @@ void conv_bwd_fused_kernel(ConvArgs a, ConvBwdArgs bw) {
           const A* __restrict__ cp = cf + coff[i];
           A gb[2 * L3 + 1][VEC];
 #pragma unroll
-          for (int m = 0; m < 2 * L3 + 1; ++m)
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) gb[m][v] = gl[(st.acc + m) * CW + li * VEC + v];
+          for (int m = 0; m < 2 * L3 + 1; ++m) VecIO<A, VEC>::load(gl + (st.acc + m) * CW + li * VEC, gb[m]);  // one VEC-wide LDS read
           // pairs are m1-major: q[m1] = sum_m3 A[m1,m3] g[m3] is folded into
           // grad_w and the grad_x partial after the last pair of its m1
           A d[VEC], q[VEC], xw[VEC];

@@ -314,23 +314,24 @@ struct RowAcc {
 };
 template <typename A, int VEC, int N>
 struct RowAcc<A, VEC, N, true> {
-  A* p;  // this lane's row 0
+  A* p;  // this lane's row 0 (16-byte aligned: the rows start at a multiple of kBlock * VEC elements)
   __device__ __forceinline__ explicit RowAcc(A* base) : p(base + threadIdx.x * VEC) {
+    A z[VEC];
 #pragma unroll
-    for (int m = 0; m < N; ++m)
+    for (int v = 0; v < VEC; ++v) z[v] = A(0);
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) p[m * kBlock * VEC + v] = A(0);
+    for (int m = 0; m < N; ++m) VecIO<A, VEC>::store(p + m * kBlock * VEC, z);
   }
+  // one VEC-wide LDS access per row (lanes at consecutive VEC-element slots,
+  // so a wave's access has no bank conflict)
   __device__ __forceinline__ void fma_row(int m, const A (&w)[VEC], const A (&q)[VEC]) {
     A t[VEC];
     get(m, t);
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) p[m * kBlock * VEC + v] = fma(w[v], q[v], t[v]);
+    for (int v = 0; v < VEC; ++v) t[v] = fma(w[v], q[v], t[v]);
+    VecIO<A, VEC>::store(p + m * kBlock * VEC, t);
   }
-  __device__ __forceinline__ void get(int m, A (&o)[VEC]) const {
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) o[v] = p[m * kBlock * VEC + v];
-  }
+  __device__ __forceinline__ void get(int m, A (&o)[VEC]) const { VecIO<A, VEC>::load(p + m * kBlock * VEC, o); }
 };
 
 template <typename T, typename A, int VEC, int LM>
