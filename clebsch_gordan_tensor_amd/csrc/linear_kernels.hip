@@ -241,6 +241,33 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 constexpr int kKB = 32;         // contraction rows per B chunk (the MFMA's K)
 constexpr int kBTP = kKB + 8;   // padded n-major LDS row of a B chunk, in elements
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// n-major LDS tiles T[n][k] (rows of kBTP elements: 32 k and 16 bytes of
+// padding) hold their 16-byte k runs (k = 8c .. 8c + 7) at run position
+// c ^ ((n >> 3) & 3). With the 80-byte rows, any 8 consecutive n read at one
+// run position, and the transposing writes below (8 lanes with consecutive
+// column blocks and one row block), land in 8 different groups of 4 banks.
+__device__ __forceinline__ int tile_run(int n, int c) { return n * kBTP + 8 * (c ^ ((n >> 3) & 3)); }
+
+// Transposing stash of one block of a row-major (k slow) bf16 tile: R[r]
+// holds W consecutive n of row k = 8 kb + r (W = 2 or 4, packed two per
+// dword); each of the W columns n0 + j goes to T[n0 + j][8 kb .. 8 kb + 7]
+// as one 16-byte write.
+template <int W>
+__device__ __forceinline__ void stash_block(uint16_t* __restrict__ T, int n0, int kb, const uint32_t (&R)[8][W / 2]) {
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    const int d = j >> 1;
+    u32x4 o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t lo = R[2 * p][d], hi = R[2 * p + 1][d];
+      o[p] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+    *reinterpret_cast<u32x4*>(T + tile_run(n0 + j, kb)) = o;
+  }
+}
 
 __global__ __launch_bounds__(kLinThreads) void lin_rows_bf16_kernel(const bf16* __restrict__ A, int64_t lda,
                                                                   const bf16* __restrict__ W, bf16* __restrict__ C,
@@ -271,41 +298,50 @@ __global__ __launch_bounds__(kLinThreads) void lin_rows_bf16_kernel(const bf16* 
         reinterpret_cast<const uint16_t*>(W) + tm.b_off + int64_t(jb.b_n0) * tm.b_sn;
     const bool kfast = tm.b_sk == 1;  // transposed weights: runs of 8 along k
     const int nch = (tm.K + kKB - 1) / kKB;
-    // B chunk: 32 x 128 as 512 runs of 8 elements, two per thread, requested
-    // unconditionally from clamped addresses and masked when stashed
+    // B chunk, 32 x 128: with runs along k (transposed weights), 512 runs of
+    // 8 elements, two per thread, stored as they are; with runs along n, one
+    // 8 (k) x 2 (n) block per thread, transposed on the way into LDS. Requests
+    // go out unconditionally from clamped addresses and are masked when stashed.
     u16x8 pre[2];
-    auto unit = [&](int q, int c, int& n, int& k) {
+    uint32_t preb[8][1];
+    auto unit = [&](int q, int c, int& n, int& k) {  // runs along k
       const int u = int(threadIdx.x) + q * kLinThreads;
-      if (kfast) {
-        n = u >> 2;
-        k = c * kKB + (u & 3) * 8;
-      } else {
-        k = c * kKB + (u >> 4);
-        n = (u & 15) * 8;
-      }
+      n = u >> 2;
+      k = c * kKB + (u & 3) * 8;
     };
+    const int bn = 2 * (int(threadIdx.x) & 63), bk = int(threadIdx.x) >> 6;  // runs along n: block origin
     auto fetch = [&](int c) {
+      if (kfast) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        int n, k;
-        unit(q, c, n, k);
-        const bool ok = k < tm.K && n < jb.n_len;
-        pre[q] = *reinterpret_cast<const u16x8*>(wb + int64_t(ok ? k : 0) * tm.b_sk + int64_t(ok ? n : 0) * tm.b_sn);
+        for (int q = 0; q < 2; ++q) {
+          int n, k;
+          unit(q, c, n, k);
+          const bool ok = k < tm.K && n < jb.n_len;
+          pre[q] = *reinterpret_cast<const u16x8*>(wb + int64_t(ok ? k : 0) * tm.b_sk + int64_t(ok ? n : 0) * tm.b_sn);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int k = c * kKB + 8 * bk + r;
+          const bool ok = k < tm.K && bn < jb.n_len;
+          preb[r][0] = *reinterpret_cast<const uint32_t*>(wb + int64_t(ok ? k : 0) * tm.b_sk + (ok ? bn : 0));
+        }
       }
     };
     auto stash = [&](int c, int buf) {
+      if (kfast) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        int n, k;
-        unit(q, c, n, k);
-        const u16x8 v = (k < tm.K && n < jb.n_len) ? pre[q] : zero8;
-        const int kk = k - c * kKB;
-        if (kfast) {
-          *reinterpret_cast<u16x8*>(&bt[buf][n * kBTP + kk]) = v;
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) bt[buf][(n + j) * kBTP + kk] = v[j];
+        for (int q = 0; q < 2; ++q) {
+          int n, k;
+          unit(q, c, n, k);
+          const u16x8 v = (k < tm.K && n < jb.n_len) ? pre[q] : zero8;
+          *reinterpret_cast<u16x8*>(&bt[buf][tile_run(n, (k - c * kKB) >> 3)]) = v;
         }
+      } else {
+        uint32_t m[8][1];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) m[r][0] = (c * kKB + 8 * bk + r < tm.K && bn < jb.n_len) ? preb[r][0] : 0u;
+        stash_block<2>(bt[buf], bn, bk, m);
       }
     };
     // this lane's 8 consecutive k of each of its two rows (K is a multiple of
@@ -337,7 +373,7 @@ __global__ __launch_bounds__(kLinThreads) void lin_rows_bf16_kernel(const bf16* 
       for (int s2 = 0; s2 < 2; ++s2) av[s2] = __builtin_bit_cast(bf16x8, kin ? ac[s2] : zero8);
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(bc + (tt * 16 + li) * kBTP + 8 * lk));
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(bc + tile_run(tt * 16 + li, lk)));
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
           acc[s2][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s2], bv, acc[s2][tt], 0, 0, 0);
@@ -425,9 +461,11 @@ __global__ __launch_bounds__(kLinThreads) void lin_dw_kernel(const T* __restrict
 
 // grad_W partials with bf16 storage on v_mfma_f32_16x16x32_bf16: the
 // contraction runs over rows, which are strided in memory, so each 32-row
-// step stages x and g transposed in LDS ([u][row] and [v][row], from 16-byte
-// row loads) and every lane then reads its 8 consecutive rows of one u (A)
-// and one v (B) in one access. Widths and offsets are multiples of 8.
+// step stages x and g transposed in LDS ([u][row] and [v][row]: each thread
+// loads an 8-row x 4-column block with 8-byte row loads and writes its four
+// columns as 16-byte runs, at the swizzled positions of tile_run) and every
+// lane then reads its 8 consecutive rows of one u (A) and one v (B) in one
+// access. Widths and offsets are multiples of 8.
 __global__ __launch_bounds__(kLinThreads) void lin_dw_bf16_kernel(const bf16* __restrict__ X, int64_t ldx,
                                                                 const bf16* __restrict__ G, int64_t ldg,
                                                                 float* __restrict__ part, int64_t w_numel,
@@ -446,52 +484,43 @@ __global__ __launch_bounds__(kLinThreads) void lin_dw_bf16_kernel(const bf16* __
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[s][t] = v4f{0.f, 0.f, 0.f, 0.f};
-  const u16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
   const uint16_t* __restrict__ Xs = reinterpret_cast<const uint16_t*>(X);
   const uint16_t* __restrict__ Gs = reinterpret_cast<const uint16_t*>(G);
-  // one 32-row step: 512 runs of 8 for x (row, u run) and as many for g,
-  // two of each per thread, requested from clamped addresses, masked when stashed
-  u16x8 px[2], pg[2];
-  auto unit = [&](int q, int& r, int& n) {
-    const int u = int(threadIdx.x) + q * kLinThreads;
-    r = u >> 4;
-    n = (u & 15) * 8;
-  };
+  // one 32-row step: threads 0-127 take one 8 (row) x 4 (u) block of x each,
+  // threads 128-255 one 8 x 4 block of g, requested from clamped addresses,
+  // masked and transposed when stashed
+  const bool tg = threadIdx.x >= 128;
+  const int bc = 4 * (int(threadIdx.x) & 31), bz = (int(threadIdx.x) >> 5) & 3;  // block origin (column, row block)
+  const int mlim = tg ? jb.mv : jb.mu, c0 = tg ? jb.v0 : jb.u0;
+  const bool col_ok = c0 + bc < mlim;
+  uint32_t pr[8][2];
   const int nsteps = int((z1 - z0 + kKB - 1) / kKB);
   const int total = jb.nm * nsteps;
   auto fetch = [&](int it) {
-    const int m = it / nsteps;
+    const int m = it < total ? it / nsteps : 0;
     const int64_t zs = z0 + int64_t(it - m * nsteps) * kKB;
+    const uint16_t* __restrict__ base = tg ? Gs + jb.g_off + int64_t(m) * jb.mv : Xs + jb.x_off + int64_t(m) * jb.mu;
+    const int64_t ld = tg ? ldg : ldx;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      int r, n;
-      unit(q, r, n);
-      const int64_t z = zs + r;
-      const bool zok = it < total && z < z1;
-      const int64_t zr = zok ? z : z0;
-      const int mm = it < total ? m : 0;
-      px[q] = *reinterpret_cast<const u16x8*>(Xs + zr * ldx + jb.x_off + int64_t(mm) * jb.mu +
-                                              (jb.u0 + n < jb.mu ? jb.u0 + n : 0));
-      pg[q] = *reinterpret_cast<const u16x8*>(Gs + zr * ldg + jb.g_off + int64_t(mm) * jb.mv +
-                                              (jb.v0 + n < jb.mv ? jb.v0 + n : 0));
+    for (int r = 0; r < 8; ++r) {
+      const int64_t z = zs + 8 * bz + r;
+      const bool ok = it < total && z < z1;
+      const uint2 v = *reinterpret_cast<const uint2*>(base + (ok ? z : z0) * ld + (col_ok ? c0 + bc : 0));
+      pr[r][0] = v.x;
+      pr[r][1] = v.y;
     }
   };
   auto stash = [&](int it, int buf) {
-    const int m = it / nsteps;
+    const int m = it < total ? it / nsteps : 0;
     const int64_t zs = z0 + int64_t(it - m * nsteps) * kKB;
+    uint32_t q[8][2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      int r, n;
-      unit(q, r, n);
-      const bool zok = it < total && zs + r < z1;
-      const u16x8 vx = (zok && jb.u0 + n < jb.mu) ? px[q] : zero8;
-      const u16x8 vg = (zok && jb.v0 + n < jb.mv) ? pg[q] : zero8;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        xt[buf][(n + j) * kBTP + r] = vx[j];
-        gt[buf][(n + j) * kBTP + r] = vg[j];
-      }
+    for (int r = 0; r < 8; ++r) {
+      const bool ok = it < total && zs + 8 * bz + r < z1 && col_ok;
+      q[r][0] = ok ? pr[r][0] : 0u;
+      q[r][1] = ok ? pr[r][1] : 0u;
     }
+    stash_block<4>(tg ? gt[buf] : xt[buf], bc, bz, q);
   };
   if (total > 0) {
     fetch(0);
@@ -505,10 +534,10 @@ __global__ __launch_bounds__(kLinThreads) void lin_dw_bf16_kernel(const bf16* __
       bf16x8 av[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
-        av[s2] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(xc + (ub + 16 * s2 + li) * kBTP + 8 * lk));
+        av[s2] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(xc + tile_run(ub + 16 * s2 + li, lk)));
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(gc + (16 * tt + li) * kBTP + 8 * lk));
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(gc + tile_run(16 * tt + li, lk)));
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
           acc[s2][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s2], bv, acc[s2][tt], 0, 0, 0);

@@ -177,7 +177,9 @@ __device__ __forceinline__ void uvw_mix_chunk(int kn, const typename UvwMma<T>::
   }
 }
 
-template <typename T>
+// LM: the plan's largest degree (x, y and outputs), so that only the
+// coefficient patterns a plan can take are compiled into the kernel.
+template <typename T, int LM>
 __global__ __launch_bounds__(kUvwThreads) void uvw_fwd_kernel(UvwArgs a) {
   using M = UvwMma<T>;
   extern __shared__ __attribute__((aligned(16))) unsigned char uvw_smem[];
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(kUvwThreads) void uvw_fwd_kernel(UvwArgs a) {
   T* __restrict__ orow = static_cast<T*>(a.out) + (row_out < a.B ? row_out : int64_t(0)) * a.dim_out;
   for (int gi = 0; gi < a.ngroups; ++gi) {
     const UvwGroupDev gd = ldc(a.groups + gi);
-    static_for<0, kLmax + 1>([&](auto L3c) {
+    static_for<0, LM + 1>([&](auto L3c) {
       constexpr int L3 = decltype(L3c)::value;
       if (gd.l3 != L3) return;
       for (int c0 = 0; c0 < gd.w_out; c0 += kUvwCols) {
@@ -209,9 +211,9 @@ __global__ __launch_bounds__(kUvwThreads) void uvw_fwd_kernel(UvwArgs a) {
             typename M::AW aw[M::NK];
             uvw_load_w<T>(W, pd.u, gd.w_out, k0, lk, kout, kok, aw);
             __syncthreads();  // the previous chunk's T has been read
-            static_for<0, kLmax + 1>([&](auto L1c) {
+            static_for<0, LM + 1>([&](auto L1c) {
               constexpr int L1 = decltype(L1c)::value;
-              static_for<0, kLmax + 1>([&](auto L2c) {
+              static_for<0, LM + 1>([&](auto L2c) {
                 constexpr int L2 = decltype(L2c)::value;
                 if constexpr (L3 >= (L1 > L2 ? L1 - L2 : L2 - L1) && L3 <= L1 + L2) {
                   if (pd.l1 == L1 && pd.l2 == L2) uvw_t_chunk<T, L1, L2, L3>(a, pd, xr, yr, k0, zt, rt, tl);
@@ -321,10 +323,20 @@ void uvw_forward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void*
   a.dim_out = int(plan->dim_out);
   a.ngroups = t.ngroups;
   const dim3 grid(unsigned((B + kUvwRows - 1) / kUvwRows));
-  if (plan->dtype == CGTP_BF16)
-    hipLaunchKernelGGL((uvw_fwd_kernel<bf16>), grid, dim3(kUvwThreads), uvw_lds_bytes<bf16>(t.max_l3), s, a);
-  else
-    hipLaunchKernelGGL((uvw_fwd_kernel<float>), grid, dim3(kUvwThreads), uvw_lds_bytes<float>(t.max_l3), s, a);
+  int lm = plan->lm;
+  for (const BlockInfo& b : plan->blocks) lm = std::max(lm, b.l1);
+  const bool h = plan->dtype == CGTP_BF16;
+  const size_t lds = h ? uvw_lds_bytes<bf16>(t.max_l3) : uvw_lds_bytes<float>(t.max_l3);
+  if (lm <= 2) {
+    if (h) hipLaunchKernelGGL((uvw_fwd_kernel<bf16, 2>), grid, dim3(kUvwThreads), lds, s, a);
+    else hipLaunchKernelGGL((uvw_fwd_kernel<float, 2>), grid, dim3(kUvwThreads), lds, s, a);
+  } else if (lm == 3) {
+    if (h) hipLaunchKernelGGL((uvw_fwd_kernel<bf16, 3>), grid, dim3(kUvwThreads), lds, s, a);
+    else hipLaunchKernelGGL((uvw_fwd_kernel<float, 3>), grid, dim3(kUvwThreads), lds, s, a);
+  } else {
+    if (h) hipLaunchKernelGGL((uvw_fwd_kernel<bf16, kLmax>), grid, dim3(kUvwThreads), lds, s, a);
+    else hipLaunchKernelGGL((uvw_fwd_kernel<float, kLmax>), grid, dim3(kUvwThreads), lds, s, a);
+  }
   CGTP_CHECK_HIP(hipGetLastError());
 }
 
