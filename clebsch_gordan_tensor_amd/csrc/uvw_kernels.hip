@@ -11,15 +11,15 @@
 // with W_p = [u][1][w] = [u][w] (shared weights). Collapsed outputs put every
 // path of one (l3, p3) into one block o (the fully connected product).
 //
-// Forward, one kernel: a workgroup owns 16 rows and walks every output block
+// Forward, one kernel: a workgroup owns 32 rows and walks every output block
 // and every path into it. Per path (and chunk of 128 x channels) each lane
 // first requests its W operands for the whole chunk (from L2), then the 512
-// lanes form T_p for the 16 rows in LDS on the vector ALUs (lane = (row, 4
+// lanes form T_p for the 32 rows in LDS on the vector ALUs (lane = (row, 4
 // channels), the coefficient sparsity pattern fixed at compile time, as in
 // the channel-wise product), then the eight waves run the matrix cores on
 // D[k][z] += sum_a W_p[a][k] T_p[z, m3, a] for every m3: wave w owns output
 // channels [16w, 16w + 16) of a 128-channel column tile (one 16-row A tile),
-// all 2 l3 + 1 N tiles (16 rows each). D stays in the accumulators
+// all 2 l3 + 1 components of both 16-row N tiles. D stays in the accumulators
 // over all paths of the block; each lane then stores 4 consecutive output
 // channels of one (row, m3). fp32 storage: v_mfma_f32_16x16x4_f32 on fp32 T;
 // bf16 storage: v_mfma_f32_16x16x32_bf16 on T rounded to bf16 in LDS.
@@ -69,7 +69,10 @@ struct UvwArgs {
 };
 
 constexpr int kUvwThreads = 512;
-constexpr int kUvwRows = 16;   // rows per workgroup: the MFMA's N tile
+// Rows per workgroup: RT MFMA N tiles of 16 rows (2 for plans up to degree 3,
+// 1 at degree 4, where two tiles' accumulators would spill).
+template <int LM>
+constexpr int uvw_row_tiles() { return LM >= 4 ? 1 : 2; }
 constexpr int kUvwK = 128;     // x channels of one T chunk
 constexpr int kUvwCols = 128;  // output channels per column tile (8 waves x 16)
 
@@ -99,14 +102,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
 template <typename T>
-size_t uvw_lds_bytes(int max_l3) {
+size_t uvw_lds_bytes(int max_l3, int rows) {
   using M = UvwMma<T>;
-  return size_t(2 * max_l3 + 1) * kUvwRows * M::TP * sizeof(typename M::TL);
+  return size_t(2 * max_l3 + 1) * size_t(rows) * M::TP * sizeof(typename M::TL);
 }
 
-// T_p for rows z0..z0+15 and x channels k0..k0+127 into LDS [m3][row][channel]
-// (zeros past u). Lane (zt, rt) takes row zt and the channel quad 4 rt.
-template <typename T, int L1, int L2, int L3>
+// T_p for one row of the workgroup and x channels k0..k0+127 into LDS [m3][row][channel]
+// (zeros past u). The lane takes row zt and the channel quad 4 rt.
+template <typename T, int L1, int L2, int L3, int ROWS>
 __device__ __forceinline__ void uvw_t_chunk(const UvwArgs& a, const UvwPathDev& pd, const T* __restrict__ xr,
                                             const T* __restrict__ yr, int k0, int zt, int rt,
                                             typename UvwMma<T>::TL* tl) {
@@ -127,7 +130,7 @@ __device__ __forceinline__ void uvw_t_chunk(const UvwArgs& a, const UvwPathDev& 
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = ok ? o[m][i] : 0.f;
-      VecIO<T, 4>::store(reinterpret_cast<T*>(tl + (m * kUvwRows + zt) * M::TP + al), v);
+      VecIO<T, 4>::store(reinterpret_cast<T*>(tl + (m * ROWS + zt) * M::TP + al), v);
     }
   }
 }
@@ -154,26 +157,29 @@ __device__ __forceinline__ void uvw_load_w(const T* __restrict__ W, int u, int w
     }
 }
 
-template <typename T, int L3>
+template <typename T, int L3, int RT>
 __device__ __forceinline__ void uvw_mix_chunk(int kn, const typename UvwMma<T>::TL* tl,
                                               const typename UvwMma<T>::AW (&aw)[UvwMma<T>::NK],
-                                              v4f (&acc)[2 * L3 + 1], int li, int lk) {
+                                              v4f (&acc)[RT][2 * L3 + 1], int li, int lk) {
   using M = UvwMma<T>;
 #pragma unroll
   for (int kc = 0; kc < M::NK; ++kc) {
     if (kc * M::KS >= kn) break;  // uniform: past the chunk's channels
 #pragma unroll
-    for (int nt = 0; nt < 2 * L3 + 1; ++nt) {
-      if constexpr (std::is_same<T, bf16>::value) {
-        const bf16x8 b = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u16x8*>(tl + (nt * kUvwRows + li) * M::TP + M::KS * kc + 8 * lk));
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aw[kc]), b, acc[nt], 0, 0, 0);
-      } else {
-        const v4f b = *reinterpret_cast<const v4f*>(tl + (nt * kUvwRows + li) * M::TP + M::KS * kc + 4 * lk);
+    for (int nt = 0; nt < 2 * L3 + 1; ++nt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[kc][j], b[j], acc[nt], 0, 0, 0);
+      for (int rt = 0; rt < RT; ++rt) {
+        const int row = nt * 16 * RT + 16 * rt + li;
+        if constexpr (std::is_same<T, bf16>::value) {
+          const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(tl + row * M::TP + M::KS * kc + 8 * lk));
+          acc[rt][nt] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aw[kc]), b, acc[rt][nt], 0, 0, 0);
+        } else {
+          const v4f b = *reinterpret_cast<const v4f*>(tl + row * M::TP + M::KS * kc + 4 * lk);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[kc][j], b[j], acc[rt][nt], 0, 0, 0);
+        }
       }
-    }
   }
 }
 
@@ -182,17 +188,26 @@ __device__ __forceinline__ void uvw_mix_chunk(int kn, const typename UvwMma<T>::
 template <typename T, int LM>
 __global__ __launch_bounds__(kUvwThreads) void uvw_fwd_kernel(UvwArgs a) {
   using M = UvwMma<T>;
+  constexpr int RT = uvw_row_tiles<LM>(), ROWS = 16 * RT;
   extern __shared__ __attribute__((aligned(16))) unsigned char uvw_smem[];
   typename M::TL* tl = reinterpret_cast<typename M::TL*>(uvw_smem);  // [2 l3 + 1][16 rows][M::TP]
   const int tid = int(threadIdx.x), lane = tid & 63, wave = tid >> 6, li = lane & 15, lk = lane >> 4;
-  const int64_t z0 = int64_t(blockIdx.x) * kUvwRows;
-  const int zt = tid >> 5, rt = tid & 31;
+  const int64_t z0 = int64_t(blockIdx.x) * ROWS;
+  const int zt = tid >> 5, rt = tid & 31;  // T phase: rows zt + 16 r of the workgroup, channel quad rt
   // rows past B compute from the last row; their results are not stored
-  const int64_t rowt = z0 + zt < a.B ? z0 + zt : a.B - 1;
-  const T* __restrict__ xr = static_cast<const T*>(a.x) + rowt * a.dim_x;
-  const T* __restrict__ yr = static_cast<const T*>(a.y) + rowt * a.dim_y;
-  const int64_t row_out = z0 + li;
-  T* __restrict__ orow = static_cast<T*>(a.out) + (row_out < a.B ? row_out : int64_t(0)) * a.dim_out;
+  const T* __restrict__ xr[RT];
+  const T* __restrict__ yr[RT];
+  T* __restrict__ orow[RT];
+  bool out_ok[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int64_t rowt = z0 + zt + 16 * r < a.B ? z0 + zt + 16 * r : a.B - 1;
+    xr[r] = static_cast<const T*>(a.x) + rowt * a.dim_x;
+    yr[r] = static_cast<const T*>(a.y) + rowt * a.dim_y;
+    const int64_t row_out = z0 + 16 * r + li;
+    out_ok[r] = row_out < a.B;
+    orow[r] = static_cast<T*>(a.out) + (out_ok[r] ? row_out : int64_t(0)) * a.dim_out;
+  }
   for (int gi = 0; gi < a.ngroups; ++gi) {
     const UvwGroupDev gd = ldc(a.groups + gi);
     static_for<0, LM + 1>([&](auto L3c) {
@@ -201,9 +216,11 @@ __global__ __launch_bounds__(kUvwThreads) void uvw_fwd_kernel(UvwArgs a) {
       for (int c0 = 0; c0 < gd.w_out; c0 += kUvwCols) {
         const int kout = c0 + 16 * wave + li;
         const bool kok = kout < gd.w_out;
-        v4f acc[2 * L3 + 1];
+        v4f acc[RT][2 * L3 + 1];
 #pragma unroll
-        for (int nt = 0; nt < 2 * L3 + 1; ++nt) acc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+          for (int nt = 0; nt < 2 * L3 + 1; ++nt) acc[r][nt] = v4f{0.f, 0.f, 0.f, 0.f};
         for (int pi = gd.p0; pi < gd.p1; ++pi) {
           const UvwPathDev pd = ldc(a.paths + pi);
           const T* __restrict__ W = static_cast<const T*>(a.w) + pd.w_off;
@@ -216,22 +233,30 @@ __global__ __launch_bounds__(kUvwThreads) void uvw_fwd_kernel(UvwArgs a) {
               static_for<0, LM + 1>([&](auto L2c) {
                 constexpr int L2 = decltype(L2c)::value;
                 if constexpr (L3 >= (L1 > L2 ? L1 - L2 : L2 - L1) && L3 <= L1 + L2) {
-                  if (pd.l1 == L1 && pd.l2 == L2) uvw_t_chunk<T, L1, L2, L3>(a, pd, xr, yr, k0, zt, rt, tl);
+                  if (pd.l1 == L1 && pd.l2 == L2) {
+#pragma unroll
+                    for (int r = 0; r < RT; ++r)
+                      uvw_t_chunk<T, L1, L2, L3, ROWS>(a, pd, xr[r], yr[r], k0, zt + 16 * r, rt, tl);
+                  }
                 }
               });
             });
             __syncthreads();
-            uvw_mix_chunk<T, L3>(pd.u - k0, tl, aw, acc, li, lk);
+            uvw_mix_chunk<T, L3, RT>(pd.u - k0, tl, aw, acc, li, lk);
           }
         }
-        // lane: output channels c0 + 16 wave + 4 lk + r of row z0 + li, component nt
+        // lane: output channels c0 + 16 wave + 4 lk + r of rows z0 + 16 rt + li, component nt
         const int kb = c0 + 16 * wave + 4 * lk;
-        if (row_out < a.B && kb < gd.w_out) {
+        if (kb < gd.w_out) {
 #pragma unroll
-          for (int nt = 0; nt < 2 * L3 + 1; ++nt) {
-            const float o[4] = {acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]};
-            VecIO<T, 4>::store(orow + gd.out_off + nt * gd.w_out + kb, o);
-          }
+          for (int r = 0; r < RT; ++r)
+            if (out_ok[r]) {
+#pragma unroll
+              for (int nt = 0; nt < 2 * L3 + 1; ++nt) {
+                const float o[4] = {acc[r][nt][0], acc[r][nt][1], acc[r][nt][2], acc[r][nt][3]};
+                VecIO<T, 4>::store(orow[r] + gd.out_off + nt * gd.w_out + kb, o);
+              }
+            }
         }
       }
     });
@@ -322,21 +347,25 @@ void uvw_forward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void*
   a.dim_y = int(plan->dim_y);
   a.dim_out = int(plan->dim_out);
   a.ngroups = t.ngroups;
-  const dim3 grid(unsigned((B + kUvwRows - 1) / kUvwRows));
   int lm = plan->lm;
   for (const BlockInfo& b : plan->blocks) lm = std::max(lm, b.l1);
   const bool h = plan->dtype == CGTP_BF16;
-  const size_t lds = h ? uvw_lds_bytes<bf16>(t.max_l3) : uvw_lds_bytes<float>(t.max_l3);
-  if (lm <= 2) {
-    if (h) hipLaunchKernelGGL((uvw_fwd_kernel<bf16, 2>), grid, dim3(kUvwThreads), lds, s, a);
-    else hipLaunchKernelGGL((uvw_fwd_kernel<float, 2>), grid, dim3(kUvwThreads), lds, s, a);
-  } else if (lm == 3) {
-    if (h) hipLaunchKernelGGL((uvw_fwd_kernel<bf16, 3>), grid, dim3(kUvwThreads), lds, s, a);
-    else hipLaunchKernelGGL((uvw_fwd_kernel<float, 3>), grid, dim3(kUvwThreads), lds, s, a);
-  } else {
-    if (h) hipLaunchKernelGGL((uvw_fwd_kernel<bf16, kLmax>), grid, dim3(kUvwThreads), lds, s, a);
-    else hipLaunchKernelGGL((uvw_fwd_kernel<float, kLmax>), grid, dim3(kUvwThreads), lds, s, a);
-  }
+  auto go = [&](auto LMc) {
+    constexpr int LM = decltype(LMc)::value;
+    constexpr int ROWS = 16 * uvw_row_tiles<LM>();
+    const dim3 grid(unsigned((B + ROWS - 1) / ROWS));
+    const size_t lds = h ? uvw_lds_bytes<bf16>(t.max_l3, ROWS) : uvw_lds_bytes<float>(t.max_l3, ROWS);
+    if (h)
+      hipLaunchKernelGGL((uvw_fwd_kernel<bf16, LM>), grid, dim3(kUvwThreads), lds, s, a);
+    else
+      hipLaunchKernelGGL((uvw_fwd_kernel<float, LM>), grid, dim3(kUvwThreads), lds, s, a);
+  };
+  if (lm <= 2)
+    go(std::integral_constant<int, 2>());
+  else if (lm == 3)
+    go(std::integral_constant<int, 3>());
+  else
+    go(std::integral_constant<int, kLmax>());
   CGTP_CHECK_HIP(hipGetLastError());
 }
 
