@@ -157,3 +157,29 @@ def test_water8k_full_size_sampled():
     _, rdY, rdw = otp.backward(L, hx[case.h_src[eidx]], host(Y[ei]), w_e, sc * hg[case.h_dst[eidx]])
     assert_close(host(dY[ei]), rdY, y_blocks(L), "f32", "water8k radial grad_sh")
     assert_close(host(dh[ei]), rdw @ host(W2d).T, [(0, 64)], "f32", "water8k radial grad_h")
+
+
+@pytest.mark.parametrize("ix,iy,io", [
+    ("256x0e+256x1o", "0e+1o+2e", "0e+1o+2e"),                # chunks of 1-2 slots: tiles fit the LDS
+    ("256x1o", "0e+1o+2e", "0e+0o+1e+1o+2e+2o"),              # a chunk of several slots may exceed it
+])
+def test_256_channel_blocks(ix, iy, io):
+    """Blocks of 256 channels: either parity with the oracle or a clean
+    UNSUPPORTED when a slot chunk's two weight tiles and partial sums exceed the
+    device's LDS (the call then writes nothing and raises)."""
+    L = Layout(ix, iy, io)
+    case = Case(synth.uniform_box(24, 5.0, 23), 5.0, 2.4)
+    plan = cgtp.Plan(ix, iy, io)
+    H = 64
+    x = dev(synth.gaussian((case.N, L.dim_x), 3, synth.S_X), "f32")
+    Y = dev(osh.real_sh(2, case.vec), "f32")
+    h = dev(synth.gaussian((case.E, H), 3, synth.S_MLP1), "f32")
+    W2 = dev(synth.gaussian((H, L.w_numel), 3, synth.S_MLP2) / 8.0, "f32")
+    try:
+        out = plan.conv_forward_radial(case.graph, x, Y, h, W2, 0.5)
+    except cgtp.CgtpError as e:
+        assert e.status == 3 and "LDS" in str(e)  # CGTP_ERR_UNSUPPORTED
+        return
+    torch.cuda.synchronize()
+    ref = orad.forward(L, case.h_row, case.h_src, host(x), host(Y), host(h), host(W2), 0.5)
+    assert_close(host(out), ref, out_blocks(L), "f32", "radial forward, 256 channels " + ix)
