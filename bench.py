@@ -898,14 +898,24 @@ def hbm_ceiling(torch):
     """Plain streaming rates of this device, HIP events around torch's own
     kernels: a 4 GiB elementwise copy (4 GiB read + 4 GiB written), a 4 GiB
     fill (write only) and row sums of a [2^20, 1024] view (4 GiB read, 4 MiB
-    written), best of 5."""
+    written); and the tensor product's two row mixes with torch's kernels on
+    2^15 rows: a row repeated 3 times (26.6 KB read, 79.9 KB written per row,
+    the forward's mix) and the sum of a row's 3 thirds (79.9 KB read, 26.6 KB
+    written, the backward's); best of 5."""
     n = 1 << 30
     a = torch.ones(n, device="cuda")
     b = torch.empty_like(a)
+    R, k = 1 << 15, 6656  # 3 k = 19968 floats per row: the tp_large output row
+    xr = a[:R * k].view(R, k)
+    xo = b[:3 * R * k].view(R, 3 * k)
     res = {}
     for key, fn, nbytes in (("copy", lambda: torch.mul(a, 1.0, out=b), 8 * n),
                             ("write", lambda: b.fill_(3.0), 4 * n),
-                            ("read", lambda: a.view(1 << 20, 1024).sum(dim=1), 4 * n + 4 * (1 << 20))):
+                            ("read", lambda: a.view(1 << 20, 1024).sum(dim=1), 4 * n + 4 * (1 << 20)),
+                            ("mix_read1_write3", lambda: xo.view(R, 3, k).copy_(xr.view(R, 1, k).expand(R, 3, k)),
+                             4 * R * k * 4),
+                            ("mix_read3_write1", lambda: torch.sum(xo.view(R, 3, k), dim=1, out=xr),
+                             4 * R * k * 4)):
         fn()
         best = None
         for _ in range(5):
