@@ -41,11 +41,13 @@
 // and largest degree <= 3 ask the allocator for CGTP_TP_BWD_WAVES waves per
 // SIMD (tp_large fp32 backward 27.7 -> 25.6 ms, bf16 23.2 -> 20.0 ms against
 // registers and no request); the others make no request.
-// The one-launch backward with 2-byte storage keeps its registers (no spill)
-// at 2 waves per SIMD: 3 waves spilled 47 VGPRs and were slower (18.5 vs
-// 17.7 ms on tp_large bf16).
+// The one-launch backward with 2-byte storage asks for 3 waves per SIMD when
+// its x degrees are bounded by the largest y/output degree (code for x
+// degree 4 left out at LM = 3: 224 -> 194 VGPRs at 2 waves, 168 with 26
+// spilled at 3 waves; tp_large bf16 17.8 -> 15.9 ms); compiled for every x
+// degree it keeps 2 waves (3 waves spilled 47 VGPRs and were no faster).
 #ifndef CGTP_TP_BWD_WAVES_BF16_ALL
-#define CGTP_TP_BWD_WAVES_BF16_ALL 2
+#define CGTP_TP_BWD_WAVES_BF16_ALL 3
 #endif
 #ifndef CGTP_TP_BWD_DX_LDS
 #define CGTP_TP_BWD_DX_LDS 1
@@ -454,14 +456,16 @@ struct TPBwd {
 };
 
 // (requested only where the spill it costs stays small: largest degree <= 3)
-template <typename T, int L1, int LM>
+template <typename T, int L1, int LM, int MX>
 struct BwdWaves {
-  static constexpr int waves = sizeof(T) == 2 && L1 == -2 ? CGTP_TP_BWD_WAVES_BF16_ALL : CGTP_TP_BWD_WAVES;
+  static constexpr int waves =
+      sizeof(T) == 2 && L1 == -2 ? (MX <= LM ? CGTP_TP_BWD_WAVES_BF16_ALL : 2) : CGTP_TP_BWD_WAVES;
   static constexpr int value = ((L1 >= 0 || L1 == -2) && LM <= 3 && sizeof(T) <= 4 && waves > 1) ? waves : 1;
 };
 
-template <typename T, typename A, int VEC, int L1, int LM>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BwdWaves<T, L1, LM>::value)))
+// MX: largest x degree the one-launch kernels (L1 < 0) hold code for.
+template <typename T, typename A, int VEC, int L1, int LM, int MX = kLmax>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(BwdWaves<T, L1, LM, MX>::value)))
 void tp_bwd_kernel(TPArgs a) {
   extern __shared__ unsigned char smem_raw[];
   A* lds = reinterpret_cast<A*>(smem_raw);  // [dim_y][kBlock], one column per lane
@@ -496,7 +500,7 @@ void tp_bwd_kernel(TPArgs a) {
         for (int b = 0; b < a.nblocks; ++b) {
           const BlockDev blk = ldc(a.blocks + b);
           if (c >= blk.mul) continue;
-          static_for<0, kLmax + 1>([&](auto L1c) {
+          static_for<0, MX + 1>([&](auto L1c) {
             constexpr int D = decltype(L1c)::value;
             if (blk.l1 == D)
               TPBwd<T, A, VEC, LM>::template block<D, L1 == -2 && CGTP_TP_BWD_DX_LDS != 0>(
@@ -611,9 +615,15 @@ void tp_bwd_typed(const TPArgs& a, int l1, int lm, hipStream_t s) {
       return;
     }
     if (l1 == -2) {
+      // code for x degrees up to lm only, when no x block goes beyond it
       static_for<0, kLmax + 1>([&](auto J) {
         constexpr int M = decltype(J)::value;
-        if (lm == M) hipLaunchKernelGGL((tp_bwd_kernel<T, A, VEC, -2, M>), grid, dim3(kBlock), lds, s, a);
+        if (lm == M) {
+          if (a.max_l1 <= M)
+            hipLaunchKernelGGL((tp_bwd_kernel<T, A, VEC, -2, M, M>), grid, dim3(kBlock), lds, s, a);
+          else
+            hipLaunchKernelGGL((tp_bwd_kernel<T, A, VEC, -2, M, kLmax>), grid, dim3(kBlock), lds, s, a);
+        }
       });
       return;
     }

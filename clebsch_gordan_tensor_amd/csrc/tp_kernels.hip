@@ -38,16 +38,18 @@ CGTP_TP_EXTERN_BWD(double, 2)
 #ifndef CGTP_TP_BWD_VEC_BF16
 #define CGTP_TP_BWD_VEC_BF16 4
 #endif
-// Channels per lane of the collapsed-output forward with 4- and 2-byte
-// storage: its accumulators for every output degree stay in registers, and
-// 2 channels keep the kernel at 3-4 waves per SIMD where 4 channels drop
-// it to 1-2.
+// One backward launch over every x block, for collapsed and uncollapsed
+// outputs (1), or one launch per x block (0).
 #ifndef CGTP_TP_BWDC_ALL_BLOCKS
 #define CGTP_TP_BWDC_ALL_BLOCKS 1
 #endif
 #ifndef CGTP_TP_BWD_ALL_BLOCKS
 #define CGTP_TP_BWD_ALL_BLOCKS 1
 #endif
+// Channels per lane of the collapsed-output forward with 4- and 2-byte
+// storage: its accumulators for every output degree stay in registers, and
+// 2 channels keep the kernel at 3-4 waves per SIMD where 4 channels drop
+// it to 1-2.
 #ifndef CGTP_TP_FWDC_VEC
 #define CGTP_TP_FWDC_VEC 2
 #endif
