@@ -273,7 +273,7 @@ __global__ __launch_bounds__(kLinThreads) void lin_rows_bf16_kernel(const bf16* 
                                                                   const bf16* __restrict__ W, bf16* __restrict__ C,
                                                                   int64_t ldcr, int64_t rows,
                                                                   const LinJob* __restrict__ jobs,
-                                                                  const LinTerm* __restrict__ terms) {
+                                                                  const LinTerm* __restrict__ terms, int cvec) {
   __shared__ __attribute__((aligned(16))) uint16_t bt[2][kLinCols * kBTP];
   const LinJob jb = ldc(jobs + blockIdx.y);
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
@@ -320,12 +320,12 @@ __global__ __launch_bounds__(kLinThreads) void lin_rows_bf16_kernel(const bf16* 
           pre[q] = *reinterpret_cast<const u16x8*>(wb + int64_t(ok ? k : 0) * tm.b_sk + int64_t(ok ? n : 0) * tm.b_sn);
         }
       } else {
+        // K is a multiple of 8: the block's 8 rows are all inside or all past it
+        const int k0 = c * kKB + 8 * bk;
+        const bool ok = k0 < tm.K && bn < jb.n_len;
+        const uint16_t* __restrict__ bp = wb + int64_t(ok ? k0 : 0) * tm.b_sk + (ok ? bn : 0);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int k = c * kKB + 8 * bk + r;
-          const bool ok = k < tm.K && bn < jb.n_len;
-          preb[r][0] = *reinterpret_cast<const uint32_t*>(wb + int64_t(ok ? k : 0) * tm.b_sk + (ok ? bn : 0));
-        }
+        for (int r = 0; r < 8; ++r) preb[r][0] = *reinterpret_cast<const uint32_t*>(bp + int64_t(r) * tm.b_sk);
       }
     };
     auto stash = [&](int c, int buf) {
@@ -339,8 +339,9 @@ __global__ __launch_bounds__(kLinThreads) void lin_rows_bf16_kernel(const bf16* 
         }
       } else {
         uint32_t m[8][1];
+        const bool ok = c * kKB + 8 * bk < tm.K && bn < jb.n_len;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) m[r][0] = (c * kKB + 8 * bk + r < tm.K && bn < jb.n_len) ? preb[r][0] : 0u;
+        for (int r = 0; r < 8; ++r) m[r][0] = ok ? preb[r][0] : 0u;
         stash_block<2>(bt[buf], bn, bk, m);
       }
     };
@@ -384,6 +385,32 @@ __global__ __launch_bounds__(kLinThreads) void lin_rows_bf16_kernel(const bf16* 
       for (int s2 = 0; s2 < 2; ++s2) ac[s2] = an[s2];
       __syncthreads();
     }
+  }
+  if (cvec) {
+    // 16-row halves of the wave's tile through LDS (the B chunks are consumed:
+    // every wave passed the chunk loop's last barrier), so each lane stores
+    // 8 consecutive columns of a row with one 16-byte write
+    constexpr int kCP = kLinCols + 8;  // padded row of the staged tile, in elements
+    static_assert((kLinThreads / 64) * 16 * kCP <= 2 * kLinCols * kBTP, "staged tiles fit the B buffers");
+    uint16_t* __restrict__ tile = &bt[0][0] + wave * (16 * kCP);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tile[(4 * lk + r) * kCP + tt * 16 + li] = f32_to_bf16(acc[s][tt][r]);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = lane + 64 * i, row = q >> 4, n = (q & 15) * 8;
+        const int64_t grow = r0 + 16 * s + row;
+        const u16x8 v = *reinterpret_cast<const u16x8*>(tile + row * kCP + n);
+        if (grow < rows && n < jb.n_len)
+          *reinterpret_cast<u16x8*>(reinterpret_cast<uint16_t*>(C) + grow * ldcr + jb.c_off + n) = v;
+      }
+      __syncthreads();
+    }
+    return;
   }
 #pragma unroll
   for (int s = 0; s < 2; ++s)
@@ -579,6 +606,7 @@ struct LinTables {
   int nf = 0, nx = 0, nw = 0;
   bool avec_f = true, avec_x = true;  // 4-aligned A offsets and K (row strides checked per call)
   bool v8_f = true, v8_x = true, v8_w = true;  // offsets and widths multiples of 8 (bf16 matrix-core kernels)
+  bool c8_f = true, c8_x = true;  // output column runs of the row jobs start and end at multiples of 8
 };
 
 std::mutex g_lin_mu;
@@ -617,6 +645,7 @@ const LinTables& lin_tables(const cgtp_linear_s* lin) {
             t.v8_f = t.v8_f && a_off % 8 == 0 && p.mu % 8 == 0 && p.mv % 8 == 0 && p.w_off % 8 == 0;
           }
         j.t1 = int32_t(ft.size());
+        t.c8_f = t.c8_f && j.c_off % 8 == 0 && j.n_len % 8 == 0;
         fj.push_back(j);
       }
   }
@@ -635,6 +664,7 @@ const LinTables& lin_tables(const cgtp_linear_s* lin) {
             t.v8_x = t.v8_x && a_off % 8 == 0 && p.mu % 8 == 0 && p.mv % 8 == 0 && p.w_off % 8 == 0;
           }
         j.t1 = int32_t(xt.size());
+        t.c8_x = t.c8_x && j.c_off % 8 == 0 && j.n_len % 8 == 0;
         xj.push_back(j);
       }
   }
@@ -681,13 +711,16 @@ void rows_launch(const T* A, int64_t lda, const T* W, T* C, int64_t ldc, int64_t
 }
 
 // bf16 with 8-aligned offsets, widths and row strides: the bf16 matrix-core kernel
+// (16-byte output stores when every job's column run and the output rows are
+// 8-aligned)
 bool rows_bf16_mfma(const void* A, int64_t lda, const void* W, void* C, int64_t ldcr, int64_t rows,
-                    const LinJob* jobs, const LinTerm* terms, int njobs, bool v8, hipStream_t s) {
+                    const LinJob* jobs, const LinTerm* terms, int njobs, bool v8, bool c8, hipStream_t s) {
   if (!v8 || lda % 8 != 0 || !aligned16(A, 16) || !aligned16(W, 16) || CGTP_LINEAR_BF16_MFMA == 0) return false;
   if (rows == 0 || njobs == 0) return true;
   const dim3 grid(unsigned((rows + kLinRows - 1) / kLinRows), unsigned(njobs));
+  const int cvec = c8 && ldcr % 8 == 0 && aligned16(C, 16) ? 1 : 0;
   hipLaunchKernelGGL(lin_rows_bf16_kernel, grid, dim3(kLinThreads), 0, s, static_cast<const bf16*>(A), lda,
-                     static_cast<const bf16*>(W), static_cast<bf16*>(C), ldcr, rows, jobs, terms);
+                     static_cast<const bf16*>(W), static_cast<bf16*>(C), ldcr, rows, jobs, terms, cvec);
   CGTP_CHECK_HIP(hipGetLastError());
   return true;
 }
@@ -696,7 +729,7 @@ template <typename T>
 void forward_typed(const cgtp_linear_s* lin, int64_t B, const void* x, const void* w, void* out, hipStream_t s) {
   const LinTables& t = lin_tables(lin);
   if (std::is_same<T, bf16>::value &&
-      rows_bf16_mfma(x, lin->dim_in, w, out, lin->dim_out, B, t.fjobs, t.fterms, t.nf, t.v8_f, s))
+      rows_bf16_mfma(x, lin->dim_in, w, out, lin->dim_out, B, t.fjobs, t.fterms, t.nf, t.v8_f, t.c8_f, s))
     return;
   const bool avec = t.avec_f && lin->dim_in % 4 == 0 && aligned16(x, 4 * sizeof(T));
   rows_launch<T>(static_cast<const T*>(x), lin->dim_in, static_cast<const T*>(w), static_cast<T*>(out), lin->dim_out,
@@ -708,7 +741,7 @@ void backward_typed(const cgtp_linear_s* lin, int64_t B, const void* x, const vo
                     void* dw, void* ws, hipStream_t s) {
   const LinTables& t = lin_tables(lin);
   if (dx && std::is_same<T, bf16>::value &&
-      rows_bf16_mfma(g, lin->dim_out, w, dx, lin->dim_in, B, t.xjobs, t.xterms, t.nx, t.v8_x, s))
+      rows_bf16_mfma(g, lin->dim_out, w, dx, lin->dim_in, B, t.xjobs, t.xterms, t.nx, t.v8_x, t.c8_x, s))
     dx = nullptr;  // done
   if (dx) {
     const bool avec = t.avec_x && lin->dim_out % 4 == 0 && aligned16(g, 4 * sizeof(T));

@@ -85,6 +85,18 @@ def test_irregular_plans(ix, iy, io, shared):
     run_case(ix, iy, io, 77, "f32", shared=shared)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f64"])
+@pytest.mark.parametrize("ix,iy,io", [
+    ("8x3o+8x1e", "0e+1o+2e", "0e+1o+1e+2e+2o"),  # an x degree above the largest y/output degree
+    ("16x0e+16x1o", "0e+1o", "0e+1o+1e"),           # x degrees within it
+])
+def test_backward_x_degree_bound(ix, iy, io, dtype):
+    """The one-launch backward is compiled for x degrees up to the plan's largest
+    y/output degree when no x block goes beyond it, and for every degree
+    otherwise: both kinds, in every storage type, with vectorised channels."""
+    run_case(ix, iy, io, 133, dtype, shared=False)
+
+
 def test_empty_and_single_row():
     c = synth.CONFIGS["tp_large"]
     plan = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"])
