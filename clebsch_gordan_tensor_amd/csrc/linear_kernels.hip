@@ -104,12 +104,12 @@ __global__ __launch_bounds__(kLinThreads) void lin_rows_kernel(const T* __restri
                                                              const T* __restrict__ W, T* __restrict__ C,
                                                              int64_t ldcr, int64_t rows,
                                                              const LinJob* __restrict__ jobs,
-                                                             const LinTerm* __restrict__ terms) {
+                                                             const LinTerm* __restrict__ terms, int njobs) {
   __shared__ float bs[2][kKC * kBP];
-  const LinJob jb = ldc(jobs + blockIdx.y);
+  const LinJob jb = ldc(jobs + blockIdx.x % unsigned(njobs));
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
   const int li = lane & 15, lk = lane >> 4;
-  const int64_t r0 = int64_t(blockIdx.x) * kLinRows + wave * 32;  // two 16-row tiles per wave
+  const int64_t r0 = int64_t(blockIdx.x / unsigned(njobs)) * kLinRows + wave * 32;  // two 16-row tiles per wave
   int64_t arow[2];
   bool row_ok[2];
 #pragma unroll
@@ -269,22 +269,32 @@ __device__ __forceinline__ void stash_block(uint16_t* __restrict__ T, int n0, in
   }
 }
 
-__global__ __launch_bounds__(kLinThreads) void lin_rows_bf16_kernel(const bf16* __restrict__ A, int64_t lda,
+// One workgroup = 128 rows (4 waves x 32) x the 128 output columns of one job.
+// The contraction runs in super-chunks of kSC B chunks (128 k): every global
+// load of a super-chunk (the lane's A runs and its share of the B chunks) is
+// issued before any is used, so with K <= 128 a workgroup waits for one
+// memory round trip, not one per chunk (the kernel is latency-bound: few
+// MFMAs per byte).
+constexpr int kSC = 4;  // B chunks per super-chunk
+
+__global__ __launch_bounds__(kLinThreads) __attribute__((amdgpu_waves_per_eu(3))) void lin_rows_bf16_kernel(const bf16* __restrict__ A, int64_t lda,
                                                                   const bf16* __restrict__ W, bf16* __restrict__ C,
                                                                   int64_t ldcr, int64_t rows,
                                                                   const LinJob* __restrict__ jobs,
-                                                                  const LinTerm* __restrict__ terms, int cvec) {
-  __shared__ __attribute__((aligned(16))) uint16_t bt[2][kLinCols * kBTP];
-  const LinJob jb = ldc(jobs + blockIdx.y);
+                                                                  const LinTerm* __restrict__ terms, int njobs,
+                                                                  int cvec) {
+  __shared__ __attribute__((aligned(16))) uint16_t bt[kSC][kLinCols * kBTP];
+  const LinJob jb = ldc(jobs + blockIdx.x % unsigned(njobs));
   const int lane = int(threadIdx.x & 63), wave = int(threadIdx.x >> 6);
   const int li = lane & 15, lk = lane >> 4;
-  const int64_t r0 = int64_t(blockIdx.x) * kLinRows + wave * 32;  // two 16-row tiles per wave
-  int64_t arow[2];
-  bool row_ok[2];
+  const int64_t r0 = int64_t(blockIdx.x / unsigned(njobs)) * kLinRows + wave * 32;  // two 16-row tiles per wave
+  // this lane's two A rows (rows past the end read row 0; their results are
+  // not stored)
+  const uint16_t* arp[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    arow[s] = r0 + 16 * s + li;
-    row_ok[s] = arow[s] < rows;
+    const int64_t ar = r0 + 16 * s + li;
+    arp[s] = reinterpret_cast<const uint16_t*>(A) + (ar < rows ? ar : int64_t(0)) * lda;
   }
   v4f acc[2][8];
 #pragma unroll
@@ -292,107 +302,91 @@ __global__ __launch_bounds__(kLinThreads) void lin_rows_bf16_kernel(const bf16* 
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[s][t] = v4f{0.f, 0.f, 0.f, 0.f};
   const u16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int bn = 2 * (int(threadIdx.x) & 63), bk = int(threadIdx.x) >> 6;  // runs along n: block origin
   for (int t = jb.t0; t < jb.t1; ++t) {
     const LinTerm tm = ldc(terms + t);
     const uint16_t* __restrict__ wb =
         reinterpret_cast<const uint16_t*>(W) + tm.b_off + int64_t(jb.b_n0) * tm.b_sn;
     const bool kfast = tm.b_sk == 1;  // transposed weights: runs of 8 along k
-    const int nch = (tm.K + kKB - 1) / kKB;
-    // B chunk, 32 x 128: with runs along k (transposed weights), 512 runs of
-    // 8 elements, two per thread, stored as they are; with runs along n, one
-    // 8 (k) x 2 (n) block per thread, transposed on the way into LDS. Requests
-    // go out unconditionally from clamped addresses and are masked when stashed.
-    u16x8 pre[2];
-    uint32_t preb[8][1];
-    auto unit = [&](int q, int c, int& n, int& k) {  // runs along k
-      const int u = int(threadIdx.x) + q * kLinThreads;
-      n = u >> 2;
-      k = c * kKB + (u & 3) * 8;
-    };
-    const int bn = 2 * (int(threadIdx.x) & 63), bk = int(threadIdx.x) >> 6;  // runs along n: block origin
-    auto fetch = [&](int c) {
-      if (kfast) {
+    for (int kb = 0; kb < tm.K; kb += kSC * kKB) {
+      // Requests, unconditional from clamped addresses (masked when used or
+      // stashed). A: 8 consecutive k of each of the lane's two rows per chunk
+      // (K is a multiple of 8, so a run is wholly inside or past K). B chunk,
+      // 32 x 128: with runs along k (transposed weights), 512 runs of 8, two
+      // per thread, stored as they are; with runs along n, one 8 (k) x 2 (n)
+      // block per thread, transposed on the way into LDS.
+      u16x8 a[kSC][2];
+      uint32_t wv[kSC][8];  // the thread's B values of each chunk, as loaded (either layout)
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          int n, k;
-          unit(q, c, n, k);
-          const bool ok = k < tm.K && n < jb.n_len;
-          pre[q] = *reinterpret_cast<const u16x8*>(wb + int64_t(ok ? k : 0) * tm.b_sk + int64_t(ok ? n : 0) * tm.b_sn);
-        }
-      } else {
-        // K is a multiple of 8: the block's 8 rows are all inside or all past it
-        const int k0 = c * kKB + 8 * bk;
-        const bool ok = k0 < tm.K && bn < jb.n_len;
-        const uint16_t* __restrict__ bp = wb + int64_t(ok ? k0 : 0) * tm.b_sk + (ok ? bn : 0);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) preb[r][0] = *reinterpret_cast<const uint32_t*>(bp + int64_t(r) * tm.b_sk);
-      }
-    };
-    auto stash = [&](int c, int buf) {
-      if (kfast) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          int n, k;
-          unit(q, c, n, k);
-          const u16x8 v = (k < tm.K && n < jb.n_len) ? pre[q] : zero8;
-          *reinterpret_cast<u16x8*>(&bt[buf][tile_run(n, (k - c * kKB) >> 3)]) = v;
-        }
-      } else {
-        uint32_t m[8][1];
-        const bool ok = c * kKB + 8 * bk < tm.K && bn < jb.n_len;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) m[r][0] = ok ? preb[r][0] : 0u;
-        stash_block<2>(bt[buf], bn, bk, m);
-      }
-    };
-    // this lane's 8 consecutive k of each of its two rows (K is a multiple of
-    // 8, so a run is wholly inside or past K; rows past the end read row 0,
-    // whose results are not stored)
-    auto load_a = [&](int c, u16x8 (&a)[2]) {
-      const int ka = c * kKB + 8 * lk;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const uint16_t* __restrict__ ar =
-            reinterpret_cast<const uint16_t*>(A) + (row_ok[s2] ? arow[s2] : int64_t(0)) * lda + tm.a_off;
-        a[s2] = *reinterpret_cast<const u16x8*>(ar + (ka < tm.K ? ka : 0));
-      }
-    };
-    __syncthreads();  // the previous term's last chunk is consumed
-    u16x8 ac[2], an[2];
-    fetch(0);
-    load_a(0, ac);
-    stash(0, 0);
-    __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-      fetch(c + 1);
-      load_a(c + 1, an);
-      __builtin_amdgcn_sched_barrier(0);  // keep the requests ahead of the MFMAs
-      const uint16_t* __restrict__ bc = bt[c & 1];
-      const bool kin = c * kKB + 8 * lk < tm.K;
-      bf16x8 av[2];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) av[s2] = __builtin_bit_cast(bf16x8, kin ? ac[s2] : zero8);
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(bc + tile_run(tt * 16 + li, lk)));
+      for (int c = 0; c < kSC; ++c) {
+        const int ka = kb + c * kKB + 8 * lk;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
-          acc[s2][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s2], bv, acc[s2][tt], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // the requests complete behind the MFMAs
-      stash(c + 1, (c + 1) & 1);
+          a[c][s2] = *reinterpret_cast<const u16x8*>(arp[s2] + tm.a_off + (ka < tm.K ? ka : 0));
+        if (kfast) {
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) ac[s2] = an[s2];
+          for (int q = 0; q < 2; ++q) {
+            const int u = int(threadIdx.x) + q * kLinThreads, n = u >> 2, k = kb + c * kKB + (u & 3) * 8;
+            const bool ok = k < tm.K && n < jb.n_len;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(wb + (ok ? k : 0) + int64_t(ok ? n : 0) * tm.b_sn);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wv[c][4 * q + j] = v[j];
+          }
+        } else {
+          const int k0 = kb + c * kKB + 8 * bk;
+          const bool ok = k0 < tm.K && bn < jb.n_len;
+          const uint16_t* __restrict__ bp = wb + int64_t(ok ? k0 : 0) * tm.b_sk + (ok ? bn : 0);
+#pragma unroll
+          for (int r = 0; r < 8; ++r) wv[c][r] = *reinterpret_cast<const uint32_t*>(bp + int64_t(r) * tm.b_sk);
+        }
+      }
+      __syncthreads();  // the previous super-chunk's B tiles are consumed
+#pragma unroll
+      for (int c = 0; c < kSC; ++c) {
+        if (kfast) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int u = int(threadIdx.x) + q * kLinThreads, n = u >> 2, k = kb + c * kKB + (u & 3) * 8;
+            const bool ok = k < tm.K && n < jb.n_len;
+            u32x4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = ok ? wv[c][4 * q + j] : 0u;
+            *reinterpret_cast<u32x4*>(&bt[c][tile_run(n, u & 3)]) = v;
+          }
+        } else {
+          uint32_t m[8][1];
+          const bool ok = kb + c * kKB + 8 * bk < tm.K && bn < jb.n_len;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) m[r][0] = ok ? wv[c][r] : 0u;
+          stash_block<2>(bt[c], bn, bk, m);
+        }
+      }
       __syncthreads();
+#pragma unroll
+      for (int c = 0; c < kSC; ++c) {
+        if (kb + c * kKB >= tm.K) break;  // uniform: chunks past K
+        const bool kin = kb + c * kKB + 8 * lk < tm.K;
+        bf16x8 av[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) av[s2] = __builtin_bit_cast(bf16x8, kin ? a[c][s2] : zero8);
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+          const bf16x8 bv =
+              __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(&bt[c][tile_run(tt * 16 + li, lk)]));
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+            acc[s2][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s2], bv, acc[s2][tt], 0, 0, 0);
+        }
+      }
     }
   }
   if (cvec) {
-    // 16-row halves of the wave's tile through LDS (the B chunks are consumed:
-    // every wave passed the chunk loop's last barrier), so each lane stores
-    // 8 consecutive columns of a row with one 16-byte write
+    // 16-row halves of the wave's tile through LDS, so each lane stores 8
+    // consecutive columns of a row with one 16-byte write
     constexpr int kCP = kLinCols + 8;  // padded row of the staged tile, in elements
-    static_assert((kLinThreads / 64) * 16 * kCP <= 2 * kLinCols * kBTP, "staged tiles fit the B buffers");
+    static_assert((kLinThreads / 64) * 16 * kCP <= kSC * kLinCols * kBTP, "staged tiles fit the B buffers");
     uint16_t* __restrict__ tile = &bt[0][0] + wave * (16 * kCP);
+    __syncthreads();  // every wave's MFMAs have read their last B tile
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -696,17 +690,27 @@ int64_t dw_rows_per_chunk(int64_t B) {
 }
 int64_t dw_chunks(int64_t B) { return B == 0 ? 0 : (B + dw_rows_per_chunk(B) - 1) / dw_rows_per_chunk(B); }
 
+// Workgroups of the row kernels take (row tile, job) with the job fastest: the
+// jobs of one row tile run side by side, so each tile's rows are read and
+// written whole (every job covers one slice of a row) while their DRAM pages
+// are open, rather than one slice per row across the whole matrix at a time.
+dim3 rows_grid(int64_t rows, int njobs) {
+  const int64_t n = (rows + kLinRows - 1) / kLinRows * int64_t(njobs);
+  if (n > int64_t(UINT32_MAX)) throw Error{CGTP_ERR_UNSUPPORTED, "linear map: too many rows for one launch"};
+  return dim3(unsigned(n));
+}
+
 template <typename T>
 void rows_launch(const T* A, int64_t lda, const T* W, T* C, int64_t ldc, int64_t rows, const LinJob* jobs,
                  const LinTerm* terms, int njobs, bool avec, hipStream_t s) {
   if (rows == 0 || njobs == 0) return;
-  const dim3 grid(unsigned((rows + kLinRows - 1) / kLinRows), unsigned(njobs));
+  const dim3 grid = rows_grid(rows, njobs);
   if (avec)
     hipLaunchKernelGGL((lin_rows_kernel<T, true>), grid, dim3(kLinThreads), 0, s, A, lda, W, C, ldc, rows, jobs,
-                       terms);
+                       terms, njobs);
   else
     hipLaunchKernelGGL((lin_rows_kernel<T, false>), grid, dim3(kLinThreads), 0, s, A, lda, W, C, ldc, rows, jobs,
-                       terms);
+                       terms, njobs);
   CGTP_CHECK_HIP(hipGetLastError());
 }
 
@@ -717,10 +721,10 @@ bool rows_bf16_mfma(const void* A, int64_t lda, const void* W, void* C, int64_t 
                     const LinJob* jobs, const LinTerm* terms, int njobs, bool v8, bool c8, hipStream_t s) {
   if (!v8 || lda % 8 != 0 || !aligned16(A, 16) || !aligned16(W, 16) || CGTP_LINEAR_BF16_MFMA == 0) return false;
   if (rows == 0 || njobs == 0) return true;
-  const dim3 grid(unsigned((rows + kLinRows - 1) / kLinRows), unsigned(njobs));
+  const dim3 grid = rows_grid(rows, njobs);
   const int cvec = c8 && ldcr % 8 == 0 && aligned16(C, 16) ? 1 : 0;
   hipLaunchKernelGGL(lin_rows_bf16_kernel, grid, dim3(kLinThreads), 0, s, static_cast<const bf16*>(A), lda,
-                     static_cast<const bf16*>(W), static_cast<bf16*>(C), ldcr, rows, jobs, terms, cvec);
+                     static_cast<const bf16*>(W), static_cast<bf16*>(C), ldcr, rows, jobs, terms, njobs, cvec);
   CGTP_CHECK_HIP(hipGetLastError());
   return true;
 }
