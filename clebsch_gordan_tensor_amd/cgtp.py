@@ -20,7 +20,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 F32, F64, BF16 = 0, 1, 2
 W_SHARED, W_PER_ROW = 0, 1
-OP_TP_BACKWARD, OP_CONV_BACKWARD, OP_TP_DOUBLE_BACKWARD, OP_CONV_DOUBLE_BACKWARD = 1, 2, 3, 4
+OP_TP_BACKWARD, OP_CONV_BACKWARD, OP_TP_DOUBLE_BACKWARD, OP_CONV_DOUBLE_BACKWARD, OP_CONV_FORWARD = 1, 2, 3, 4, 5
 LMAX = 4
 
 _c_i64 = ctypes.c_int64
@@ -50,6 +50,8 @@ _SIGS = {
     "cgtp_graph_destroy": ([_vp], ctypes.c_int),
     "cgtp_graph_transpose": ([_vp, _vp, _vp, _vp], ctypes.c_int),
     "cgtp_conv_forward": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_double, _vp, _vp], ctypes.c_int),
+    "cgtp_conv_forward_ws": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_double, _vp, _vp, ctypes.c_size_t, _vp],
+                             ctypes.c_int),
     "cgtp_tp_double_backward": ([_vp, _c_i64] + [_vp] * 12 + [ctypes.c_size_t, _vp], ctypes.c_int),
     "cgtp_conv_double_backward": ([_vp, _vp, _vp, _vp, _vp, ctypes.c_double] + [_vp] * 9 + [ctypes.c_size_t, _vp],
                                   ctypes.c_int),
@@ -273,7 +275,10 @@ class Plan:
         return tuple(res)
 
     # -------------------------------------------------------------- convolution
-    def conv_forward(self, graph, x, sh, w, scale, out=None):
+    def conv_forward(self, graph, x, sh, w, scale, out=None, ws=None, fp32_running_sum=True):
+        """cgtp_conv_forward_ws; for collapsed bf16 plans a workspace for the fp32
+        running sum over x blocks is allocated unless ``fp32_running_sum`` is False
+        (then the sum is rounded to bf16 after every x block, as cgtp_conv_forward)."""
         torch = _torch()
         dt = self.torch_dtype
         _need(x, (graph.N, self.dim_x), dt, "x")
@@ -282,8 +287,13 @@ class Plan:
         if out is None:
             out = torch.empty((graph.N, self.dim_out), dtype=dt, device=x.device)
         _need(out, (graph.N, self.dim_out), dt, "out")
-        _check(_lib.cgtp_conv_forward(self._h, graph._h, _ptr(x), _ptr(sh), _ptr(w), float(scale),
-                                      _ptr(out), _stream(x)), "cgtp_conv_forward")
+        if ws is None and fp32_running_sum:
+            nws = self.workspace_size(OP_CONV_FORWARD, graph=graph)
+            if nws:
+                ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
+        _check(_lib.cgtp_conv_forward_ws(self._h, graph._h, _ptr(x), _ptr(sh), _ptr(w), float(scale), _ptr(out),
+                                         _ptr(ws) if ws is not None else _vp(0),
+                                         _ws_bytes(ws) if ws is not None else 0, _stream(x)), "cgtp_conv_forward_ws")
         return out
 
     def _double_outputs(self, shapes, need, out, dt, device):
@@ -356,8 +366,10 @@ class Plan:
                 continue
             t = out[k] if out[k] is not None else torch.empty(shapes[k], dtype=dt, device=x.device)
             res.append(_need(t, shapes[k], dt, "grad"))
-        nws = self.workspace_size(OP_CONV_BACKWARD, graph=graph) if need[0] else 0
-        if nws and ws is None:
+        nws = self.workspace_size(OP_CONV_BACKWARD, graph=graph) if (need[0] or need[1]) else 0
+        if ws is not None:
+            nws = _ws_bytes(ws)
+        elif nws:
             ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
         _check(_lib.cgtp_conv_backward(self._h, graph._h, _ptr(x), _ptr(sh), _ptr(w), float(scale),
                                        _ptr(grad_out), _ptr(res[0]), _ptr(res[1]), _ptr(res[2]),

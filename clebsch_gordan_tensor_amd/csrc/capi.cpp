@@ -245,6 +245,10 @@ cgtp_status cgtp_workspace_size(cgtp_plan plan, cgtp_graph graph, int64_t B, int
       *bytes = plan->mode == 1       ? uvw_backward_ws_bytes(plan, B)
                : plan->max_ymul > 1 ? uvuv_backward_ws_bytes(plan, B)
                                     : tp_backward_ws_bytes(plan, B);
+    } else if (op == CGTP_OP_CONV_FORWARD) {
+      need(graph != nullptr, "graph is NULL");
+      need_plain_uvu(plan, "the convolution");
+      *bytes = conv_forward_ws_bytes(plan, graph);
     } else if (op == CGTP_OP_CONV_BACKWARD) {
       need(graph != nullptr, "graph is NULL");
       need_plain_uvu(plan, "the convolution");
@@ -316,6 +320,12 @@ cgtp_status cgtp_graph_transpose(cgtp_graph graph, int32_t* col_ptr, int32_t* ei
 
 cgtp_status cgtp_conv_forward(cgtp_plan plan, cgtp_graph graph, const void* x, const void* sh,
                               const void* w, double scale, void* out, void* stream) {
+  return cgtp_conv_forward_ws(plan, graph, x, sh, w, scale, out, nullptr, 0, stream);
+}
+
+cgtp_status cgtp_conv_forward_ws(cgtp_plan plan, cgtp_graph graph, const void* x, const void* sh,
+                                 const void* w, double scale, void* out, void* ws, size_t ws_bytes,
+                                 void* stream) {
   return guarded([&] {
     need(plan != nullptr && graph != nullptr, "NULL plan or graph");
     need_plain_uvu(plan, "the convolution");
@@ -324,7 +334,14 @@ cgtp_status cgtp_conv_forward(cgtp_plan plan, cgtp_graph graph, const void* x, c
     if (graph->N == 0) return;
     need(out != nullptr, "out is NULL");
     need(graph->E == 0 || (x && sh && w), "NULL input tensor");
-    conv_forward_launch(plan, graph, x, sh, w, scale, out, as_stream(stream));
+    if (ws) {
+      const size_t nws = conv_forward_ws_bytes(plan, graph);
+      if (ws_bytes < nws)
+        throw Error{CGTP_ERR_WORKSPACE, "conv_forward needs " + std::to_string(nws) + " workspace bytes"};
+      if (reinterpret_cast<uintptr_t>(ws) % 16 != 0)
+        throw Error{CGTP_ERR_INVALID_ARG, "the workspace must be 16-byte aligned"};
+    }
+    conv_forward_launch(plan, graph, x, sh, w, scale, out, as_stream(stream), ws, ws_bytes);
   });
 }
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <functional>
 #include <map>
 #include <mutex>
 #include <string>
@@ -135,6 +136,19 @@ std::vector<double> real_cg_ladder(int l1, int l2, int l3);
 // Device tables of a plan on the current device (uploaded on first use).
 const DevTables& plan_tables(cgtp_plan_s* plan);
 void free_plan_tables(cgtp_plan_s* plan);
+
+// Launches of one call that write disjoint memory, run side by side: f(i, st)
+// is called for i in [0, n) with st = s for i = 0 and a library-owned stream
+// of the current device (default priority) for the others; those streams
+// first wait for the work queued on s before the call, and s waits for them
+// afterwards, so the call stays ordered on s (and capturable: the fork and
+// join are event waits). The side streams are created with a plan's first
+// device tables on a device. fork = false runs every f(i, s) on s in order:
+// the fork and join cost about 10-20 us, more than small calls gain.
+constexpr int kSideStreams = 3;
+constexpr double kSideMinBytes = 256.0 * (1 << 20);  // calls that move less stay on s
+void side_run(hipStream_t s, int n, const std::function<void(int, hipStream_t)>& f, bool fork = true);
+void side_streams_init();
 
 inline size_t dtype_size(cgtp_dtype d) { return d == CGTP_F64 ? 8 : (d == CGTP_BF16 ? 2 : 4); }
 inline size_t acc_size(cgtp_dtype d) { return d == CGTP_F64 ? 8 : 4; }

@@ -145,6 +145,8 @@ struct ConvArgs {
   int block;    // x block of a degree-specialised launch
   int lg_log2;  // lanes per edge group (fused forward)
   int collapse; // outputs collapsed by (l3, p3): add into the (zeroed) output instead of storing
+  void* acc;    // collapsed outputs: running sum [N][dim_out] in the accumulation type that the
+                // x blocks add into instead of the output (NULL: the output itself)
   int coef_zero;  // offset of a run of zero coefficients (one whole pattern) in the table
   int pad;        // padding node (its incoming edges are skipped) or -1
   int yoff[kLmax + 1];
@@ -351,13 +353,21 @@ __device__ __forceinline__ void fwd_fused_chunk(const ConvArgs& a, int64_t n, co
       });
       if (path >= 0) {
         const PathDev pd = ldc(a.paths + path);
+        A* __restrict__ accn = a.acc ? static_cast<A*>(a.acc) + n * a.dim_out : nullptr;
 #pragma unroll
         for (int m = 0; m < 2 * st.l3 + 1; ++m) {
           A o[VEC], prev[VEC];
-          VecIO<T, VEC>::load(outn + pd.out_off + m * pd.mul + c, prev);
+          const int off = pd.out_off + m * pd.mul + c;
+          if (accn)
+            VecIO<A, VEC>::load(accn + off, prev);
+          else
+            VecIO<T, VEC>::load(outn + off, prev);
 #pragma unroll
           for (int v = 0; v < VEC; ++v) o[v] = prev[v] + sc * acc[st.acc - acc0 + m][v];
-          VecIO<T, VEC>::store(outn + pd.out_off + m * pd.mul + c, o);
+          if (accn)
+            VecIO<A, VEC>::store(accn + off, o);
+          else
+            VecIO<T, VEC>::store(outn + off, o);
         }
       }
     }
@@ -435,12 +445,18 @@ __device__ __forceinline__ void fwd_general_path(const ConvArgs& a, int64_t n, c
     for (int m = 0; m < 2 * L3 + 1; ++m) acc[m] = fma(wv, t[m][0], acc[m]);
   }
   T* __restrict__ outn = static_cast<T*>(a.out) + n * a.dim_out;
+  A* __restrict__ accn = a.acc ? static_cast<A*>(a.acc) + n * a.dim_out : nullptr;
   const A sc = A(a.scale);
 #pragma unroll
   for (int m = 0; m < 2 * L3 + 1; ++m) {
+    const int off = pd.out_off + m * pd.mul + c;
     A o = sc * acc[m];
-    if (a.collapse) o += to_acc<A>(outn[pd.out_off + m * pd.mul + c]);
-    from_acc(outn[pd.out_off + m * pd.mul + c], o);
+    if (accn) {
+      accn[off] += o;
+    } else {
+      if (a.collapse) o += to_acc<A>(outn[off]);
+      from_acc(outn[off], o);
+    }
   }
 }
 
@@ -492,6 +508,7 @@ struct ConvBwdArgs {
   void* dw;       // grad_w [E][W]
   void* dxp;      // grad_x partials [E][dim_x], accumulation type
   int dy_accum;
+  int dsh_acc;    // dsh is this x block's own [E][dim_y] in the accumulation type
 };
 
 // One workgroup = (receiver n, x block b, channel chunk). The block's slice
@@ -689,7 +706,10 @@ void conv_bwd_fused_kernel(ConvArgs a, ConvBwdArgs bw) {
     }
     // the batch's grad_sh rows leave in one coalesced pass
     __syncthreads();
-    if (bw.dsh) {
+    if (bw.dsh && bw.dsh_acc) {
+      A* __restrict__ dsb = static_cast<A*>(bw.dsh) + int64_t(base) * a.dim_y;
+      for (int t = threadIdx.x; t < nb * a.dim_y; t += kBlock) dsb[t] = dsl[t];
+    } else if (bw.dsh) {
       T* __restrict__ dsb = static_cast<T*>(bw.dsh) + int64_t(base) * a.dim_y;
       for (int t = threadIdx.x; t < nb * a.dim_y; t += kBlock) from_acc(dsb[t], dsl[t]);
     }

@@ -1,4 +1,5 @@
 // Launchers of the message-passing convolution (kernels in conv_impl.hpp).
+#include <algorithm>
 #include <vector>
 
 #include "conv_impl.hpp"
@@ -50,6 +51,29 @@ __global__ __launch_bounds__(kBlock) void dx_gather_kernel(const int32_t* __rest
   VecIO<T, V>::store(dx + n * dim_x + k, s);
 }
 
+// grad_sh[i] = sum over x blocks k = 0, 1, ... of part[k][i], added in that
+// order (the order in which the x-block launches would accumulate it in place).
+template <typename T, typename A>
+__global__ __launch_bounds__(kBlock) void dsh_sum_kernel(const A* __restrict__ part, T* __restrict__ dsh, int64_t n,
+                                                         int nb) {
+  const int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+  if (i >= n) return;
+  A v = part[i];
+  for (int k = 1; k < nb; ++k) v += part[int64_t(k) * n + i];
+  from_acc(dsh[i], v);
+}
+
+template <typename T>
+void dsh_sum(const void* part, void* dsh, int64_t n, int nb, hipStream_t s) {
+  using A = typename AccOf<T>::type;
+  const unsigned grid = unsigned((n + kBlock - 1) / kBlock);
+  hipLaunchKernelGGL((dsh_sum_kernel<T, A>), dim3(grid), dim3(kBlock), 0, s, static_cast<const A*>(part),
+                     static_cast<T*>(dsh), n, nb);
+  CGTP_CHECK_HIP(hipGetLastError());
+}
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
 ConvArgs make_conv_args(cgtp_plan_s* plan, const DevTables& t, const cgtp_graph_s* g) {
   ConvArgs a{};
   a.paths = t.paths;
@@ -77,37 +101,85 @@ ConvArgs make_conv_args(cgtp_plan_s* plan, const DevTables& t, const cgtp_graph_
 
 bool aligned_to(const void* p, size_t bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
 
+// out[i] = acc[i] rounded to the storage type (one rounding of the running sum).
+template <typename T, typename A>
+__global__ __launch_bounds__(kBlock) void acc_store_kernel(const A* __restrict__ acc, T* __restrict__ out, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+  if (i < n) from_acc(out[i], acc[i]);
+}
+
 template <typename T>
-void fwd_typed(cgtp_plan_s* plan, ConvArgs a, hipStream_t s) {
+void fwd_launches(cgtp_plan_s* plan, ConvArgs a, bool big, hipStream_t s);
+
+// Edge-tensor bytes of one call (weights and harmonics): calls below
+// kSideMinBytes keep their x-block launches on the caller's stream.
+double conv_edge_bytes(const cgtp_plan_s* plan, const cgtp_graph_s* g) {
+  return double(g->E) * double(plan->w_numel + plan->dim_y) * double(dtype_size(plan->dtype));
+}
+
+template <typename T>
+void fwd_typed(cgtp_plan_s* plan, ConvArgs a, void* acc_ws, bool big, hipStream_t s) {
+  using A = typename AccOf<T>::type;
+  const int64_t nout = a.N * int64_t(a.dim_out);
+  if (plan->collapse) {  // the kernels add into the output, or into an accumulation-type running sum
+    a.collapse = 1;
+    a.acc = acc_ws;
+    if (a.acc)
+      zero_rows(a.acc, nout, sizeof(A), s);
+    else
+      zero_rows(a.out, nout, dtype_size(plan->dtype), s);
+  }
+  fwd_launches<T>(plan, a, big, s);
+  if (a.acc && nout > 0) {  // the running sum leaves rounded once, after every x block added into it
+    hipLaunchKernelGGL((acc_store_kernel<T, A>), dim3(unsigned((nout + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
+                       static_cast<const A*>(a.acc), static_cast<T*>(a.out), nout);
+    CGTP_CHECK_HIP(hipGetLastError());
+  }
+}
+
+template <typename T>
+void fwd_launches(cgtp_plan_s* plan, ConvArgs a, bool big, hipStream_t s) {
   const size_t vb = size_t(conv_vec(plan->dtype)) * dtype_size(plan->dtype);
   const bool fused = plan->conv_fused && (!plan->collapse || plan->conv_col_fused) &&
                      plan->vec == conv_vec(plan->dtype) && aligned_to(a.x, vb) && aligned_to(a.w, vb) &&
                      aligned_to(a.out, vb);
-  if (plan->collapse) {  // the kernels add into the output
-    zero_rows(a.out, a.N * int64_t(a.dim_out), dtype_size(plan->dtype), s);
-    a.collapse = 1;
-  }
   if (!fused) {
     const int64_t items = a.N * int64_t(a.collapse ? 1 : a.npaths) * a.nchunks;
     conv_fwd_general_typed<T>(a, dim3(unsigned((items + kWaves - 1) / kWaves)), s);
     CGTP_CHECK_HIP(hipGetLastError());
     return;
   }
-  // one launch per x block, specialised for its degree and the plan's largest degree
+  // One launch per x block, specialised for its degree and the plan's largest
+  // degree. Without collapse the blocks write disjoint output columns, so
+  // their launches run side by side (the memory-bound small degrees beside the
+  // ALU-bound large ones), the largest degree first; collapsed blocks add into
+  // shared output blocks in block order on s.
   const int VEC = conv_vec(plan->dtype);
-  for (size_t b = 0; b < plan->blocks.size(); ++b) {
+  const int nb = int(plan->blocks.size());
+  std::vector<int> order(nb);
+  for (int b = 0; b < nb; ++b) order[b] = b;
+  if (!a.collapse)
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int i, int j) { return plan->blocks[i].l1 > plan->blocks[j].l1; });
+  auto launch = [&](int i, hipStream_t st) {
+    const int b = order[i];
     const BlockInfo& blk = plan->blocks[b];
     const int lanes = (blk.mul + VEC - 1) / VEC;
     int lg = 0;
     while ((1 << lg) < lanes && lg < 6) ++lg;
-    a.block = int(b);
-    a.lg_log2 = lg;
-    a.nchunks = (lanes + (1 << lg) - 1) >> lg;
-    const int nch = conv_fused_chunks<T>(blk.l1, plan->conv_L, a.collapse != 0);
-    const int64_t items = a.N * int64_t(nch) * a.nchunks;
-    conv_fwd_fused_typed<T>(a, blk.l1, plan->conv_L, dim3(unsigned((items + kWaves - 1) / kWaves)), s);
+    ConvArgs ab = a;
+    ab.block = b;
+    ab.lg_log2 = lg;
+    ab.nchunks = (lanes + (1 << lg) - 1) >> lg;
+    const int nch = conv_fused_chunks<T>(blk.l1, plan->conv_L, ab.collapse != 0);
+    const int64_t items = ab.N * int64_t(nch) * ab.nchunks;
+    conv_fwd_fused_typed<T>(ab, blk.l1, plan->conv_L, dim3(unsigned((items + kWaves - 1) / kWaves)), st);
     CGTP_CHECK_HIP(hipGetLastError());
-  }
+  };
+  if (a.collapse)
+    for (int i = 0; i < nb; ++i) launch(i, s);
+  else
+    side_run(s, nb, launch, big);
 }
 
 template <typename T>
@@ -138,7 +210,7 @@ void bwd_fused_typed(const ConvArgs& a, const ConvBwdArgs& b, int l1, int L, dim
 // not fit it (then the row-parallel backward over gathered rows is used).
 bool conv_backward_fused(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x, const void* sh,
                          const void* w, double scale, const void* grad_out, void* grad_x, void* grad_sh,
-                         void* grad_w, void* ws, hipStream_t s) {
+                         void* grad_w, void* ws, size_t ws_bytes, hipStream_t s) {
   const int VEC = plan->dtype == CGTP_F64 ? 2 : CGTP_CONV_BWD_VEC;
   const size_t vb = size_t(VEC) * dtype_size(plan->dtype);
   if (!plan->conv_fused || plan->vec % VEC != 0) return false;
@@ -176,17 +248,53 @@ bool conv_backward_fused(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x
   b.dsh = grad_sh;
   b.dw = grad_w;
   b.dxp = grad_x ? ws : nullptr;
-  for (size_t k = 0; k < plan->blocks.size(); ++k) {
-    a.block = int(k);
-    a.lg_log2 = lgs[k];
-    b.dy_accum = k > 0 ? 1 : 0;
+  // The x blocks write disjoint columns of grad_w and of the grad_x partials.
+  // grad_sh sums over blocks: with room in the workspace each block writes its
+  // own accumulation-type copy and the launches run side by side (largest
+  // degree first), then one kernel adds the copies in block order; otherwise
+  // the launches accumulate into grad_sh in block order on s.
+  const int nb = int(plan->blocks.size());
+  const size_t dy_off = grad_x ? align256(conv_backward_partials_bytes(plan, g)) : 0;
+  const size_t dy_one = size_t(g->E) * size_t(plan->dim_y) * acc_size(plan->dtype);
+  const bool side = nb > 1 && (!grad_sh || (ws && ws_bytes >= dy_off + size_t(nb) * dy_one));
+  std::vector<int> order(nb);
+  for (int k = 0; k < nb; ++k) order[k] = k;
+  if (side)
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int i, int j) { return plan->blocks[i].l1 > plan->blocks[j].l1; });
+  auto launch = [&](int i, hipStream_t st) {
+    const int k = order[i];
+    ConvArgs ak = a;
+    ConvBwdArgs bk = b;
+    ak.block = k;
+    ak.lg_log2 = lgs[k];
+    if (side && grad_sh) {
+      bk.dsh = static_cast<char*>(ws) + dy_off + size_t(k) * dy_one;
+      bk.dsh_acc = 1;
+    } else {
+      bk.dy_accum = k > 0 ? 1 : 0;
+    }
     const dim3 grid(unsigned(g->N));
     switch (plan->dtype) {
-      case CGTP_F32: bwd_fused_typed<float>(a, b, plan->blocks[k].l1, plan->conv_L, grid, ldss[k], s); break;
-      case CGTP_F64: bwd_fused_typed<double>(a, b, plan->blocks[k].l1, plan->conv_L, grid, ldss[k], s); break;
-      case CGTP_BF16: bwd_fused_typed<bf16>(a, b, plan->blocks[k].l1, plan->conv_L, grid, ldss[k], s); break;
+      case CGTP_F32: bwd_fused_typed<float>(ak, bk, plan->blocks[k].l1, plan->conv_L, grid, ldss[k], st); break;
+      case CGTP_F64: bwd_fused_typed<double>(ak, bk, plan->blocks[k].l1, plan->conv_L, grid, ldss[k], st); break;
+      case CGTP_BF16: bwd_fused_typed<bf16>(ak, bk, plan->blocks[k].l1, plan->conv_L, grid, ldss[k], st); break;
     }
     CGTP_CHECK_HIP(hipGetLastError());
+  };
+  if (side) {
+    side_run(s, nb, launch, conv_edge_bytes(plan, g) >= kSideMinBytes);
+    if (grad_sh) {
+      const char* part = static_cast<const char*>(ws) + dy_off;
+      const int64_t n = g->E * plan->dim_y;
+      switch (plan->dtype) {
+        case CGTP_F32: dsh_sum<float>(part, grad_sh, n, nb, s); break;
+        case CGTP_F64: dsh_sum<double>(part, grad_sh, n, nb, s); break;
+        case CGTP_BF16: dsh_sum<bf16>(part, grad_sh, n, nb, s); break;
+      }
+    }
+  } else {
+    for (int i = 0; i < nb; ++i) launch(i, s);
   }
   if (grad_x) {
     switch (plan->dtype) {
@@ -200,8 +308,13 @@ bool conv_backward_fused(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x
 
 }  // namespace
 
+size_t conv_forward_ws_bytes(const cgtp_plan_s* plan, const cgtp_graph_s* g) {
+  if (!plan->collapse || acc_size(plan->dtype) == dtype_size(plan->dtype)) return 0;
+  return size_t(g->N) * size_t(plan->dim_out) * acc_size(plan->dtype);
+}
+
 void conv_forward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x, const void* sh,
-                         const void* w, double scale, void* out, hipStream_t s) {
+                         const void* w, double scale, void* out, hipStream_t s, void* ws, size_t ws_bytes) {
   if (g->E == 0) {
     zero_rows(out, g->N * plan->dim_out, dtype_size(plan->dtype), s);
     return;
@@ -213,15 +326,27 @@ void conv_forward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x
   a.w = w;
   a.out = out;
   a.scale = scale;
+  const size_t nacc = conv_forward_ws_bytes(plan, g);
+  void* acc_ws = nacc > 0 && ws && ws_bytes >= nacc && aligned_to(ws, 16) ? ws : nullptr;
+  const bool big = conv_edge_bytes(plan, g) >= kSideMinBytes;
   switch (plan->dtype) {
-    case CGTP_F32: fwd_typed<float>(plan, a, s); break;
-    case CGTP_F64: fwd_typed<double>(plan, a, s); break;
-    case CGTP_BF16: fwd_typed<bf16>(plan, a, s); break;
+    case CGTP_F32: fwd_typed<float>(plan, a, acc_ws, big, s); break;
+    case CGTP_F64: fwd_typed<double>(plan, a, acc_ws, big, s); break;
+    case CGTP_BF16: fwd_typed<bf16>(plan, a, acc_ws, big, s); break;
   }
 }
 
-size_t conv_backward_ws_bytes(const cgtp_plan_s* plan, const cgtp_graph_s* g) {
+size_t conv_backward_partials_bytes(const cgtp_plan_s* plan, const cgtp_graph_s* g) {
   return size_t(g->E) * size_t(plan->dim_x) * acc_size(plan->dtype);
+}
+
+// The grad_x partials, then (fused plans with several x blocks) one grad_sh
+// copy per x block so that the blocks' launches can run side by side.
+size_t conv_backward_ws_bytes(const cgtp_plan_s* plan, const cgtp_graph_s* g) {
+  size_t n = align256(conv_backward_partials_bytes(plan, g));
+  if (plan->conv_fused && plan->blocks.size() > 1)
+    n += plan->blocks.size() * size_t(g->E) * size_t(plan->dim_y) * acc_size(plan->dtype);
+  return n;
 }
 
 void conv_backward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x, const void* sh,
@@ -233,7 +358,7 @@ void conv_backward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* 
     return;
   }
   if (grad_x) {
-    const size_t need = conv_backward_ws_bytes(plan, g);
+    const size_t need = conv_backward_partials_bytes(plan, g);
     if (!ws || ws_bytes < need)
       throw Error{CGTP_ERR_WORKSPACE, "conv_backward needs " + std::to_string(need) + " workspace bytes"};
   }
@@ -247,7 +372,7 @@ void conv_backward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* 
     if (grad_sh) zero_rows(static_cast<char*>(grad_sh) + g->pad_e0 * plan->dim_y * es, np * plan->dim_y, es, s);
     if (grad_w) zero_rows(static_cast<char*>(grad_w) + g->pad_e0 * plan->w_numel * es, np * plan->w_numel, es, s);
   };
-  if (conv_backward_fused(plan, g, x, sh, w, scale, grad_out, grad_x, grad_sh, grad_w, ws, s)) {
+  if (conv_backward_fused(plan, g, x, sh, w, scale, grad_out, grad_x, grad_sh, grad_w, ws, ws_bytes, s)) {
     zero_unread_x(plan, grad_x, g->N, es, s);
     zero_padding();
     return;

@@ -28,12 +28,20 @@ cgtp_graph_s* graph_create(int64_t N, int64_t E, const int32_t* row_ptr, const i
 void graph_destroy(cgtp_graph_s* g);
 void graph_transpose_copy(const cgtp_graph_s* g, int32_t* col_ptr, int32_t* eid, hipStream_t s);
 
+// ws (nullable, conv_forward_ws_bytes): with collapsed outputs in a storage
+// type narrower than the accumulation type, the x blocks add into a running
+// sum there, rounded to the output once at the end.
 void conv_forward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x, const void* sh,
-                         const void* w, double scale, void* out, hipStream_t s);
+                         const void* w, double scale, void* out, hipStream_t s, void* ws = nullptr,
+                         size_t ws_bytes = 0);
+size_t conv_forward_ws_bytes(const cgtp_plan_s* plan, const cgtp_graph_s* g);
 void conv_backward_launch(cgtp_plan_s* plan, const cgtp_graph_s* g, const void* x, const void* sh,
                           const void* w, double scale, const void* grad_out, void* grad_x,
                           void* grad_sh, void* grad_w, void* ws, size_t ws_bytes, hipStream_t s);
 size_t conv_backward_ws_bytes(const cgtp_plan_s* plan, const cgtp_graph_s* g);
+// The part of it that grad_x needs (per-edge partials); the rest lets the
+// x blocks' launches run side by side.
+size_t conv_backward_partials_bytes(const cgtp_plan_s* plan, const cgtp_graph_s* g);
 size_t conv_double_backward_ws_bytes(const cgtp_plan_s* plan, const cgtp_graph_s* g);
 void conv_double_backward_launch(cgtp_plan_s* plan, const cgtp_graph_s* gr, const void* x, const void* sh,
                                  const void* w, double scale, const void* g, const void* gx, const void* gsh,

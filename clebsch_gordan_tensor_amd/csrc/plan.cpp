@@ -460,9 +460,64 @@ void destroy_plan(cgtp_plan_s* plan) {
   delete plan;
 }
 
+namespace {
+struct SideSet {
+  hipStream_t st[kSideStreams] = {};
+  hipEvent_t fork = nullptr;
+  hipEvent_t join[kSideStreams] = {};
+};
+std::mutex g_side_mu;
+std::map<int, SideSet> g_side;  // per HIP device id; kept until the process ends
+
+SideSet& side_set_locked(int dev) {
+  auto it = g_side.find(dev);
+  if (it != g_side.end()) return it->second;
+  SideSet ss;
+  for (int i = 0; i < kSideStreams; ++i) {
+    CGTP_CHECK_HIP(hipStreamCreateWithFlags(&ss.st[i], hipStreamNonBlocking));
+    CGTP_CHECK_HIP(hipEventCreateWithFlags(&ss.join[i], hipEventDisableTiming));
+  }
+  CGTP_CHECK_HIP(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming));
+  return g_side.emplace(dev, ss).first->second;
+}
+}  // namespace
+
+void side_streams_init() {
+  int dev = 0;
+  CGTP_CHECK_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  side_set_locked(dev);
+}
+
+#ifndef CGTP_SIDE_STREAMS
+#define CGTP_SIDE_STREAMS 1  // 0: the launches of side_run stay on s, in order (for timing)
+#endif
+
+void side_run(hipStream_t s, int n, const std::function<void(int, hipStream_t)>& f, bool fork) {
+  if (n <= 1 || !fork || CGTP_SIDE_STREAMS == 0) {
+    for (int i = 0; i < n; ++i) f(i, s);
+    return;
+  }
+  int dev = 0;
+  CGTP_CHECK_HIP(hipGetDevice(&dev));
+  // one call's fork and join are queued under the lock, so calls from several
+  // host threads do not interleave their event records
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideSet& ss = side_set_locked(dev);
+  const int used = std::min(n - 1, kSideStreams);
+  CGTP_CHECK_HIP(hipEventRecord(ss.fork, s));
+  for (int j = 0; j < used; ++j) CGTP_CHECK_HIP(hipStreamWaitEvent(ss.st[j], ss.fork, 0));
+  for (int i = 0; i < n; ++i) f(i, i == 0 ? s : ss.st[(i - 1) % kSideStreams]);
+  for (int j = 0; j < used; ++j) {
+    CGTP_CHECK_HIP(hipEventRecord(ss.join[j], ss.st[j]));
+    CGTP_CHECK_HIP(hipStreamWaitEvent(s, ss.join[j], 0));
+  }
+}
+
 const DevTables& plan_tables(cgtp_plan_s* plan) {
   int dev = 0;
   CGTP_CHECK_HIP(hipGetDevice(&dev));
+  side_streams_init();  // before any capture, like the tables
   std::lock_guard<std::mutex> lock(plan->mu);
   auto it = plan->dev.find(dev);
   if (it != plan->dev.end()) return it->second;

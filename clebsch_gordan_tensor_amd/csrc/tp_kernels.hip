@@ -137,49 +137,62 @@ void tp_forward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* 
       a.gmul[pi][o.l3] = o.mul;
       any[pi] = true;
     }
-    for (int pi = 0; pi < 2; ++pi) {
-      if (!any[pi]) continue;
-      a.par = pi == 0 ? 1 : -1;
+    // the two parities write disjoint output blocks: their launches run side by side
+    std::vector<int> pars;
+    for (int pi = 0; pi < 2; ++pi)
+      if (any[pi]) pars.push_back(pi);
+    const bool big = double(B) * double(plan->dim_out + plan->dim_x) * double(es) >= kSideMinBytes;
+    side_run(stream, int(pars.size()), [&](int i, hipStream_t st) {
+      TPArgs ap = a;
+      ap.par = pars[size_t(i)] == 0 ? 1 : -1;
       switch (plan->dtype) {
         case CGTP_F32:
-          vec == 1   ? tp_fwd_collapsed_typed<float, 1>(a, plan->lm, stream)
-          : vec == 2 ? tp_fwd_collapsed_typed<float, 2>(a, plan->lm, stream)
-                     : tp_fwd_collapsed_typed<float, 4>(a, plan->lm, stream);
+          vec == 1   ? tp_fwd_collapsed_typed<float, 1>(ap, plan->lm, st)
+          : vec == 2 ? tp_fwd_collapsed_typed<float, 2>(ap, plan->lm, st)
+                     : tp_fwd_collapsed_typed<float, 4>(ap, plan->lm, st);
           break;
         case CGTP_BF16:
-          vec == 1   ? tp_fwd_collapsed_typed<bf16, 1>(a, plan->lm, stream)
-          : vec == 2 ? tp_fwd_collapsed_typed<bf16, 2>(a, plan->lm, stream)
-                     : tp_fwd_collapsed_typed<bf16, 4>(a, plan->lm, stream);
+          vec == 1   ? tp_fwd_collapsed_typed<bf16, 1>(ap, plan->lm, st)
+          : vec == 2 ? tp_fwd_collapsed_typed<bf16, 2>(ap, plan->lm, st)
+                     : tp_fwd_collapsed_typed<bf16, 4>(ap, plan->lm, st);
           break;
         case CGTP_F64:
-          vec == 1 ? tp_fwd_collapsed_typed<double, 1>(a, plan->lm, stream)
-                   : tp_fwd_collapsed_typed<double, 2>(a, plan->lm, stream);
+          vec == 1 ? tp_fwd_collapsed_typed<double, 1>(ap, plan->lm, st)
+                   : tp_fwd_collapsed_typed<double, 2>(ap, plan->lm, st);
           break;
       }
       CGTP_CHECK_HIP(hipGetLastError());
-    }
+    }, big);
     return;
   }
-  // one launch per x block with the kernel specialised for its degree (the
-  // general kernel in one launch when channels are not vectorised)
+  // One launch per x block with the kernel specialised for its degree (the
+  // general kernel in one launch when channels are not vectorised). The
+  // blocks write disjoint output columns, so their launches run side by side,
+  // the largest degree first.
   const int nb = vec == 1 ? 1 : int(plan->blocks.size());
-  for (int b = 0; b < nb; ++b) {
-    a.block = b;
-    const int l1 = vec == 1 ? -1 : plan->blocks[size_t(b)].l1;
+  std::vector<int> order(nb);
+  for (int b = 0; b < nb; ++b) order[b] = b;
+  if (vec != 1)
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int i, int j) { return plan->blocks[size_t(i)].l1 > plan->blocks[size_t(j)].l1; });
+  const bool big = double(B) * double(plan->dim_out + plan->dim_x) * double(es) >= kSideMinBytes;
+  side_run(stream, nb, [&](int i, hipStream_t st) {
+    TPArgs ab = a;
+    ab.block = order[size_t(i)];
+    const int l1 = vec == 1 ? -1 : plan->blocks[size_t(ab.block)].l1;
     switch (plan->dtype) {
       case CGTP_F32:
-        vec == 1 ? tp_fwd_typed<float, 1>(a, l1, plan->lm, stream) : tp_fwd_typed<float, 4>(a, l1, plan->lm, stream);
+        vec == 1 ? tp_fwd_typed<float, 1>(ab, l1, plan->lm, st) : tp_fwd_typed<float, 4>(ab, l1, plan->lm, st);
         break;
       case CGTP_BF16:
-        vec == 1 ? tp_fwd_typed<bf16, 1>(a, l1, plan->lm, stream) : tp_fwd_typed<bf16, 4>(a, l1, plan->lm, stream);
+        vec == 1 ? tp_fwd_typed<bf16, 1>(ab, l1, plan->lm, st) : tp_fwd_typed<bf16, 4>(ab, l1, plan->lm, st);
         break;
       case CGTP_F64:
-        vec == 1 ? tp_fwd_typed<double, 1>(a, l1, plan->lm, stream)
-                 : tp_fwd_typed<double, 2>(a, l1, plan->lm, stream);
+        vec == 1 ? tp_fwd_typed<double, 1>(ab, l1, plan->lm, st) : tp_fwd_typed<double, 2>(ab, l1, plan->lm, st);
         break;
     }
     CGTP_CHECK_HIP(hipGetLastError());
-  }
+  }, big);
 }
 
 namespace {

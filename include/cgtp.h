@@ -57,8 +57,12 @@
  *    compute calls (tensor product, convolution, harmonics, linear map and
  *    their backward / double backward) only launch kernels on `stream` (fills
  *    by kernel, no memset nodes), so they can be captured in a HIP graph and
- *    replayed. cgtp_csr_from_coo, graph create and graph transpose allocate
- *    or synchronise and are not capturable.
+ *    replayed. Large calls fork onto library-owned streams and join back by
+ *    events, which a capture records as graph dependencies. cgtp_csr_from_coo,
+ *    graph create and graph transpose allocate or synchronise and are not
+ *    capturable; the destroy calls free device memory, so no plan, graph or
+ *    linear map may be destroyed while a capture is open (a hipFree during a
+ *    global-mode capture invalidates it).
  *  - Errors are status codes; cgtp_last_error() returns a thread-local
  *    message for the last failure. Nothing else escapes the ABI.
  */
@@ -99,7 +103,8 @@ typedef enum {
   CGTP_OP_TP_BACKWARD = 1,
   CGTP_OP_CONV_BACKWARD = 2,
   CGTP_OP_TP_DOUBLE_BACKWARD = 3,
-  CGTP_OP_CONV_DOUBLE_BACKWARD = 4
+  CGTP_OP_CONV_DOUBLE_BACKWARD = 4,
+  CGTP_OP_CONV_FORWARD = 5
 } cgtp_op;
 
 typedef struct cgtp_plan_s* cgtp_plan;
@@ -277,13 +282,34 @@ cgtp_status cgtp_graph_transpose(cgtp_graph graph, int32_t* col_ptr, int32_t* ei
 cgtp_status cgtp_conv_forward(cgtp_plan plan, cgtp_graph graph, const void* x, const void* sh,
                               const void* w, double scale, void* out, void* stream);
 
+/* cgtp_conv_forward with a workspace (same sum, E3J B.3 for collapsed
+ * outputs). With collapsed outputs the x blocks' contributions to one output
+ * block are added one x block at a time (one path at a time where the
+ * general kernel runs: channels not a multiple of 4, misaligned pointers, y
+ * degrees repeated); in bf16 storage cgtp_conv_forward rounds that running
+ * sum to bf16 after every step, while with a workspace
+ * of cgtp_workspace_size(plan, graph, 0, CGTP_OP_CONV_FORWARD) bytes
+ * (N * dim_out fp32 values; 0 for other plans) it stays fp32 and is rounded
+ * once. ws may be NULL (then as cgtp_conv_forward); a non-NULL ws must be
+ * 16-byte aligned. Errors: WORKSPACE if ws is non-NULL and smaller than that
+ * size, INVALID_ARG if misaligned. */
+cgtp_status cgtp_conv_forward_ws(cgtp_plan plan, cgtp_graph graph, const void* x, const void* sh,
+                                 const void* w, double scale, void* out, void* ws, size_t ws_bytes,
+                                 void* stream);
+
 /* Reverse mode of cgtp_conv_forward, with g_e = scale * grad_out[dst(e)]:
  *   grad_sh[e] = d/dsh of <g_e, TP(x[src(e)], sh[e], w[e])>   [E][dim_y]
  *   grad_w[e]  = d/dw  of the same                             [E][W]
  *   grad_x[n]  = sum_{e: src(e)=n} d/dx of the same            [N][dim_x]
  * grad_x is summed over the transpose in fixed order from per-edge partials
  * kept in the workspace (cgtp_workspace_size(plan, graph, 0,
- * CGTP_OP_CONV_BACKWARD) bytes). Errors: WORKSPACE if too small. */
+ * CGTP_OP_CONV_BACKWARD) bytes). That size also holds one grad_sh copy per
+ * x block in the accumulation type, which lets the x blocks' launches run
+ * side by side; grad_sh is then their sum in block order, the order in which
+ * the launches accumulate it in place when the workspace only holds the
+ * partials (E * dim_x accumulation-type values, required whenever grad_x is
+ * requested; without grad_x the workspace may be NULL). Errors: WORKSPACE if
+ * grad_x is requested and the workspace cannot hold the partials. */
 cgtp_status cgtp_conv_backward(cgtp_plan plan, cgtp_graph graph, const void* x, const void* sh,
                                const void* w, double scale, const void* grad_out, void* grad_x,
                                void* grad_sh, void* grad_w, void* ws, size_t ws_bytes, void* stream);

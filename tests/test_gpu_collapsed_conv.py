@@ -27,7 +27,7 @@ from oracle import conv as oconv
 from oracle import sh as osh
 from oracle.irreps import Layout
 from clebsch_gordan_tensor_amd import synth
-from tests.gpu_util import assert_close, dev, host, out_blocks, w_blocks, x_blocks, y_blocks
+from tests.gpu_util import assert_close, block_errors, dev, host, out_blocks, w_blocks, x_blocks, y_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -125,3 +125,51 @@ def test_collapsed_double_backward_l4():
     for got, want, blocks, what in zip(res, ref, (x_blocks(L), y_blocks(L), w_blocks(L), out_blocks(L)),
                                        ("x", "sh", "w", "grad_out")):
         assert_close(host(got), want, blocks, "f32", "collapsed double backward " + what)
+
+
+@pytest.mark.parametrize("general", [False, True])
+@pytest.mark.parametrize("name", ["conv_collapsed_l3", "conv_collapsed_l4"])
+def test_bf16_collapsed_running_sum_in_fp32(name, general):
+    """bf16 storage with a workspace: the x blocks add into an fp32 running sum
+    that is rounded to bf16 once, so the output is bitwise the fp32 plan's
+    output (same kernels and order on the same bf16-representable inputs)
+    rounded to bf16. Without the workspace the running sum is rounded after
+    every x block (within the bf16 tolerance of the oracle), or by the general
+    kernel after every path. general: misaligned weights send both plans to
+    the general (per-path) kernel."""
+    c = synth.CONFIGS[name]
+    ix, iy, io = c["irreps_x"], c["irreps_y"], c["irreps_out"]
+    L = Layout(ix, iy, io, "all", True)
+    case = small_case(n=40, seed=21)
+    pb = cgtp.Plan(ix, iy, io, dtype="bf16", collapse=True)
+    pf = cgtp.Plan(ix, iy, io, dtype="f32", collapse=True)
+    assert pb.workspace_size(cgtp.OP_CONV_FORWARD, graph=case.graph) == case.N * L.dim_out * 4
+    assert pf.workspace_size(cgtp.OP_CONV_FORWARD, graph=case.graph) == 0
+    x = dev(synth.gaussian((case.N, L.dim_x), 6, synth.S_X), "bf16")
+    Y = dev(osh.real_sh(c["L"], case.vec), "bf16")
+    w = dev(synth.gaussian((case.E, L.w_numel), 6, synth.S_W), "bf16")
+
+    def maybe_misalign(t):
+        if not general:
+            return t
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+
+    xf, Yf, wf = x.float(), Y.float(), maybe_misalign(w.float())
+    wb = maybe_misalign(w)
+    sc = 0.37
+    once = pb.conv_forward(case.graph, x, Y, wb, sc)
+    per_block = pb.conv_forward(case.graph, x, Y, wb, sc, fp32_running_sum=False)
+    ref32 = pf.conv_forward(case.graph, xf, Yf, wf, sc)
+    torch.cuda.synchronize()
+    assert torch.equal(once, ref32.to(torch.bfloat16))
+    want = oconv.forward(L, case.h_row, case.h_src, host(x), host(Y), host(w), sc)
+    e_once = assert_close(host(once), want, out_blocks(L), "bf16", "fp32 running sum")
+    if general:
+        # the general kernel adds path by path: without the workspace the sum is
+        # rounded once per path (65 at L = 4), which can exceed the tolerance
+        assert e_once <= max(block_errors(host(per_block), want, out_blocks(L)))
+    else:
+        assert_close(host(per_block), want, out_blocks(L), "bf16", "running sum rounded per x block")

@@ -296,9 +296,10 @@ def test_conv_error_paths():
     with pytest.raises(cgtp.CgtpError) as e:
         plan.conv_backward(case.graph, x, Y, w, 1.0, torch.zeros((case.N, L.dim_out), device="cuda"), ws=small_ws)
     assert e.value.status == 5
-    # the workspace size is the per-edge grad_x partials in the accumulation type
+    # the workspace size is the per-edge grad_x partials in the accumulation
+    # type (256-byte aligned), then one grad_sh copy per x block
     nws = plan.workspace_size(cgtp.OP_CONV_BACKWARD, graph=case.graph)
-    assert nws == case.E * L.dim_x * 4
+    assert nws == -(-case.E * L.dim_x * 4 // 256) * 256 + 2 * case.E * L.dim_y * 4
     g = torch.zeros((case.N, L.dim_out), device="cuda")
     # a host workspace is refused before any launch; a workspace of another
     # dtype counts in bytes
@@ -395,3 +396,37 @@ def test_conv_water8k_forces_full_size():
     assert_close(host(out[torch.from_numpy(nodes).cuda()]), rout, out_blocks(L), "f32", "sampled forward")
     del w, out, dx, gvec
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "bf16"])
+def test_conv_backward_blocks_side_by_side(dtype):
+    """The x blocks' backward launches run side by side when the workspace holds
+    a grad_sh copy per block; with room for the grad_x partials only they
+    accumulate grad_sh in place in block order. Same sums in the same order:
+    fp32 and fp64 results are bitwise equal; bf16 rounds grad_sh once instead
+    of once per block (both within tolerance of the oracle)."""
+    ix, iy, io = "8x0e+8x1o+8x2e", "0e+1o+2e+3o", "0e+0o+1e+1o+2e+2o+3e+3o"
+    L = Layout(ix, iy, io)
+    case = Case(synth.uniform_box(200, 8.0, 11), 8.0, 3.0)
+    plan = cgtp.Plan(ix, iy, io, dtype=dtype, wkind="per_row")
+    x, Y, w, g = small_inputs(L, case, 3, dtype, 3)
+    es = 8 if dtype == "f64" else 4
+    part = -(-case.E * L.dim_x * es // 256) * 256
+    nws = plan.workspace_size(cgtp.OP_CONV_BACKWARD, graph=case.graph)
+    assert nws == part + 3 * case.E * L.dim_y * es
+    full = plan.conv_backward(case.graph, x, Y, w, 0.7, g)
+    serial = plan.conv_backward(case.graph, x, Y, w, 0.7, g,
+                                ws=torch.empty(part, dtype=torch.uint8, device="cuda"))
+    # without grad_x and without a workspace the launches also run in place
+    _, dy_nows, dw_nows = plan.conv_backward(case.graph, x, Y, w, 0.7, g, need=(False, True, True),
+                                             ws=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    rdx, rdY, rdw = oconv.backward(L, case.h_row, case.h_src, host(x), host(Y), host(w), 0.7, host(g))
+    for name, (a, b) in zip(("grad_x", "grad_sh", "grad_w"), zip(full, serial)):
+        if dtype != "bf16" or name != "grad_sh":
+            assert torch.equal(a, b), name
+    assert torch.equal(serial[1], dy_nows) and torch.equal(serial[2], dw_nows)
+    for res in (full, serial):
+        assert_close(host(res[0]), rdx, x_blocks(L), dtype, "grad_x")
+        assert_close(host(res[1]), rdY, y_blocks(L), dtype, "grad_sh")
+        assert_close(host(res[2]), rdw, w_blocks(L), dtype, "grad_w")

@@ -9,6 +9,8 @@ work (the same calls outside the graph) between replays; every replay must
 equal the eager result bit for bit (the kernels are deterministic).
 """
 
+import gc
+
 import numpy as np
 import pytest
 
@@ -26,15 +28,26 @@ REPLAYS = 3
 
 
 def capture(step):
-    """Capture step() in a CUDA/HIP graph on a side stream (torch's recipe)."""
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(g, stream=s):
-            step()
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
+    """Capture step() in a CUDA/HIP graph on a side stream (torch's recipe).
+
+    Plans and graphs of earlier tests that sit in reference cycles (a
+    pytest.raises traceback holds its test's frame) are freed by Python's
+    cyclic collector whenever it runs; their destructors free device memory,
+    and a hipFree during a global-mode capture invalidates it. So the collector
+    runs before the capture and is off during it."""
+    gc.collect()
+    gc.disable()
+    try:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
     return g
 
 
