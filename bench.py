@@ -455,10 +455,12 @@ def conv_bench(args, torch, cgtp, synth, name, steps, forces=False):
     torch.cuda.synchronize()
     bf, bb = wl.bytes_fwd(), wl.bytes_bwd()
     msf, msb = tf.mean_ms(), tb.mean_ms()
-    b1, b2 = traffic_for("conv_bwd_fused_kernel", name, E), traffic_for("dx_gather_kernel", name, E)
+    # backward call: the x blocks' fused launches, the grad_sh sum over their
+    # copies and the grad-x gather
+    bparts = [traffic_for(k, name, E) for k in ("conv_bwd_fused_kernel", "dsh_sum_kernel", "dx_gather_kernel")]
     res = dict(N=N, E=E, paths=wl.plan.num_paths,
                fwd_traffic_bytes=traffic_for("conv_fwd_fused_kernel", name, E),
-               bwd_traffic_bytes=b1 + b2 if b1 is not None and b2 is not None else None,
+               bwd_traffic_bytes=sum(bparts) if None not in bparts else None,
                fwd_ms=round(msf, 3), fwd_edges_per_s=E / (msf * 1e-3),
                fwd_algorithmic_GBs=round(bf / (msf * 1e-3) / 1e9, 1),
                fwd_frac_of_hbm_peak=round(bf / (msf * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
