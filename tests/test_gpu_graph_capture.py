@@ -181,3 +181,53 @@ def test_linear_step():
         return (lin.forward(x, w),) + tuple(lin.backward(x, w, g))
 
     check_replays(hg, [x, w, g], [out, dx, dw], eager, "linear")
+
+
+def test_forked_launches_under_capture():
+    """Calls that move enough memory run their x-block launches on the
+    library's own streams beside the caller's (fork and join by events). Under
+    capture those waits become graph dependencies: the tensor-product forward
+    and the convolution forward and backward of sizes that fork are captured
+    and replayed, each replay bitwise equal to eager calls."""
+    c = synth.CONFIGS["tp_small"]
+    plan = cgtp.Plan(c["irreps_x"], c["irreps_y"], c["irreps_out"], wkind="per_row")
+    B = 40000
+    assert B * (plan.dim_out + plan.dim_x) * 4 >= 256 << 20      # the forward forks
+    x = torch.randn(B, plan.dim_x, device="cuda")
+    y = torch.randn(B, plan.dim_y, device="cuda")
+    w = torch.randn(B, plan.w_numel, device="cuda")
+    out = torch.empty(B, plan.dim_out, device="cuda")
+
+    ix, iy, io = "64x0e+64x1o+64x2e", "0e+1o+2e", "0e+0o+1e+1o+2e+2o"
+    cp = cgtp.Plan(ix, iy, io)
+    pos = synth.uniform_box(4000, 20.0, 7)
+    src, dst, _ = synth.radius_graph(pos, 20.0, 3.0)
+    N = pos.shape[0]
+    row_ptr, s, _ = ograph.csr_from_coo(N, src, dst)
+    E = len(s)
+    assert E * (cp.w_numel + cp.dim_y) * 4 >= 256 << 20          # the convolution calls fork
+    graph = cgtp.Graph(N, torch.from_numpy(row_ptr.astype(np.int32)).cuda(),
+                       torch.from_numpy(s.astype(np.int32)).cuda())
+    cx = torch.randn(N, cp.dim_x, device="cuda")
+    Y = torch.randn(E, cp.dim_y, device="cuda")
+    cw = torch.randn(E, cp.w_numel, device="cuda")
+    g = torch.randn(N, cp.dim_out, device="cuda")
+    cout = torch.empty(N, cp.dim_out, device="cuda")
+    dx, dY, dw = torch.empty_like(cx), torch.empty_like(Y), torch.empty_like(cw)
+    ws = torch.empty(cp.workspace_size(cgtp.OP_CONV_BACKWARD, graph=graph), dtype=torch.uint8, device="cuda")
+    sc = 0.21
+
+    def step():
+        plan.tp_forward(x, y, w, out=out)
+        cp.conv_forward(graph, cx, Y, cw, sc, out=cout)
+        cp.conv_backward(graph, cx, Y, cw, sc, g, out=(dx, dY, dw), ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    hg = capture(step)
+
+    def eager():
+        return ((plan.tp_forward(x, y, w), cp.conv_forward(graph, cx, Y, cw, sc))
+                + tuple(cp.conv_backward(graph, cx, Y, cw, sc, g)))
+
+    check_replays(hg, [x, y, w, cx, Y, cw, g], [out, cout, dx, dY, dw], eager, "forked launches")
