@@ -233,7 +233,9 @@ cgtp_status cgtp_tp_double_backward(cgtp_plan plan, int64_t B, const void* x, co
 
 /* ------------------------------------------------------------------ graphs */
 
-/* COO -> CSR by destination. Sort key (dst, src), ties in input order (so
+/* COO -> CSR by destination (E3J E.2.2: the receiver-ordered aggregation
+ * streams each destination's edges as one contiguous segment, so one owner
+ * sums a receiver without atomics). Sort key (dst, src), ties in input order (so
  * the result is the stable lexicographic sort of the pairs). Outputs (device,
  * caller-owned): row_ptr[N+1], src_sorted[E], perm[E] with perm[k] = input
  * index of CSR edge k. Allocates and frees temporary device memory and
@@ -242,8 +244,9 @@ cgtp_status cgtp_tp_double_backward(cgtp_plan plan, int64_t B, const void* x, co
 cgtp_status cgtp_csr_from_coo(int64_t N, int64_t E, const int32_t* src, const int32_t* dst,
                               int32_t* row_ptr, int32_t* src_sorted, int32_t* perm, void* stream);
 
-/* Wrap a CSR-by-destination graph (device arrays, caller-owned, must outlive
- * the handle): validates row_ptr (row_ptr[0] = 0, non-decreasing,
+/* Wrap a CSR-by-destination graph (E3J E.2.2 for the receiver segments, E.3
+ * for the backward's source-side gradient locality; device arrays,
+ * caller-owned, must outlive the handle): validates row_ptr (row_ptr[0] = 0, non-decreasing,
  * row_ptr[N] = E) and src (in [0, N)), and builds the source-ordered
  * transpose used by the backward pass (owned by the handle; edges grouped by
  * source, in CSR-position order). It also copies the two arrays to the host
