@@ -144,7 +144,11 @@ void free_plan_tables(cgtp_plan_s* plan);
 // afterwards, so the call stays ordered on s (and capturable: the fork and
 // join are event waits). The side streams are created with a plan's first
 // device tables on a device. fork = false runs every f(i, s) on s in order:
-// the fork and join cost about 10-20 us, more than small calls gain.
+// the fork and join cost about 10-20 us, more than small calls gain. The
+// fork, the launches and the join are queued under one lock (so calls from
+// several host threads do not interleave their event records): f must only
+// launch, never call side_run or plan_tables itself. Concurrent calls share
+// the side streams, so their forked launches run one call after another.
 constexpr int kSideStreams = 3;
 constexpr double kSideMinBytes = 256.0 * (1 << 20);  // calls that move less stay on s
 void side_run(hipStream_t s, int n, const std::function<void(int, hipStream_t)>& f, bool fork = true);
