@@ -173,3 +173,38 @@ def test_bf16_collapsed_running_sum_in_fp32(name, general):
         assert e_once <= max(block_errors(host(per_block), want, out_blocks(L)))
     else:
         assert_close(host(per_block), want, out_blocks(L), "bf16", "running sum rounded per x block")
+
+
+def test_conv_forward_ws_errors_and_ignored_workspace():
+    """cgtp_conv_forward_ws: a workspace smaller than the size query is refused
+    (WORKSPACE) and a misaligned one too (INVALID_ARG), before any launch; plans
+    that need none (fp32 storage, uncollapsed bf16) ignore one and give the
+    results of cgtp_conv_forward bit for bit."""
+    c = synth.CONFIGS["conv_collapsed_l3"]
+    ix, iy, io = c["irreps_x"], c["irreps_y"], c["irreps_out"]
+    L = Layout(ix, iy, io, "all", True)
+    case = small_case(n=30, seed=22)
+    pb = cgtp.Plan(ix, iy, io, dtype="bf16", collapse=True)
+    x = dev(synth.gaussian((case.N, L.dim_x), 8, synth.S_X), "bf16")
+    Y = dev(osh.real_sh(c["L"], case.vec), "bf16")
+    w = dev(synth.gaussian((case.E, L.w_numel), 8, synth.S_W), "bf16")
+    nws = pb.workspace_size(cgtp.OP_CONV_FORWARD, graph=case.graph)
+    with pytest.raises(cgtp.CgtpError) as e:
+        pb.conv_forward(case.graph, x, Y, w, 0.5, ws=torch.empty(nws - 16, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == 5
+    buf = torch.empty(nws + 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(cgtp.CgtpError) as e:
+        pb.conv_forward(case.graph, x, Y, w, 0.5, ws=buf[4:4 + nws])
+    assert e.value.status == 1
+    del e
+    for dtype, collapse in (("f32", True), ("bf16", False)):
+        Lp = Layout(ix, iy, io, "all", collapse)
+        p = cgtp.Plan(ix, iy, io, dtype=dtype, collapse=collapse)
+        assert p.workspace_size(cgtp.OP_CONV_FORWARD, graph=case.graph) == 0
+        xx = dev(synth.gaussian((case.N, Lp.dim_x), 9, synth.S_X), dtype)
+        YY = dev(osh.real_sh(c["L"], case.vec), dtype)
+        ww = dev(synth.gaussian((case.E, Lp.w_numel), 9, synth.S_W), dtype)
+        a = p.conv_forward(case.graph, xx, YY, ww, 0.5, ws=torch.empty(64, dtype=torch.uint8, device="cuda"))
+        b = p.conv_forward(case.graph, xx, YY, ww, 0.5, fp32_running_sum=False)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), (dtype, collapse)
