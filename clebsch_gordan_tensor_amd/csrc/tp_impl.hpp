@@ -159,7 +159,9 @@ struct TPFwd {
 };
 
 // L1 >= 0: one x block (a.block) of degree L1; L1 < 0: every block, degree
-// dispatched at run time (the general kernel, LM = CGTP_LMAX).
+// dispatched at run time (L1 = -1: the general kernel, LM = CGTP_LMAX;
+// L1 = -2: code for x degrees up to LM only, for calls too small for the
+// degree-specialised launches to pay for their launch overhead).
 template <typename T, typename A, int VEC, int L1, int LM>
 __global__ __launch_bounds__(kBlock) CGTP_FWD_OCC void tp_fwd_kernel(TPArgs a) {
   const int64_t gt = int64_t(blockIdx.x) * kBlock + threadIdx.x;
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(kBlock) CGTP_FWD_OCC void tp_fwd_kernel(TPArgs a) {
       for (int b = 0; b < a.nblocks; ++b) {
         const BlockDev blk = ldc(a.blocks + b);
         if (c >= blk.mul) continue;
-        static_for<0, kLmax + 1>([&](auto L1c) {
+        static_for<0, (L1 == -2 ? LM : kLmax) + 1>([&](auto L1c) {
           constexpr int D = decltype(L1c)::value;
           if (blk.l1 == D) TPFwd<T, A, VEC, LM>::template block<D>(a, blk, xr, yr, wr, outr, c);
         });
@@ -577,6 +579,13 @@ void tp_fwd_typed(const TPArgs& a, int l1, int lm, hipStream_t s) {
     (void)lm;
     hipLaunchKernelGGL((tp_fwd_kernel<T, A, VEC, -1, kLmax>), grid, dim3(kBlock), 0, s, a);
   } else {
+    if (l1 == -2) {
+      static_for<0, kLmax + 1>([&](auto J) {
+        constexpr int M = decltype(J)::value;
+        if (lm == M) hipLaunchKernelGGL((tp_fwd_kernel<T, A, VEC, -2, M>), grid, dim3(kBlock), 0, s, a);
+      });
+      return;
+    }
     if (l1 < 0) {
       hipLaunchKernelGGL((tp_fwd_kernel<T, A, VEC, -1, kLmax>), grid, dim3(kBlock), 0, s, a);
       return;

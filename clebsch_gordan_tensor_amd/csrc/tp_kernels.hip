@@ -165,17 +165,29 @@ void tp_forward_launch(cgtp_plan_s* plan, int64_t B, const void* x, const void* 
     }, big);
     return;
   }
-  // One launch per x block with the kernel specialised for its degree (the
-  // general kernel in one launch when channels are not vectorised). The
-  // blocks write disjoint output columns, so their launches run side by side,
-  // the largest degree first.
+  const bool big = double(B) * double(plan->dim_out + plan->dim_x) * double(es) >= kSideMinBytes;
+  // Small calls are bound by launch overhead: one launch over every x block
+  // (x degrees up to the plan's largest y/output degree).
+  if (!big && vec != 1 && plan->blocks.size() > 1 && a.max_l1 <= plan->lm) {
+    switch (plan->dtype) {
+      case CGTP_F32: tp_fwd_typed<float, 4>(a, -2, plan->lm, stream); break;
+      case CGTP_BF16: tp_fwd_typed<bf16, 4>(a, -2, plan->lm, stream); break;
+      case CGTP_F64: tp_fwd_typed<double, 2>(a, -2, plan->lm, stream); break;
+    }
+    CGTP_CHECK_HIP(hipGetLastError());
+    return;
+  }
+  // Otherwise one launch per x block with the kernel specialised for its
+  // degree (the general kernel in one launch when channels are not
+  // vectorised). The blocks write disjoint output columns, so their launches
+  // run side by side, the largest degree first (measured against one launch
+  // over every block at 2^20 rows: 19.8-20.0 against 20.9 ms).
   const int nb = vec == 1 ? 1 : int(plan->blocks.size());
   std::vector<int> order(nb);
   for (int b = 0; b < nb; ++b) order[b] = b;
   if (vec != 1)
     std::stable_sort(order.begin(), order.end(),
                      [&](int i, int j) { return plan->blocks[size_t(i)].l1 > plan->blocks[size_t(j)].l1; });
-  const bool big = double(B) * double(plan->dim_out + plan->dim_x) * double(es) >= kSideMinBytes;
   side_run(stream, nb, [&](int i, hipStream_t st) {
     TPArgs ab = a;
     ab.block = order[size_t(i)];
